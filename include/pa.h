@@ -1,0 +1,257 @@
+/*
+ * pa.h — C ABI of the paged KV-cache library (MI355X / gfx950).
+ *
+ * Three operations on a paged KV cache, as described in the pages on
+ * PagedAttention:
+ *
+ *   pa_write_kv     slot-mapped writes of new keys/values into the block pool
+ *                   ("When KV Capacity Runs Out", Figure 2: the KV of position
+ *                   8 lands in the first slot of the newly attached block;
+ *                   "Efficient Memory Management for Large Language Model
+ *                   Serving with PagedAttention" (summary page), block-table
+ *                   paragraph: logical blocks fill left to right).
+ *   pa_decode       one decode query per sequence attending over the keys and
+ *                   values of its context, fetched block by block through the
+ *                   block table (same summary page, kernel paragraph: the
+ *                   result is identical to ordinary attention; "Continuous
+ *                   Batching and PagedAttention", section "The block table is
+ *                   a page table").
+ *   pa_copy_blocks  whole-block copies: copy-on-write of a shared block inside
+ *                   device memory (summary page, sampling and prefix
+ *                   paragraphs) and swap between device and pinned host memory
+ *                   ("When KV Capacity Runs Out", section "Restore KV stored
+ *                   outside the GPU", Figure 4).
+ *
+ * Conventions shared by every call
+ *  - Ownership: the caller owns every buffer (pools, tables, workspace). The
+ *    library never allocates, never frees, never synchronises the host and
+ *    keeps no pointer after a call returns. It holds no global state and is
+ *    reentrant.
+ *  - Streams: all device work is enqueued on the caller's `stream` and is
+ *    asynchronous with respect to the host; stream order gives the ordering
+ *    between calls (e.g. a swap-out copy finishes before a later write that
+ *    reuses the released block, as "Restore KV stored outside the GPU"
+ *    requires).
+ *  - Errors: argument problems that the host can see (null pointers, shapes,
+ *    dtype combinations, unsupported sizes, a too-small workspace, host-side
+ *    copy pairs) are reported before any HIP call is made and leave every
+ *    buffer untouched. Launch failures return PA_ERR_HIP.
+ *  - Bad values inside device arrays never cause an out-of-bounds access:
+ *      * pa_write_kv skips a token whose slot lies beyond the pool;
+ *      * pa_decode writes a NaN output row for a sequence whose context
+ *        length is negative, exceeds max_context_len or max_blocks_per_seq *
+ *        block_size, or whose block table names a block outside the pool;
+ *      * pa_copy_blocks (device pairs) skips a pair naming a block outside
+ *        either pool.
+ *
+ * Pool layout (one pool for K and one for V, same geometry)
+ *   Element (layer l, block b, kv head h, slot o, dim d) lives at element index
+ *       b * block_stride + l * layer_stride + (h * block_size + o) * head_dim + d
+ *   Blocks are fixed-size and may sit anywhere in the pool ("Continuous
+ *   Batching and PagedAttention", section "Fixed-size blocks make every free
+ *   block usable"). The default, block-major layout has
+ *       layer_stride = num_kv_heads * block_size * head_dim,
+ *       block_stride = num_layers * layer_stride,
+ *   so all layers of one block are one contiguous range, which makes a swap
+ *   of a block a single transfer ("KV Cache Preemption in vLLM", section
+ *   "Swap versus recompute", notes that a block's data spans every layer).
+ *   Positions are 0-based: token t of a sequence lives in logical block
+ *   t / block_size at slot t % block_size ("When KV Capacity Runs Out",
+ *   section "Running out of KV space during generation": positions count
+ *   from 0).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad dtype combination   */
+  PA_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. head_dim)  */
+  PA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required  */
+  PA_ERR_HIP = 4          /* a HIP launch or copy call failed                 */
+} pa_status;
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  /* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; subnormals
+     m * 2^-9; largest finite 448 (0x7E); 0x7F / 0xFF are NaN; no infinity.
+     The pages mention an FP8 KV cache only as a capacity lever ("KV Cache
+     Preemption in vLLM", sections "How much KV cache a token costs" and "A
+     worked example"); this format is the reading adopted for it. */
+  PA_FP8_E4M3 = 3
+} pa_dtype;
+
+/* One KV pool: K and V tensors of identical geometry, in device memory or in
+ * pinned host memory (host pools are only valid as a side of an H2D / D2H
+ * pa_copy_blocks call). */
+typedef struct {
+  void* k;                /* K elements, layout above                           */
+  void* v;                /* V elements, layout above                           */
+  pa_dtype dtype;         /* storage type of both tensors                       */
+  int32_t num_blocks;     /* physical blocks in the pool                        */
+  int32_t num_layers;     /* layers held per block (>= 1)                       */
+  int32_t num_kv_heads;   /* KV heads per layer                                 */
+  int32_t block_size;     /* token slots per block: power of two, 1..256        */
+  int32_t head_dim;       /* elements per head vector                           */
+  int64_t block_stride;   /* elements between consecutive blocks               */
+  int64_t layer_stride;   /* elements between consecutive layers of one block  */
+  float k_scale;          /* FP8 only: value = code * k_scale (> 0, finite);    */
+  float v_scale;          /*   must be exactly 1.0f for the other dtypes        */
+} pa_kv_cache;
+
+/* ------------------------------------------------------------------------ */
+/* pa_write_kv — store the keys and values of num_tokens new tokens.         */
+/*                                                                           */
+/* For token i with slot_mapping[i] >= 0, block = slot / block_size and      */
+/* offset = slot % block_size; K[i][h][:] and V[i][h][:] are stored at       */
+/* (layer, block, h, offset, :) for every KV head h. Tokens with a negative  */
+/* slot are skipped (padding). ("When KV Capacity Runs Out", Figure 2 and    */
+/* section "Restore KV stored outside the GPU": the new position's KV is     */
+/* written into the next free slot of the sequence's last block.)            */
+/*                                                                           */
+/*  k, v         device, [num_tokens][num_kv_heads][head_dim], dense, of     */
+/*               src_dtype. src_dtype must equal cache->dtype, or, when the  */
+/*               cache is PA_FP8_E4M3, be PA_F32 / PA_F16 / PA_BF16.         */
+/*  slot_mapping device int64 [num_tokens]. Non-negative slots must be       */
+/*               distinct within one call (undefined result otherwise); a    */
+/*               slot >= num_blocks * block_size is skipped.                 */
+/*  Same dtype: the stored bytes equal the source bytes.                     */
+/*  FP8: code = RNE_e4m3(clamp(fp32(x) / scale, -448, 448)) with an IEEE     */
+/*  correctly rounded fp32 division (scale = k_scale or v_scale); a NaN      */
+/*  input gives the NaN code with the input's sign; -0 stays -0.             */
+/*  num_tokens == 0 is a no-op.                                              */
+/* ------------------------------------------------------------------------ */
+pa_status pa_write_kv(const pa_kv_cache* cache, int32_t layer, const void* k,
+                      const void* v, pa_dtype src_dtype,
+                      const int64_t* slot_mapping, int32_t num_tokens,
+                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* pa_decode — paged attention for one query token per sequence.             */
+/*                                                                           */
+/* For sequence s with n = context_lens[s] and query head h (group size      */
+/* g = num_q_heads / num_kv_heads, KV head kvh = h / g):                     */
+/*   z_t  = scale * <q[s][h], K[t][kvh]>,            t = 0 .. n-1            */
+/*   out[s][h] = sum_t softmax(z)_t * V[t][kvh]                              */
+/* where token t is read from block block_tables[s][t / block_size], slot    */
+/* t % block_size ("Efficient Memory Management for Large Language Model     */
+/* Serving with PagedAttention", kernel paragraph: fetch each block wherever */
+/* it lives, score the query against it, combine with its values; the       */
+/* result is that of ordinary attention). n counts the token written by  */
+/* this step's pa_write_kv. n == 0 gives a zero output row. FP8 pools are    */
+/* dequantised as code * k_scale / v_scale. No mask beyond the context      */
+/* length is applied (the query is the last position).                       */
+/*                                                                           */
+/*  q, out        device, [num_seqs][num_q_heads][head_dim], dense, q_dtype  */
+/*                (PA_F32, PA_F16 or PA_BF16); out has the same dtype and is */
+/*                rounded to nearest-even from fp32 accumulation.            */
+/*  block_tables  device int32 [num_seqs][max_blocks_per_seq]; entries at    */
+/*                index >= ceil(n / block_size) are never read.              */
+/*  context_lens  device int32 [num_seqs], each in [0, max_context_len].     */
+/*  max_context_len  host upper bound on context_lens; sizes the launch.     */
+/*  workspace     device scratch of >= pa_decode_workspace_size(...) bytes,  */
+/*                256-byte aligned; contents need no initialisation.         */
+/* Supported today: head_dim 64 or 128 (64 only for PA_F32 pools);          */
+/* num_q_heads / num_kv_heads in {1, 2, 4, 8}; q_dtype equal to the pool     */
+/* dtype, or any of the three with a PA_FP8_E4M3 pool. Others return         */
+/* PA_ERR_UNSUPPORTED.                                                       */
+/*                                                                           */
+/* pa_decode is exactly pa_decode_attend followed by pa_decode_merge with    */
+/* the same arguments. The split lets a caller time or schedule the two      */
+/* launches separately; pa_decode_merge must follow pa_decode_attend on the  */
+/* same stream with unchanged inputs and workspace.                          */
+/* ------------------------------------------------------------------------ */
+pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q,
+                    pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/* Phase 1: attention over each context partition. Writes out[s] directly    */
+/* for sequences that fit one partition, partial results into workspace for  */
+/* the others.                                                               */
+pa_status pa_decode_attend(const pa_kv_cache* cache, int32_t layer,
+                           const void* q, pa_dtype q_dtype, void* out,
+                           const int32_t* block_tables,
+                           int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len,
+                           int32_t num_seqs, int32_t num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Phase 2: merge the partition partials of multi-partition sequences:       */
+/* M = max_p m_p;  out = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p.      */
+pa_status pa_decode_merge(const pa_kv_cache* cache, int32_t layer,
+                          const void* q, pa_dtype q_dtype, void* out,
+                          const int32_t* block_tables,
+                          int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len,
+                          int32_t num_seqs, int32_t num_q_heads, float scale,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Tokens per context partition that pa_decode will use for these sizes     */
+/* (a multiple of the per-wave chunk); 0 if the arguments are invalid.      */
+int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs,
+                                   int32_t num_q_heads,
+                                   int32_t max_context_len);
+
+/* Workspace bytes pa_decode needs for these sizes (0 if none is needed or   */
+/* the arguments are invalid).                                               */
+size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t max_context_len);
+
+/* ------------------------------------------------------------------------ */
+/* pa_copy_blocks — copy whole blocks (K and V, every layer, head and slot). */
+/*                                                                           */
+/*  PA_COPY_D2D  copy-on-write inside device memory: a sequence about to     */
+/*               write into a shared block first receives a private copy     */
+/*               ("Efficient Memory Management ... with PagedAttention",     */
+/*               sampling and prefix paragraphs;                             */
+/*               "Continuous Batching and PagedAttention", section "Sharing, */
+/*               the part that goes beyond fixing what broke"). `pairs` is   */
+/*               in device memory. dst and src may be the same pool.         */
+/*  PA_COPY_D2H  swap out: device `src` pool -> pinned host `dst` pool.      */
+/*  PA_COPY_H2D  swap in: pinned host `src` pool -> device `dst` pool; the   */
+/*               destination blocks may differ from the ones the data left   */
+/*               ("When KV Capacity Runs Out", section "Restore KV stored    */
+/*               outside the GPU").                                          */
+/*               For D2H / H2D `pairs` is in host memory and is validated    */
+/*               (ids in range, destination ids distinct) before any copy;   */
+/*               runs of consecutive ids become one transfer each.           */
+/*  pairs        int64 [num_pairs][2] = {src_block, dst_block}.              */
+/*  Both pools must have the same dtype, layers, heads, block size and head  */
+/*  dim (strides may differ). Destination ids must be distinct and, for D2D  */
+/*  within one pool, no id may be both a source and a destination in one     */
+/*  call (undefined result otherwise). The copied bytes are identical.       */
+/*  num_pairs == 0 is a no-op.                                               */
+/* ------------------------------------------------------------------------ */
+typedef enum { PA_COPY_D2D = 0, PA_COPY_H2D = 1, PA_COPY_D2H = 2 } pa_copy_dir;
+
+pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src,
+                         const int64_t* pairs, int32_t num_pairs,
+                         pa_copy_dir dir, hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Library version string, e.g. "0.1.0". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */
