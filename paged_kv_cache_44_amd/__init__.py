@@ -1,0 +1,183 @@
+"""Paged KV cache for MI355X: Python binding of the C ABI in include/pa.h.
+
+The three operations are hand-written HIP kernels in ``libpa.so``; this
+module only turns torch tensors into pointers, sizes and the current HIP
+stream, and raises on a non-OK status. torch supplies device memory, pinned
+host memory and streams.
+
+    cache = KVCache(k_pool, v_pool, "bf16", num_blocks, 1, 8, 16, 128)
+    write_kv(cache, 0, k_new, v_new, slot_mapping)
+    out = decode(cache, 0, q, block_tables, context_lens, max_context_len, scale)
+    copy_blocks(cache, cache, pairs, "d2d")
+
+If the library has not been built, every call raises: there is no fallback.
+"""
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+DTYPES = {"f32": B.PA_F32, "f16": B.PA_F16, "bf16": B.PA_BF16, "fp8_e4m3": B.PA_FP8_E4M3}
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+               "fp8_e4m3": torch.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+
+__all__ = ["KVCache", "write_kv", "decode", "decode_attend", "decode_merge",
+           "decode_workspace_size", "decode_partition_tokens", "copy_blocks", "version"]
+
+
+def _lib():
+    return B.load_library()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dtype_name(t: torch.Tensor) -> str:
+    for k, v in TORCH_DTYPE.items():
+        if t.dtype == v:
+            return k
+    if t.dtype == torch.float8_e4m3fn:
+        return "fp8_e4m3"
+    raise ValueError(f"unsupported tensor dtype {t.dtype}")
+
+
+@dataclass
+class KVCache:
+    """A K pool and a V pool (device, or pinned host for swap space).
+
+    Element (layer l, block b, head h, slot o, dim d) sits at flat index
+    b * block_stride + l * layer_stride + (h * block_size + o) * head_dim + d;
+    strides default to the block-major packed layout.
+    """
+    k: torch.Tensor
+    v: torch.Tensor
+    dtype: str
+    num_blocks: int
+    num_layers: int
+    num_kv_heads: int
+    block_size: int
+    head_dim: int
+    block_stride: int = -1
+    layer_stride: int = -1
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    def __post_init__(self):
+        if self.layer_stride < 0:
+            self.layer_stride = self.num_kv_heads * self.block_size * self.head_dim
+        if self.block_stride < 0:
+            self.block_stride = self.num_layers * self.layer_stride
+
+    @classmethod
+    def empty(cls, dtype: str, num_blocks: int, num_layers: int, num_kv_heads: int,
+              block_size: int, head_dim: int, device="cuda", pin_memory=False,
+              k_scale=1.0, v_scale=1.0) -> "KVCache":
+        n = num_blocks * num_layers * num_kv_heads * block_size * head_dim
+        kw = dict(dtype=TORCH_DTYPE[dtype])
+        if pin_memory:
+            k = torch.empty(n, pin_memory=True, **kw)
+            v = torch.empty(n, pin_memory=True, **kw)
+        else:
+            k = torch.empty(n, device=device, **kw)
+            v = torch.empty(n, device=device, **kw)
+        return cls(k, v, dtype, num_blocks, num_layers, num_kv_heads, block_size, head_dim,
+                   k_scale=k_scale, v_scale=v_scale)
+
+    def struct(self) -> B.PaKvCache:
+        return B.PaKvCache(self.k.data_ptr(), self.v.data_ptr(), DTYPES[self.dtype],
+                           self.num_blocks, self.num_layers, self.num_kv_heads,
+                           self.block_size, self.head_dim, self.block_stride,
+                           self.layer_stride, self.k_scale, self.v_scale)
+
+
+def write_kv(cache: KVCache, layer: int, k: torch.Tensor, v: torch.Tensor,
+             slot_mapping: torch.Tensor, stream=None) -> None:
+    """Store k, v [T][H_kv][D] at their slots (int64 [T], negative = skip)."""
+    c = cache.struct()
+    st = _lib().pa_write_kv(ctypes.byref(c), layer, _ptr(k), _ptr(v), DTYPES[dtype_name(k)],
+                            _ptr(slot_mapping), int(slot_mapping.numel()), _stream(stream))
+    B.check(st, "pa_write_kv")
+
+
+def decode_workspace_size(cache: KVCache, num_seqs: int, num_q_heads: int,
+                          max_context_len: int) -> int:
+    c = cache.struct()
+    return int(_lib().pa_decode_workspace_size(ctypes.byref(c), num_seqs, num_q_heads,
+                                               max_context_len))
+
+
+def decode_partition_tokens(cache: KVCache, num_seqs: int, num_q_heads: int,
+                            max_context_len: int) -> int:
+    c = cache.struct()
+    return int(_lib().pa_decode_partition_tokens(ctypes.byref(c), num_seqs, num_q_heads,
+                                                 max_context_len))
+
+
+def _decode_call(fn_name, cache, layer, q, block_tables, context_lens, max_context_len, scale,
+                 out, workspace, stream):
+    S, Hq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = decode_workspace_size(cache, S, Hq, max_context_len)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    c = cache.struct()
+    st = getattr(_lib(), fn_name)(
+        ctypes.byref(c), layer, _ptr(q), DTYPES[dtype_name(q)], _ptr(out), _ptr(block_tables),
+        int(block_tables.shape[1]) if block_tables.dim() == 2 else 0, _ptr(context_lens),
+        int(max_context_len), S, Hq, float(scale), _ptr(workspace), int(workspace.numel()),
+        _stream(stream))
+    B.check(st, fn_name)
+    return out, workspace
+
+
+def decode(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, max_context_len: int, scale: float,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream=None) -> torch.Tensor:
+    """Paged decode attention: q [S][H_q][D] -> out [S][H_q][D] (q's dtype)."""
+    return _decode_call("pa_decode", cache, layer, q, block_tables, context_lens,
+                        max_context_len, scale, out, workspace, stream)[0]
+
+
+def decode_attend(cache, layer, q, block_tables, context_lens, max_context_len, scale,
+                  out, workspace, stream=None):
+    """Phase 1 of :func:`decode` (partition attention)."""
+    _decode_call("pa_decode_attend", cache, layer, q, block_tables, context_lens,
+                 max_context_len, scale, out, workspace, stream)
+
+
+def decode_merge(cache, layer, q, block_tables, context_lens, max_context_len, scale,
+                 out, workspace, stream=None):
+    """Phase 2 of :func:`decode` (merge of partition partials)."""
+    _decode_call("pa_decode_merge", cache, layer, q, block_tables, context_lens,
+                 max_context_len, scale, out, workspace, stream)
+
+
+_DIRS = {"d2d": B.PA_COPY_D2D, "h2d": B.PA_COPY_H2D, "d2h": B.PA_COPY_D2H}
+
+
+def copy_blocks(dst: KVCache, src: KVCache, pairs: torch.Tensor, direction: str = "d2d",
+                stream=None) -> None:
+    """Copy whole blocks: pairs int64 [N][2] = (src_block, dst_block); device
+    memory for "d2d", host memory for "h2d" / "d2h"."""
+    d, s = dst.struct(), src.struct()
+    n = int(pairs.shape[0]) if pairs.dim() == 2 else 0
+    st = _lib().pa_copy_blocks(ctypes.byref(d), ctypes.byref(s), _ptr(pairs), n,
+                               _DIRS[direction], _stream(stream))
+    B.check(st, "pa_copy_blocks")
+
+
+def version() -> str:
+    return _lib().pa_version().decode()

@@ -1,0 +1,80 @@
+"""ctypes declarations of the C ABI in include/pa.h (argument marshalling
+only; every computation happens in the HIP library)."""
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = range(4)
+PA_COPY_D2D, PA_COPY_H2D, PA_COPY_D2H = range(3)
+
+#: every function the header declares
+EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_attend", "pa_decode_merge",
+            "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_copy_blocks",
+            "pa_status_string", "pa_version")
+
+
+class PaKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("dtype", ctypes.c_int),
+        ("num_blocks", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_stride", ctypes.c_int64),
+        ("layer_stride", ctypes.c_int64),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_44_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(PaKvCache)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.pa_write_kv.argtypes = [P, i32, vp, vp, ctypes.c_int, vp, i32, vp]
+    lib.pa_write_kv.restype = ctypes.c_int
+    dec = [P, i32, vp, ctypes.c_int, vp, vp, i32, vp, i32, i32, i32, f32, vp, sz, vp]
+    for name in ("pa_decode", "pa_decode_attend", "pa_decode_merge"):
+        getattr(lib, name).argtypes = dec
+        getattr(lib, name).restype = ctypes.c_int
+    lib.pa_decode_partition_tokens.argtypes = [P, i32, i32, i32]
+    lib.pa_decode_partition_tokens.restype = i32
+    lib.pa_decode_workspace_size.argtypes = [P, i32, i32, i32]
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_copy_blocks.argtypes = [P, P, vp, i32, ctypes.c_int, vp]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = load_library()
+        super().__init__(f"{what}: {lib.pa_status_string(status).decode()}")
+        self.status = status
+
+
+def check(status: int, what: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, what)

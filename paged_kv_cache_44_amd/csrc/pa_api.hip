@@ -1,0 +1,396 @@
+// pa_api.hip — the C ABI declared in include/pa.h: argument validation on
+// the host, launch-size choices, and dispatch to the gfx950 kernels. Nothing
+// here allocates device memory or synchronises the host.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+using pa::DecodeParams;
+
+namespace {
+
+int elem_bytes(pa_dtype t) {
+  switch (t) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+bool valid_dtype(int t) { return t >= PA_F32 && t <= PA_FP8_E4M3; }
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Geometry checks shared by every call. `need_ptrs` requires k and v.
+pa_status check_cache(const pa_kv_cache* c, bool need_ptrs) {
+  if (!c) return PA_ERR_INVALID_ARG;
+  if (!valid_dtype(c->dtype)) return PA_ERR_INVALID_ARG;
+  if (need_ptrs && (!c->k || !c->v)) return PA_ERR_INVALID_ARG;
+  if (c->num_blocks <= 0 || c->num_layers <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (!is_pow2(c->block_size) || c->block_size > 256) return PA_ERR_INVALID_ARG;
+  const int64_t slab = (int64_t)c->num_kv_heads * c->block_size * c->head_dim;
+  if (c->layer_stride < slab && c->num_layers > 1) return PA_ERR_INVALID_ARG;
+  if (c->layer_stride < 0) return PA_ERR_INVALID_ARG;
+  const int64_t span = (int64_t)(c->num_layers - 1) * c->layer_stride + slab;
+  if (c->block_stride < span && c->num_blocks > 1) return PA_ERR_INVALID_ARG;
+  if (c->block_stride < 0) return PA_ERR_INVALID_ARG;
+  const int eb = elem_bytes(c->dtype);
+  if ((c->block_stride * eb) % 16 || (c->layer_stride * eb) % 16) return PA_ERR_UNSUPPORTED;
+  if ((c->head_dim * eb) % 16) return PA_ERR_UNSUPPORTED;
+  if (need_ptrs && (!aligned(c->k, 16) || !aligned(c->v, 16))) return PA_ERR_UNSUPPORTED;
+  if (c->dtype == PA_FP8_E4M3) {
+    if (!(c->k_scale > 0.f) || !isfinite(c->k_scale) || !(c->v_scale > 0.f) || !isfinite(c->v_scale))
+      return PA_ERR_INVALID_ARG;
+  } else if (c->k_scale != 1.0f || c->v_scale != 1.0f) {
+    return PA_ERR_INVALID_ARG;
+  }
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode planning
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int g;
+  int part_tokens;
+  int num_parts;
+  size_t ws_bytes;     // 0 when no sequence can need a merge
+};
+
+pa_status decode_supported(const pa_kv_cache* c, int num_q_heads, pa_dtype q_dtype, int* g_out) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads) return PA_ERR_INVALID_ARG;
+  const int g = num_q_heads / c->num_kv_heads;
+  if (!(g == 1 || g == 2 || g == 4 || g == 8)) return PA_ERR_UNSUPPORTED;
+  if (!(q_dtype == PA_F32 || q_dtype == PA_F16 || q_dtype == PA_BF16)) return PA_ERR_INVALID_ARG;
+  const bool pair_ok = (c->dtype == q_dtype) || (c->dtype == PA_FP8_E4M3);
+  if (!pair_ok) return PA_ERR_UNSUPPORTED;
+  if (c->dtype == PA_F32) {
+    if (c->head_dim != 64) return PA_ERR_UNSUPPORTED;
+  } else if (!(c->head_dim == 64 || c->head_dim == 128)) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  *g_out = g;
+  return PA_OK;
+}
+
+// Tokens per partition: large enough that the fp32 partial results stay a
+// small fraction of the key/value bytes of a partition (about 4 * G / P /
+// elem_bytes of them), small enough that long contexts still spread over
+// many workgroups.
+int choose_part_tokens(const pa_kv_cache* c, int g, int num_seqs, int max_ctx) {
+  const int eb = elem_bytes(c->dtype);
+  int p = 256;
+  const int want = 256 * g / eb;
+  while (p < want && p < 2048) p *= 2;
+  const int64_t units = (int64_t)num_seqs * c->num_kv_heads;
+  while (p > 256 && units * ((max_ctx + p - 1) / p) < 4096) p /= 2;
+  // a partition may span at most PA_MAX_PART_BLOCKS table entries
+  while (p / c->block_size > pa::PA_MAX_PART_BLOCKS && p > 64) p /= 2;
+  return p;
+}
+
+pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dtype q_dtype,
+                      int max_ctx, DecodePlan* plan) {
+  pa_status st = check_cache(c, false);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || max_ctx < 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  int g = 0;
+  st = decode_supported(c, num_q_heads, q_dtype, &g);
+  if (st != PA_OK) return st;
+  plan->g = g;
+  plan->part_tokens = choose_part_tokens(c, g, num_seqs, max_ctx);
+  plan->num_parts = std::max(1, (max_ctx + plan->part_tokens - 1) / plan->part_tokens);
+  if (plan->num_parts > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
+    const size_t o = rows * c->head_dim * sizeof(float);
+    const size_t ml = rows * sizeof(float);
+    // three 256-byte aligned regions: o, m, l
+    plan->ws_bytes = ((o + 255) & ~(size_t)255) + 2 * ((ml + 255) & ~(size_t)255);
+  } else {
+    plan->ws_bytes = 0;
+  }
+  return PA_OK;
+}
+
+enum Phase { PHASE_ATTEND = 1, PHASE_MERGE = 2, PHASE_BOTH = 3 };
+
+pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const void* q,
+                      pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                      float scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !out || !context_lens || (!block_tables && max_blocks_per_seq > 0))
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * cache->block_size < 0) return PA_ERR_INVALID_ARG;
+  DecodePlan plan;
+  st = plan_decode(cache, num_seqs, num_q_heads, q_dtype, max_context_len, &plan);
+  if (st != PA_OK) return st;
+  const int qb = elem_bytes(q_dtype);
+  if (!aligned(q, 16) || !aligned(out, 4)) return PA_ERR_UNSUPPORTED;
+  (void)qb;
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256))
+      return PA_ERR_WORKSPACE;
+  }
+
+  DecodeParams a;
+  memset(&a, 0, sizeof(a));
+  a.k_pool = cache->k;
+  a.v_pool = cache->v;
+  a.block_stride = cache->block_stride;
+  a.layer_offset = (int64_t)layer * cache->layer_stride;
+  a.num_blocks = cache->num_blocks;
+  a.block_size = cache->block_size;
+  a.log2_block_size = ilog2(cache->block_size);
+  a.head_dim = cache->head_dim;
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  a.v_scale = fp8 ? cache->v_scale : 1.0f;
+  const double log2e = 1.4426950408889634;
+  a.qk_scale_log2 = (float)((double)scale * log2e * (fp8 ? (double)cache->k_scale : 1.0));
+  a.q = q;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.part_tokens = plan.part_tokens;
+  a.num_parts = plan.num_parts;
+  if (plan.ws_bytes > 0) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * plan.num_parts;
+    const size_t o = ((rows * cache->head_dim * sizeof(float)) + 255) & ~(size_t)255;
+    const size_t ml = ((rows * sizeof(float)) + 255) & ~(size_t)255;
+    char* w = reinterpret_cast<char*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(w);
+    a.ws_m = reinterpret_cast<float*>(w + o);
+    a.ws_l = reinterpret_cast<float*>(w + o + ml);
+  }
+  if (phases & PHASE_ATTEND) {
+    if (pa::launch_attend(a, (int)cache->dtype, (int)q_dtype, plan.g, stream) != hipSuccess)
+      return PA_ERR_HIP;
+  }
+  if ((phases & PHASE_MERGE) && plan.num_parts > 1) {
+    if (pa::launch_merge(a, (int)q_dtype, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+bool same_shape(const pa_kv_cache* a, const pa_kv_cache* b) {
+  return a->dtype == b->dtype && a->num_layers == b->num_layers &&
+         a->num_kv_heads == b->num_kv_heads && a->block_size == b->block_size &&
+         a->head_dim == b->head_dim;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_write_kv(const pa_kv_cache* cache, int32_t layer, const void* k, const void* v,
+                      pa_dtype src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                      hipStream_t stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (!valid_dtype(src_dtype)) return PA_ERR_INVALID_ARG;
+  const bool conv = src_dtype != cache->dtype;
+  if (conv && !(cache->dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3)) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k, 16) || !aligned(v, 16)) return PA_ERR_UNSUPPORTED;
+  if (((int64_t)cache->head_dim * elem_bytes(src_dtype)) % 16) return PA_ERR_UNSUPPORTED;
+  pa::WriteParams a;
+  memset(&a, 0, sizeof(a));
+  a.k_pool = cache->k;
+  a.v_pool = cache->v;
+  a.block_stride = cache->block_stride;
+  a.layer_offset = (int64_t)layer * cache->layer_stride;
+  a.num_blocks = cache->num_blocks;
+  a.block_size = cache->block_size;
+  a.log2_block_size = ilog2(cache->block_size);
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  a.k_src = k;
+  a.v_src = v;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  if (pa::launch_write(a, (int)src_dtype, (int)cache->dtype, stream) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t max_context_len) {
+  DecodePlan plan;
+  if (!cache) return 0;
+  pa_dtype qd = cache->dtype == PA_FP8_E4M3 ? PA_BF16 : cache->dtype;
+  if (plan_decode(cache, num_seqs, num_q_heads, qd, max_context_len, &plan) != PA_OK) return 0;
+  return plan.ws_bytes;
+}
+
+int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_context_len) {
+  DecodePlan plan;
+  if (!cache) return 0;
+  pa_dtype qd = cache->dtype == PA_FP8_E4M3 ? PA_BF16 : cache->dtype;
+  if (plan_decode(cache, num_seqs, num_q_heads, qd, max_context_len, &plan) != PA_OK) return 0;
+  return plan.part_tokens;
+}
+
+pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q, pa_dtype q_dtype,
+                    void* out, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                    int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return decode_impl(PHASE_BOTH, cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_seqs, num_q_heads, scale, workspace,
+                     workspace_bytes, stream);
+}
+
+pa_status pa_decode_attend(const pa_kv_cache* cache, int32_t layer, const void* q,
+                           pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return decode_impl(PHASE_ATTEND, cache, layer, q, q_dtype, out, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     scale, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_merge(const pa_kv_cache* cache, int32_t layer, const void* q,
+                          pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                          float scale, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return decode_impl(PHASE_MERGE, cache, layer, q, q_dtype, out, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                     scale, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src, const int64_t* pairs,
+                         int32_t num_pairs, pa_copy_dir dir, hipStream_t stream) {
+  pa_status st = check_cache(dst, true);
+  if (st != PA_OK) return st;
+  st = check_cache(src, true);
+  if (st != PA_OK) return st;
+  if (!same_shape(dst, src)) return PA_ERR_INVALID_ARG;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (!(dir == PA_COPY_D2D || dir == PA_COPY_H2D || dir == PA_COPY_D2H)) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs) return PA_ERR_INVALID_ARG;
+  const int eb = elem_bytes(dst->dtype);
+  const int64_t slab = (int64_t)dst->num_kv_heads * dst->block_size * dst->head_dim * eb;
+
+  if (dir == PA_COPY_D2D) {
+    pa::CopyParams a;
+    memset(&a, 0, sizeof(a));
+    a.dst_k = reinterpret_cast<char*>(dst->k);
+    a.dst_v = reinterpret_cast<char*>(dst->v);
+    a.src_k = reinterpret_cast<const char*>(src->k);
+    a.src_v = reinterpret_cast<const char*>(src->v);
+    a.dst_block_bytes = dst->block_stride * eb;
+    a.dst_layer_bytes = dst->layer_stride * eb;
+    a.src_block_bytes = src->block_stride * eb;
+    a.src_layer_bytes = src->layer_stride * eb;
+    a.slab_bytes = slab;
+    a.dst_num_blocks = dst->num_blocks;
+    a.src_num_blocks = src->num_blocks;
+    a.num_layers = dst->num_layers;
+    a.pairs = pairs;
+    a.num_pairs = num_pairs;
+    if (dst->num_layers > 32767) return PA_ERR_UNSUPPORTED;
+    if (pa::launch_copy(a, stream) != hipSuccess) return PA_ERR_HIP;
+    return PA_OK;
+  }
+
+  // host pairs: validate everything before the first copy
+  std::vector<int64_t> dsts(num_pairs);
+  for (int i = 0; i < num_pairs; ++i) {
+    const int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= src->num_blocks || d < 0 || d >= dst->num_blocks) return PA_ERR_INVALID_ARG;
+    dsts[i] = d;
+  }
+  std::sort(dsts.begin(), dsts.end());
+  if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end()) return PA_ERR_INVALID_ARG;
+
+  const hipMemcpyKind kind = dir == PA_COPY_H2D ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+  const int L = dst->num_layers;
+  const int64_t block_bytes = slab * L;
+  // a block is one contiguous range when its layers sit back to back; runs of
+  // consecutive ids are one range when blocks are packed back to back too
+  const bool dst_contig = L == 1 || dst->layer_stride * eb == slab;
+  const bool src_contig = L == 1 || src->layer_stride * eb == slab;
+  const bool packed = dst_contig && src_contig && dst->block_stride * eb == block_bytes &&
+                      src->block_stride * eb == block_bytes;
+  int i = 0;
+  while (i < num_pairs) {
+    const int64_t s0 = pairs[2 * i], d0 = pairs[2 * i + 1];
+    int run = 1;
+    if (packed) {
+      while (i + run < num_pairs && pairs[2 * (i + run)] == s0 + run &&
+             pairs[2 * (i + run) + 1] == d0 + run)
+        ++run;
+    }
+    for (int kvsel = 0; kvsel < 2; ++kvsel) {
+      const char* sb = reinterpret_cast<const char*>(kvsel ? src->v : src->k);
+      char* db = reinterpret_cast<char*>(kvsel ? dst->v : dst->k);
+      if (dst_contig && src_contig) {
+        if (hipMemcpyAsync(db + d0 * dst->block_stride * eb, sb + s0 * src->block_stride * eb,
+                           (size_t)run * (size_t)block_bytes, kind, stream) != hipSuccess)
+          return PA_ERR_HIP;
+        continue;
+      }
+      for (int l = 0; l < L; ++l)
+        if (hipMemcpyAsync(db + d0 * dst->block_stride * eb + l * dst->layer_stride * eb,
+                           sb + s0 * src->block_stride * eb + l * src->layer_stride * eb,
+                           (size_t)slab, kind, stream) != hipSuccess)
+          return PA_ERR_HIP;
+    }
+    i += run;
+  }
+  return PA_OK;
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported size, dtype or alignment";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch or copy failed";
+  }
+  return "unknown pa_status";
+}
+
+const char* pa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// pa_internal.h — launch parameters shared between the C-ABI layer and the
+// kernels. Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Largest number of block-table entries one decode partition may span.
+constexpr int PA_MAX_PART_BLOCKS = 1024;
+
+struct DecodeParams {
+  const void* k_pool;
+  const void* v_pool;
+  int64_t block_stride;      // elements
+  int64_t layer_offset;      // elements: layer * layer_stride
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t log2_block_size;
+  int32_t head_dim;
+  float v_scale;             // applied to the output (1 unless FP8)
+  float qk_scale_log2;       // scale * log2(e) (* k_scale for FP8)
+  const void* q;
+  void* out;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t part_tokens;       // tokens per partition
+  int32_t num_parts;         // partitions per sequence in the launch grid
+  float* ws_o;               // [num_seqs][num_q_heads][num_parts][head_dim]
+  float* ws_m;               // [num_seqs][num_q_heads][num_parts]
+  float* ws_l;               // [num_seqs][num_q_heads][num_parts]
+};
+
+struct WriteParams {
+  void* k_pool;
+  void* v_pool;
+  int64_t block_stride;
+  int64_t layer_offset;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t log2_block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  float k_scale;
+  float v_scale;
+  const void* k_src;
+  const void* v_src;
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+};
+
+struct CopyParams {
+  char* dst_k;
+  char* dst_v;
+  const char* src_k;
+  const char* src_v;
+  int64_t dst_block_bytes;   // block stride in bytes
+  int64_t dst_layer_bytes;   // layer stride in bytes
+  int64_t src_block_bytes;
+  int64_t src_layer_bytes;
+  int64_t slab_bytes;        // bytes of one (block, layer): heads * slots * dim
+  int32_t dst_num_blocks;
+  int32_t src_num_blocks;
+  int32_t num_layers;
+  const int64_t* pairs;      // device [num_pairs][2]
+  int32_t num_pairs;
+};
+
+hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st);
+hipError_t launch_merge(const DecodeParams& a, int q_ty, hipStream_t st);
+hipError_t launch_write(const WriteParams& a, int src_ty, int dst_ty, hipStream_t st);
+hipError_t launch_copy(const CopyParams& a, hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,126 @@
+"""Helpers for GPU tests: put a workload's inputs on the device, drive the
+library through its Python binding, and run the same steps in the oracle."""
+
+import sys
+
+import numpy as np
+import torch
+
+import paged_kv_cache_44_amd as pa
+import workloads
+from oracle import codecs, paged
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2, "fp8_e4m3": 3e-2}
+
+_TORCH_CODE = {np.uint8: torch.uint8, np.uint16: torch.int16, np.uint32: torch.int32}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def codes_to_tensor(codes: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Storage codes -> a torch tensor of the storage dtype (same bytes)."""
+    codes = np.ascontiguousarray(codes)
+    if dtype == "fp8_e4m3":
+        t = torch.from_numpy(codes.view(np.uint8))
+    elif dtype == "f32":
+        t = torch.from_numpy(codes.view(np.int32)).view(torch.float32)
+    elif dtype == "f16":
+        t = torch.from_numpy(codes.view(np.int16)).view(torch.float16)
+    else:
+        t = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16)
+    return t.to(device) if device != "cpu" else t.clone()
+
+
+def tensor_codes(t: torch.Tensor) -> np.ndarray:
+    """A tensor's bytes as unsigned codes on the host."""
+    t = t.detach().contiguous().cpu()
+    if t.element_size() == 1:
+        return t.view(torch.uint8).numpy().copy()
+    if t.element_size() == 2:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.view(torch.int32).numpy().view(np.uint32).copy()
+
+
+def geometry(wl) -> paged.Geometry:
+    return paged.Geometry(wl.num_blocks, wl.num_layers, wl.num_kv_heads, wl.block_size,
+                          wl.head_dim)
+
+
+class DeviceState:
+    """Device pools of a workload plus the matching oracle pools."""
+
+    def __init__(self, wl, poison=True):
+        self.wl = wl
+        pool = wl.empty_pool() if poison else np.zeros(wl.pool_elements(),
+                                                       dtype=workloads.CODE_TYPE[wl.pool_dtype])
+        self.ok = pool.copy()                      # oracle K pool codes
+        self.ov = pool.copy()                      # oracle V pool codes
+        kt = codes_to_tensor(pool, wl.pool_dtype)
+        vt = codes_to_tensor(pool, wl.pool_dtype)
+        self.cache = pa.KVCache(kt, vt, wl.pool_dtype, wl.num_blocks, wl.num_layers,
+                                wl.num_kv_heads, wl.block_size, wl.head_dim,
+                                k_scale=wl.k_scale, v_scale=wl.v_scale)
+        self.geom = geometry(wl)
+
+    def write(self, k_codes, v_codes, slots, src_dtype=None, oracle=True):
+        wl = self.wl
+        src_dtype = src_dtype or wl.src_dtype
+        kt = codes_to_tensor(k_codes, src_dtype)
+        vt = codes_to_tensor(v_codes, src_dtype)
+        st = torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int64)).cuda()
+        pa.write_kv(self.cache, wl.layer, kt, vt, st)
+        if oracle:
+            self.ok, self.ov = paged.write_kv(self.ok, self.ov, self.geom, wl.pool_dtype,
+                                              wl.layer, k_codes, v_codes, src_dtype, slots,
+                                              wl.k_scale, wl.v_scale)
+
+    def copy_d2d(self, pairs):
+        p = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)).cuda()
+        pa.copy_blocks(self.cache, self.cache, p, "d2d")
+        self.ok, self.ov = paged.copy_blocks(self.ok, self.ov, self.geom, self.ok, self.ov,
+                                             self.geom, pairs, same_pool=True)
+
+    def pools_equal_oracle(self):
+        torch.cuda.synchronize()
+        gk = tensor_codes(self.cache.k)
+        gv = tensor_codes(self.cache.v)
+        return np.array_equal(gk, self.ok) and np.array_equal(gv, self.ov), gk, gv
+
+    def decode(self, q_codes=None, tables=None, ctx=None, max_ctx=None, scale=None, split=False):
+        wl = self.wl
+        q_codes = wl.q if q_codes is None else q_codes
+        tables = wl.block_tables if tables is None else tables
+        ctx = wl.context_lens if ctx is None else ctx
+        max_ctx = int(np.max(ctx)) if max_ctx is None else max_ctx
+        scale = wl.scale if scale is None else scale
+        q = codes_to_tensor(q_codes, wl.q_dtype)
+        tt = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).cuda()
+        ct = torch.from_numpy(np.ascontiguousarray(ctx, dtype=np.int32)).cuda()
+        if split:
+            out = torch.empty_like(q)
+            n = pa.decode_workspace_size(self.cache, q.shape[0], q.shape[1], max_ctx)
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+            pa.decode_attend(self.cache, wl.layer, q, tt, ct, max_ctx, scale, out, ws)
+            pa.decode_merge(self.cache, wl.layer, q, tt, ct, max_ctx, scale, out, ws)
+        else:
+            out = pa.decode(self.cache, wl.layer, q, tt, ct, max_ctx, scale)
+        torch.cuda.synchronize()
+        return codecs.decode(tensor_codes(out), wl.q_dtype)
+
+    def oracle_decode(self, q_codes=None, tables=None, ctx=None, scale=None, seqs=None):
+        wl = self.wl
+        return paged.decode(wl.q if q_codes is None else q_codes, wl.q_dtype, self.ok, self.ov,
+                            self.geom, wl.pool_dtype, wl.layer,
+                            wl.block_tables if tables is None else tables,
+                            wl.context_lens if ctx is None else ctx,
+                            wl.scale if scale is None else scale, wl.k_scale, wl.v_scale,
+                            seqs=seqs)
+
+
+def max_err(gpu, ref, rows=None):
+    if rows is not None:
+        gpu, ref = gpu[rows], ref[rows]
+    return float(np.max(np.abs(gpu - ref), initial=0.0))

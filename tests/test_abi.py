@@ -1,0 +1,109 @@
+"""The C-ABI library on the CPU: it loads, exports every function
+include/pa.h declares, and rejects bad arguments before any HIP call (so no
+GPU is needed here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_44_amd import _binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pa.h")
+FAKE = 0x100000          # aligned, never dereferenced: every call below fails or
+                         # returns before touching memory
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(pa_lib):
+    for name in declared_functions():
+        assert hasattr(pa_lib, name), name
+    assert pa_lib.pa_version().decode().count(".") == 2
+
+
+def test_status_strings(pa_lib):
+    for s in range(5):
+        assert pa_lib.pa_status_string(s).decode().startswith("PA_")
+    assert b"unknown" in pa_lib.pa_status_string(99)
+
+
+def _cache(dtype=B.PA_BF16, blocks=100, layers=1, heads=8, bs=16, dim=128, ks=1.0, vs=1.0):
+    ls = heads * bs * dim
+    return B.PaKvCache(FAKE, FAKE, dtype, blocks, layers, heads, bs, dim, layers * ls, ls, ks, vs)
+
+
+def test_workspace_and_partition_queries(pa_lib):
+    c = _cache()
+    p = pa_lib.pa_decode_partition_tokens(ctypes.byref(c), 256, 32, 4000)
+    assert p >= 64 and p % 64 == 0
+    parts = -(-4000 // p)
+    ws = pa_lib.pa_decode_workspace_size(ctypes.byref(c), 256, 32, 4000)
+    if parts > 1:
+        assert ws >= 256 * 32 * parts * (128 + 2) * 4
+    # one partition only: no workspace needed
+    assert pa_lib.pa_decode_workspace_size(ctypes.byref(c), 4, 32, 16) == 0
+    # invalid geometry -> 0
+    bad = _cache(bs=12)
+    assert pa_lib.pa_decode_partition_tokens(ctypes.byref(bad), 4, 32, 100) == 0
+
+
+def _decode(lib, c, q_dtype=B.PA_BF16, hq=32, seqs=4, max_ctx=100, ws=None, ws_bytes=0,
+            q=FAKE, out=FAKE, tables=FAKE, ctx=FAKE, scale=0.1, layer=0):
+    return lib.pa_decode(ctypes.byref(c), layer, q, q_dtype, out, tables, 8, ctx, max_ctx, seqs,
+                         hq, scale, ws, ws_bytes, None)
+
+
+def test_decode_argument_errors(pa_lib):
+    c = _cache()
+    assert _decode(pa_lib, c, seqs=0) == B.PA_OK                      # nothing to do
+    assert _decode(pa_lib, c, hq=30) == B.PA_ERR_INVALID_ARG          # not a multiple of 8
+    assert _decode(pa_lib, c, hq=8 * 16) == B.PA_ERR_UNSUPPORTED      # group of 16
+    assert _decode(pa_lib, c, q_dtype=B.PA_F16) == B.PA_ERR_UNSUPPORTED
+    assert _decode(pa_lib, c, layer=1) == B.PA_ERR_INVALID_ARG
+    assert _decode(pa_lib, c, q=None) == B.PA_ERR_INVALID_ARG
+    assert _decode(pa_lib, c, scale=float("inf")) == B.PA_ERR_INVALID_ARG
+    assert _decode(pa_lib, c, max_ctx=5000) == B.PA_ERR_WORKSPACE     # needs a workspace
+    assert _decode(pa_lib, _cache(dim=96)) == B.PA_ERR_UNSUPPORTED
+    assert _decode(pa_lib, _cache(dtype=B.PA_F32, dim=128), q_dtype=B.PA_F32) == B.PA_ERR_UNSUPPORTED
+    assert _decode(pa_lib, _cache(ks=0.5)) == B.PA_ERR_INVALID_ARG    # scale on a bf16 pool
+    assert _decode(pa_lib, _cache(dtype=B.PA_FP8_E4M3, ks=0.0)) == B.PA_ERR_INVALID_ARG
+
+
+def test_write_argument_errors(pa_lib):
+    c = _cache()
+    w = lambda **kw: pa_lib.pa_write_kv(ctypes.byref(kw.get("c", c)), kw.get("layer", 0), FAKE,
+                                        FAKE, kw.get("src", B.PA_BF16), FAKE, kw.get("n", 5), None)
+    assert w(n=0) == B.PA_OK
+    assert w(n=-1) == B.PA_ERR_INVALID_ARG
+    assert w(src=B.PA_F16) == B.PA_ERR_INVALID_ARG          # no conversion into a bf16 pool
+    assert w(layer=3) == B.PA_ERR_INVALID_ARG
+    f8 = _cache(dtype=B.PA_FP8_E4M3, ks=0.1, vs=0.2)
+    assert w(c=f8, src=B.PA_FP8_E4M3, n=0) == B.PA_OK
+    assert w(c=_cache(bs=0)) == B.PA_ERR_INVALID_ARG
+
+
+def test_host_copy_pairs_validated_before_any_copy(pa_lib):
+    c = _cache(blocks=10)
+    h = _cache(blocks=4)
+
+    def run(pairs, direction=B.PA_COPY_H2D, dst=c, src=h):
+        arr = (ctypes.c_int64 * (2 * len(pairs)))(*[x for p in pairs for x in p])
+        return pa_lib.pa_copy_blocks(ctypes.byref(dst), ctypes.byref(src), arr, len(pairs),
+                                     direction, None)
+    assert run([(0, 10)]) == B.PA_ERR_INVALID_ARG            # dst out of range
+    assert run([(4, 1)]) == B.PA_ERR_INVALID_ARG             # src out of range
+    assert run([(0, 3), (1, 3)]) == B.PA_ERR_INVALID_ARG     # duplicate destination
+    assert run([(0, 1)], direction=7) == B.PA_ERR_INVALID_ARG
+    other = _cache(blocks=4, bs=8)
+    assert run([(0, 1)], src=other) == B.PA_ERR_INVALID_ARG  # geometry differs
+    assert run([], direction=B.PA_COPY_D2D) == B.PA_OK

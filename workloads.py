@@ -382,6 +382,24 @@ def config5(seed: int = 5, num_seqs: int = 8, ctx_min: int = 8192, ctx_max: int 
     return wl
 
 
+def custom(seed: int, ctx, *, pool_dtype: str, q_dtype: str, num_q_heads: int,
+           num_kv_heads: int, head_dim: int, block_size: int, src_dtype: str = None,
+           scale_from_data: bool = True) -> Workload:
+    """A small workload with given context lengths (edge cases, sweeps).
+
+    FP8 pools take bf16 sources (unless ``src_dtype`` says otherwise) and
+    per-tensor scales fp32(max |x|) / 448."""
+    rng = np.random.default_rng(seed)
+    src = src_dtype or (BF16 if pool_dtype == FP8 else pool_dtype)
+    wl = _paged_workload(f"custom_{seed}", seed, rng, np.asarray(ctx, dtype=np.int32),
+                         pool_dtype=pool_dtype, src_dtype=src, q_dtype=q_dtype,
+                         hq=num_q_heads, hkv=num_kv_heads, d=head_dim, B=block_size)
+    if pool_dtype == FP8 and scale_from_data and wl.write_k.shape[0]:
+        wl.k_scale = fp8_scale(wl.write_k, src)
+        wl.v_scale = fp8_scale(wl.write_v, src)
+    return wl
+
+
 def make(config: int, **kw) -> Workload:
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[config](**kw)
 
