@@ -1,0 +1,266 @@
+"""Benchmark of the paged-decode hot path on one MI355X.
+
+A step is one pass of the hot path over one batch: the slot write of every
+sequence's newest token (pa_write_kv), then paged decode attention over every
+sequence's whole context (pa_decode_attend + pa_decode_merge). The default
+workload is the GQA bf16 decode batch: 256 sequences, 32 query / 8 KV heads x
+128, block size 16, contexts of a lognormal ~850-token prompt plus a
+1..250-token answer (seeded synthetic data; the pages publish no dataset).
+
+Prints ONE JSON line: value = algorithmic bytes of a step / step time, in
+GB/s (KV of every context token for every KV head, queries, outputs, block
+table entries and context lengths, plus the slot write's source and pool
+bytes). Inputs are resident in HBM before timing starts. Also reported:
+the dominant kernel's roofline (HIP events on the launch stream), the CPU
+oracle timed on a bounded sample, and an L2/Infinity-Cache-flushed per-call
+decode time.
+
+    python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_44_amd", "csrc", f)
+                  for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target seconds of CPU oracle work for the baseline sample")
+    ap.add_argument("--flush-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def codes_tensor(codes, dtype, device):
+    import torch
+    codes = np.ascontiguousarray(codes)
+    if dtype == "fp8_e4m3":
+        t = torch.from_numpy(codes.view(np.uint8))
+    elif dtype == "f32":
+        t = torch.from_numpy(codes.view(np.int32)).view(torch.float32)
+    elif dtype == "f16":
+        t = torch.from_numpy(codes.view(np.int16)).view(torch.float16)
+    else:
+        t = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def attend_bytes(wl) -> int:
+    """Algorithmic bytes the attention kernel must move: every context token's
+    K and V for every KV head, the queries, the block-table entries in use and
+    the context lengths (outputs are excluded: the merge writes part of them)."""
+    import workloads
+    ctx = wl.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * wl.num_kv_heads * wl.head_dim * 2 * workloads.ELEM_BYTES[wl.pool_dtype]
+    q = wl.num_seqs * wl.num_q_heads * wl.head_dim * workloads.ELEM_BYTES[wl.q_dtype]
+    tables = int(np.sum(-(-ctx // wl.block_size))) * 4 + 4 * wl.num_seqs
+    return kv + q + tables
+
+
+def load_traffic(kernel: str, workload: str):
+    """Measured HBM bytes per launch from the committed counter summary, or
+    None when it is missing or the kernel source changed since."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle, as it is, on the host cores: its slot write builds the pool
+    on the host, then its decode runs sequence by sequence (cycling through
+    the workload) until about target_s seconds of decode work are done."""
+    from threadpoolctl import threadpool_limits
+    from oracle import paged
+    import workloads
+    geom = paged.Geometry(wl.num_blocks, wl.num_layers, wl.num_kv_heads, wl.block_size,
+                          wl.head_dim)
+    pool = wl.empty_pool()
+    ok, ov = paged.write_kv(pool, pool.copy(), geom, wl.pool_dtype, wl.layer, wl.write_k,
+                            wl.write_v, wl.src_dtype, wl.write_slots, wl.k_scale, wl.v_scale)
+    done_bytes, seqs = 0, 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        s = 0
+        while time.perf_counter() - t0 < target_s:
+            paged.decode(wl.q, wl.q_dtype, ok, ov, geom, wl.pool_dtype, wl.layer,
+                         wl.block_tables, wl.context_lens, wl.scale, wl.k_scale, wl.v_scale,
+                         seqs=[s])
+            done_bytes += workloads.decode_bytes(wl, wl.context_lens[s:s + 1])
+            seqs += 1
+            s = (s + 1) % wl.num_seqs
+        dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{seqs} single-sequence decodes (sequences 0..{min(seqs, wl.num_seqs) - 1} "
+                      f"of the workload) in {dt:.1f} s; numpy fp64, BLAS limited to 1 thread",
+            "seq_per_s": round(seqs / dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    wl = workloads.make(args.config)
+    print(f"[bench] workload {wl.name}: {wl.num_seqs} seqs, ctx mean "
+          f"{wl.context_lens.mean():.1f} max {wl.max_context_len}, pool {wl.num_blocks} blocks",
+          file=sys.stderr, flush=True)
+
+    pool = wl.empty_pool()
+    cache = pa.KVCache(codes_tensor(pool, wl.pool_dtype, dev), codes_tensor(pool, wl.pool_dtype, dev),
+                       wl.pool_dtype, wl.num_blocks, wl.num_layers, wl.num_kv_heads,
+                       wl.block_size, wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    # fill the pool (untimed): every context token; shared-prefix workloads
+    # copy their shared blocks in between, as the workload prescribes
+    kk = codes_tensor(wl.write_k, wl.src_dtype, dev)
+    vv = codes_tensor(wl.write_v, wl.src_dtype, dev)
+    ss = torch.from_numpy(wl.write_slots).to(dev)
+    if "cow_pairs" in wl.extra:
+        n0 = wl.extra["num_prefix_tokens_written"]
+        pa.write_kv(cache, wl.layer, kk[:n0], vv[:n0], ss[:n0])
+        pa.copy_blocks(cache, cache, torch.from_numpy(wl.extra["cow_pairs"]).to(dev), "d2d")
+        pa.write_kv(cache, wl.layer, kk[n0:], vv[n0:], ss[n0:])
+    else:
+        pa.write_kv(cache, wl.layer, kk, vv, ss)
+    step_idx = wl.step_token[wl.step_token >= 0]
+    step_k = kk[torch.from_numpy(step_idx).to(dev)].contiguous()
+    step_v = vv[torch.from_numpy(step_idx).to(dev)].contiguous()
+    step_slots = ss[torch.from_numpy(step_idx).to(dev)].contiguous()
+    del kk, vv, ss
+    q = codes_tensor(wl.q, wl.q_dtype, dev)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    max_ctx = wl.max_context_len
+    S, Hq = wl.num_seqs, wl.num_q_heads
+    ws = torch.empty(max(1, pa.decode_workspace_size(cache, S, Hq, max_ctx)), dtype=torch.uint8,
+                     device=dev)
+    part = pa.decode_partition_tokens(cache, S, Hq, max_ctx)
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; partition {part} tokens",
+          file=sys.stderr, flush=True)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        pa.write_kv(cache, wl.layer, step_k, step_v, step_slots)
+        if i is not None:
+            ev[i][0].record()
+        pa.decode_attend(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
+        if i is not None:
+            ev[i][1].record()
+        pa.decode_merge(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    attend_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # flushed per-call decode time: a 512 MiB scratch write evicts the L2s and
+    # the Infinity Cache before each call (untimed)
+    scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    fl = []
+    for _ in range(args.flush_iters):
+        scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pa.decode_attend(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
+        pa.decode_merge(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
+        b.record()
+        torch.cuda.synchronize()
+        fl.append(a.elapsed_time(b))
+    del scratch
+
+    step_bytes = workloads.decode_bytes(wl) + workloads.write_bytes(wl, len(step_idx))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ab = attend_bytes(wl)
+    achieved = ab / (attend_ms * 1e-3) / 1e9
+    traffic = load_traffic("attend", wl.name)
+    rec = {
+        "metric": "paged-decode KV GB/s and % of MI355X HBM peak; sequences/s at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8-e4m3 KV, bf16 q"}[wl.pool_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "block_size": wl.block_size,
+            "context_mean": round(float(wl.context_lens.mean()), 1),
+            "context_max": max_ctx, "context_tokens": int(wl.context_lens.sum()),
+            "partition_tokens": part, "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "step_bytes": step_bytes,
+        "decode_flushed_ms": {"median": round(float(np.median(fl)), 5),
+                              "p10": round(float(np.percentile(fl, 10)), 5),
+                              "p90": round(float(np.percentile(fl, 90)), 5)},
+        "roofline": {"kernel": "attend_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": ab,
+                     "avg_launch_ms": round(attend_ms, 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del cache
+        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

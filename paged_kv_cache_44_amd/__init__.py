@@ -78,6 +78,27 @@ class KVCache:
             self.layer_stride = self.num_kv_heads * self.block_size * self.head_dim
         if self.block_stride < 0:
             self.block_stride = self.num_layers * self.layer_stride
+        need = self.required_elements()
+        eb = ELEM_BYTES[self.dtype]
+        for name, t in (("k", self.k), ("v", self.v)):
+            if not t.is_contiguous():
+                raise ValueError(f"pool {name} must be contiguous")
+            if t.element_size() != eb:
+                raise ValueError(f"pool {name} has {t.element_size()}-byte elements, "
+                                 f"{self.dtype} needs {eb}")
+            if t.numel() < need:
+                raise ValueError(f"pool {name} holds {t.numel()} elements, geometry needs {need}")
+
+    def required_elements(self) -> int:
+        """Elements the geometry addresses (the last block's last element + 1)."""
+        if self.num_blocks <= 0:
+            return 0
+        return ((self.num_blocks - 1) * self.block_stride + (self.num_layers - 1) * self.layer_stride
+                + self.num_kv_heads * self.block_size * self.head_dim)
+
+    @property
+    def is_device(self) -> bool:
+        return self.k.is_cuda and self.v.is_cuda
 
     @classmethod
     def empty(cls, dtype: str, num_blocks: int, num_layers: int, num_kv_heads: int,
@@ -101,9 +122,26 @@ class KVCache:
                            self.layer_stride, self.k_scale, self.v_scale)
 
 
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_device(*ts):
+    for t in ts:
+        _need(t.is_cuda and t.is_contiguous(), "tensors must be contiguous device tensors")
+
+
 def write_kv(cache: KVCache, layer: int, k: torch.Tensor, v: torch.Tensor,
              slot_mapping: torch.Tensor, stream=None) -> None:
     """Store k, v [T][H_kv][D] at their slots (int64 [T], negative = skip)."""
+    _need(cache.is_device, "write_kv needs a device pool")
+    _on_device(k, v, slot_mapping)
+    T = int(slot_mapping.numel())
+    shape = (T, cache.num_kv_heads, cache.head_dim)
+    _need(tuple(k.shape) == shape and tuple(v.shape) == shape, f"k, v must be {shape}")
+    _need(k.dtype == v.dtype, "k and v dtypes differ")
+    _need(slot_mapping.dtype == torch.int64, "slot_mapping must be int64")
     c = cache.struct()
     st = _lib().pa_write_kv(ctypes.byref(c), layer, _ptr(k), _ptr(v), DTYPES[dtype_name(k)],
                             _ptr(slot_mapping), int(slot_mapping.numel()), _stream(stream))
@@ -126,12 +164,24 @@ def decode_partition_tokens(cache: KVCache, num_seqs: int, num_q_heads: int,
 
 def _decode_call(fn_name, cache, layer, q, block_tables, context_lens, max_context_len, scale,
                  out, workspace, stream):
+    _need(cache.is_device, "decode needs a device pool")
+    _need(q.dim() == 3 and q.shape[2] == cache.head_dim, "q must be [S][H_q][head_dim]")
     S, Hq, D = q.shape
+    _on_device(q, block_tables, context_lens)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens must be int32 [S]")
+    if out is not None:
+        _on_device(out)
+        _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
         n = decode_workspace_size(cache, S, Hq, max_context_len)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _on_device(workspace)
     c = cache.struct()
     st = getattr(_lib(), fn_name)(
         ctypes.byref(c), layer, _ptr(q), DTYPES[dtype_name(q)], _ptr(out), _ptr(block_tables),
@@ -172,6 +222,19 @@ def copy_blocks(dst: KVCache, src: KVCache, pairs: torch.Tensor, direction: str 
                 stream=None) -> None:
     """Copy whole blocks: pairs int64 [N][2] = (src_block, dst_block); device
     memory for "d2d", host memory for "h2d" / "d2h"."""
+    _need(pairs.dtype == torch.int64 and pairs.is_contiguous() and
+          (pairs.numel() == 0 or (pairs.dim() == 2 and pairs.shape[1] == 2)),
+          "pairs must be contiguous int64 [N][2]")
+    if direction == "d2d":
+        _need(dst.is_device and src.is_device and pairs.is_cuda, "d2d needs device pools and pairs")
+    elif direction == "h2d":
+        _need(dst.is_device and not src.is_device and not pairs.is_cuda,
+              "h2d copies a host pool into a device pool with host pairs")
+    elif direction == "d2h":
+        _need(src.is_device and not dst.is_device and not pairs.is_cuda,
+              "d2h copies a device pool into a host pool with host pairs")
+    else:
+        raise ValueError(f"unknown direction {direction!r}")
     d, s = dst.struct(), src.struct()
     n = int(pairs.shape[0]) if pairs.dim() == 2 else 0
     st = _lib().pa_copy_blocks(ctypes.byref(d), ctypes.byref(s), _ptr(pairs), n,
