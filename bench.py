@@ -54,7 +54,34 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target seconds of CPU oracle work for the baseline sample")
     ap.add_argument("--flush-iters", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch) a few times: the "
+                         "reference kernel for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration(reps: int = 5):
+    """A plain device-to-device copy of 1 GiB (read 1 GiB, write 1 GiB), timed;
+    its counter readings calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = float(np.median(ts))
+    print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30,
+                      "median_ms": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
 
 
 def codes_tensor(codes, dtype, device):
@@ -105,9 +132,14 @@ def cpu_baseline(wl, target_s: float):
     import workloads
     geom = paged.Geometry(wl.num_blocks, wl.num_layers, wl.num_kv_heads, wl.block_size,
                           wl.head_dim)
-    pool = wl.empty_pool()
-    ok, ov = paged.write_kv(pool, pool.copy(), geom, wl.pool_dtype, wl.layer, wl.write_k,
-                            wl.write_v, wl.src_dtype, wl.write_slots, wl.k_scale, wl.v_scale)
+    ok = wl.empty_pool()
+    ov = ok.copy()
+    for op in workloads.fill_plan(wl):
+        if op[0] == "write":
+            ok, ov = paged.write_kv(ok, ov, geom, wl.pool_dtype, wl.layer, op[1], op[2],
+                                    wl.src_dtype, op[3], wl.k_scale, wl.v_scale)
+        else:
+            ok, ov = paged.copy_blocks(ok, ov, geom, ok, ov, geom, op[1], same_pool=True)
     done_bytes, seqs = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -138,6 +170,9 @@ def main():
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     t_setup = time.perf_counter()
     wl = workloads.make(args.config)
@@ -149,23 +184,18 @@ def main():
     cache = pa.KVCache(codes_tensor(pool, wl.pool_dtype, dev), codes_tensor(pool, wl.pool_dtype, dev),
                        wl.pool_dtype, wl.num_blocks, wl.num_layers, wl.num_kv_heads,
                        wl.block_size, wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
-    # fill the pool (untimed): every context token; shared-prefix workloads
-    # copy their shared blocks in between, as the workload prescribes
-    kk = codes_tensor(wl.write_k, wl.src_dtype, dev)
-    vv = codes_tensor(wl.write_v, wl.src_dtype, dev)
-    ss = torch.from_numpy(wl.write_slots).to(dev)
-    if "cow_pairs" in wl.extra:
-        n0 = wl.extra["num_prefix_tokens_written"]
-        pa.write_kv(cache, wl.layer, kk[:n0], vv[:n0], ss[:n0])
-        pa.copy_blocks(cache, cache, torch.from_numpy(wl.extra["cow_pairs"]).to(dev), "d2d")
-        pa.write_kv(cache, wl.layer, kk[n0:], vv[n0:], ss[n0:])
-    else:
-        pa.write_kv(cache, wl.layer, kk, vv, ss)
+    # fill the pool (untimed) with every context token, as the workload prescribes
+    for op in workloads.fill_plan(wl):
+        if op[0] == "write":
+            pa.write_kv(cache, wl.layer, codes_tensor(op[1], wl.src_dtype, dev),
+                        codes_tensor(op[2], wl.src_dtype, dev), torch.from_numpy(op[3]).to(dev))
+        else:
+            pa.copy_blocks(cache, cache, torch.from_numpy(op[1]).to(dev), "d2d")
+    # the step's own write: each sequence's newest token, stored again at its slot
     step_idx = wl.step_token[wl.step_token >= 0]
-    step_k = kk[torch.from_numpy(step_idx).to(dev)].contiguous()
-    step_v = vv[torch.from_numpy(step_idx).to(dev)].contiguous()
-    step_slots = ss[torch.from_numpy(step_idx).to(dev)].contiguous()
-    del kk, vv, ss
+    step_k = codes_tensor(wl.write_k[step_idx], wl.src_dtype, dev)
+    step_v = codes_tensor(wl.write_v[step_idx], wl.src_dtype, dev)
+    step_slots = torch.from_numpy(wl.write_slots[step_idx]).to(dev)
     q = codes_tensor(wl.q, wl.q_dtype, dev)
     out = torch.empty_like(q)
     tables = torch.from_numpy(wl.block_tables).to(dev)

@@ -404,6 +404,26 @@ def make(config: int, **kw) -> Workload:
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[config](**kw)
 
 
+def fill_plan(wl: Workload):
+    """Steps that put every context token of the workload into its pool, in
+    order: ``("write", k, v, slots)`` and ``("copy", pairs)`` (device block
+    copies). The shared-prefix workload writes its prompts, copies the last
+    prompt block for the samples that privatise it, then writes the private
+    tokens; the long FP8 workload's victim is written straight into the
+    blocks it is restored into (the state after its swap-in)."""
+    if "cow_pairs" in wl.extra:
+        n0 = wl.extra["num_prefix_tokens_written"]
+        return [("write", wl.write_k[:n0], wl.write_v[:n0], wl.write_slots[:n0]),
+                ("copy", wl.extra["cow_pairs"]),
+                ("write", wl.write_k[n0:], wl.write_v[n0:], wl.write_slots[n0:])]
+    plan = [("write", wl.write_k, wl.write_v, wl.write_slots)]
+    if "victim_k" in wl.extra:
+        after = [int(b) for b in wl.extra["victim_blocks_after"]]
+        plan.append(("write", wl.extra["victim_k"], wl.extra["victim_v"],
+                     _slots_of(after, wl.extra["victim_tokens"], wl.block_size)))
+    return plan
+
+
 # --------------------------------------------------------------------------
 # byte accounting of the measurements
 # --------------------------------------------------------------------------
