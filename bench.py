@@ -276,9 +276,9 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_per_s": round(S / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
-        "decode_flushed_ms": {"median": round(float(np.median(fl)), 5),
-                              "p10": round(float(np.percentile(fl, 10)), 5),
-                              "p90": round(float(np.percentile(fl, 90)), 5)},
+        "decode_flushed_ms": ({"median": round(float(np.median(fl)), 5),
+                               "p10": round(float(np.percentile(fl, 10)), 5),
+                               "p90": round(float(np.percentile(fl, 90)), 5)} if fl else None),
         "roofline": {"kernel": "attend_kernel", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -110,13 +110,14 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
   pa_status st = check_cache(c, false);
   if (st != PA_OK) return st;
   if (num_seqs < 0 || max_ctx < 0) return PA_ERR_INVALID_ARG;
-  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (c->num_kv_heads > 65535 || num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
   int g = 0;
   st = decode_supported(c, num_q_heads, q_dtype, &g);
   if (st != PA_OK) return st;
   plan->g = g;
   plan->part_tokens = choose_part_tokens(c, g, num_seqs, max_ctx);
   plan->num_parts = std::max(1, (max_ctx + plan->part_tokens - 1) / plan->part_tokens);
+  if (plan->num_parts > 65535) return PA_ERR_UNSUPPORTED;   // grid z limit
   if (plan->num_parts > 1) {
     const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
     const size_t o = rows * c->head_dim * sizeof(float);
@@ -192,8 +193,11 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
     a.ws_l = reinterpret_cast<float*>(w + o + ml);
   }
   if (phases & PHASE_ATTEND) {
-    if (pa::launch_attend(a, (int)cache->dtype, (int)q_dtype, plan.g, stream) != hipSuccess)
-      return PA_ERR_HIP;
+    const hipError_t e =
+        pa::mfma_supported((int)cache->dtype, (int)q_dtype, cache->head_dim, plan.g)
+            ? pa::launch_attend_mfma(a, (int)cache->dtype, (int)q_dtype, plan.g, stream)
+            : pa::launch_attend(a, (int)cache->dtype, (int)q_dtype, plan.g, stream);
+    if (e != hipSuccess) return PA_ERR_HIP;
   }
   if ((phases & PHASE_MERGE) && plan.num_parts > 1) {
     if (pa::launch_merge(a, (int)q_dtype, stream) != hipSuccess) return PA_ERR_HIP;

@@ -192,11 +192,14 @@ attend_kernel(const DecodeParams a) {
   __shared__ float s_wl[NW][G];
   __shared__ float s_wo[NW][G][D];
 
-  const int part = blockIdx.x;
+  // Grid (sequence, KV head, partition): workgroups are dealt to the 8 XCDs
+  // round-robin by linear id; rotating the sequence by the partition index
+  // spreads the partitions of one sequence over the XCDs.
+  const int part = blockIdx.z;
   const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
+  const int seq = (int)((blockIdx.x + (unsigned)part) % (unsigned)a.num_seqs);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int row = lane >> 4;
   const int c = lane & 15;
@@ -222,6 +225,15 @@ attend_kernel(const DecodeParams a) {
   const int lb0 = p0 >> lg;
   const int nlb = ((pend - 1) >> lg) - lb0 + 1;
 
+  // q registers for the G heads of this KV head
+  uint32_t qr[G][Q::QW];
+  {
+    const char* qbase = reinterpret_cast<const char*>(a.q);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      Q::load_q(qbase + (out_row0 + (int64_t)h * D) * TyInfo<QT>::bytes, c, qr[h]);
+  }
+
   if (tid == 0) s_bad = 0;
   __syncthreads();
   const int32_t* trow = a.block_tables + (int64_t)seq * a.max_blocks_per_seq + lb0;
@@ -232,15 +244,6 @@ attend_kernel(const DecodeParams a) {
   }
   __syncthreads();
   const bool bad_tbl = s_bad != 0;
-
-  // q registers for the G heads of this KV head
-  uint32_t qr[G][Q::QW];
-  {
-    const char* qbase = reinterpret_cast<const char*>(a.q);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      Q::load_q(qbase + (out_row0 + (int64_t)h * D) * TyInfo<QT>::bytes, c, qr[h]);
-  }
 
   const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
   const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
@@ -261,7 +264,10 @@ attend_kernel(const DecodeParams a) {
   const int nchunks = (ntok + CHUNK - 1) / CHUNK;
   const float qk_scale = a.qk_scale_log2;
 
+  // Issue the loads of one chunk: the 4 K rows first, then the 4 V rows, so
+  // the scores can start while the values are still in flight.
   auto load_chunk = [&](int k, uint32_t (&kr)[NL][KDW], uint32_t (&vr)[NL][KDW]) {
+    int64_t widx[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       int t = p0 + k * CHUNK + i * ROWS + row;
@@ -269,105 +275,115 @@ attend_kernel(const DecodeParams a) {
       const int lb = (t >> lg) - lb0;
       const int64_t eidx = (int64_t)s_tbl[lb] * a.block_stride + lane_off +
                            (int64_t)(t & (a.block_size - 1)) * D;
-      const int64_t widx = eidx * EB / 4;
-      gload<KDW>(kpool + widx, kr[i]);
-      gload<KDW>(vpool + widx, vr[i]);
+      widx[i] = eidx * EB / 4;
     }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) gload<KDW>(kpool + widx[i], kr[i]);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) gload<KDW>(vpool + widx[i], vr[i]);
   };
 
-  if (!bad_tbl) {
-    uint32_t kc[NL][KDW], vc[NL][KDW];
-    int k = wave;
-    if (k < nchunks) load_chunk(k, kc, vc);
-    for (; k < nchunks; k += NW) {
-      uint32_t kn[NL][KDW], vn[NL][KDW];
-      const int knext = k + NW;
-      if (knext < nchunks) load_chunk(knext, kn, vn);
+  // One chunk of 16 tokens: scores, online softmax, P.V.
+  auto process_chunk = [&](int k, uint32_t (&kr)[NL][KDW], uint32_t (&vr)[NL][KDW]) {
+    const int cbase = p0 + k * CHUNK;
+    const bool tail = cbase + CHUNK > pend;
 
-      const int cbase = p0 + k * CHUNK;
-      const bool tail = cbase + CHUNK > pend;
-
-      // --- scores --------------------------------------------------------
-      float sc[NV];
+    // --- scores --------------------------------------------------------
+    float sc[NV];
 #pragma unroll
-      for (int i = 0; i < NL; ++i)
+    for (int i = 0; i < NL; ++i)
 #pragma unroll
-        for (int h = 0; h < G; ++h) sc[i * G + h] = Q::dot(qr[h], kc[i]);
-      ReduceScatter<3, NV>::run(sc, c);
+      for (int h = 0; h < G; ++h) sc[i * G + h] = Q::dot(qr[h], kr[i]);
+    ReduceScatter<3, NV>::run(sc, c);
 
-      // --- online softmax on the values this lane owns --------------------
-      float pj[NF], alj[NF];
-      const int tok_i = c >> 2;                    // token slot of this lane's values
-      const bool valid = cbase + tok_i * ROWS + row < pend;
+    // --- online softmax on the values this lane owns --------------------
+    float pj[NF], alj[NF];
+    const int tok_i = c >> 2;                    // token slot of this lane's values
+    const bool valid = cbase + tok_i * ROWS + row < pend;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      float z = valid ? sc[j] * qk_scale : -__builtin_inff();
+      float bm = row_max_bits32(z);
+      float mn = fmaxf(m[j], bm);
+      float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
+      float p = valid ? __builtin_amdgcn_exp2f(z - mn) : 0.f;
+      l[j] = l[j] * al + p;
+      m[j] = mn;
+      pj[j] = p;
+      alj[j] = al;
+    }
+    // share p (and the per-head rescale factors) inside the row
+    if ((c & ((1 << DUP) - 1)) == 0) {
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
-        float z = valid ? sc[j] * qk_scale : -__builtin_inff();
-        float bm = row_max_bits32(z);
-        float mn = fmaxf(m[j], bm);
-        float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m[j] - mn);
-        float p = valid ? __builtin_amdgcn_exp2f(z - mn) : 0.f;
-        l[j] = l[j] * al + p;
-        m[j] = mn;
-        pj[j] = p;
-        alj[j] = al;
-      }
-      // share p (and the per-head rescale factors) inside the row
-      if ((c & ((1 << DUP) - 1)) == 0) {
-#pragma unroll
-        for (int j = 0; j < NF; ++j) {
-          const int v = NF * (c >> DUP) + j;
-          s_p[wave][row][v] = pj[j];
-          if (v < G) s_p[wave][row][NV + v] = alj[j];
-        }
-      }
-      wave_sync();
-      float pp[NV], alpha[G];
-#pragma unroll
-      for (int v = 0; v < NV; ++v) pp[v] = s_p[wave][row][v];
-#pragma unroll
-      for (int h = 0; h < G; ++h) alpha[h] = s_p[wave][row][NV + h];
-      wave_sync();
-
-      bool rescale = false;
-#pragma unroll
-      for (int h = 0; h < G; ++h) rescale |= alpha[h] != 1.f;
-      if (__any(rescale)) {
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha[h];
-      }
-
-      // --- P.V -------------------------------------------------------------
-      if (tail) {
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-          if (cbase + i * ROWS + row >= pend) {
-#pragma unroll
-            for (int w = 0; w < KDW; ++w) vc[i][w] = 0u;
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        float vf[VEC];
-#pragma unroll
-        for (int w = 0; w < KDW; ++w) Widen<KV>::run(vc[i][w], vf + w * Widen<KV>::per_word);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = pp[i * G + h];
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[h][e] = __builtin_fmaf(p, vf[e], acc[h][e]);
-        }
-      }
-
-      if (knext < nchunks) {
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-#pragma unroll
-          for (int w = 0; w < KDW; ++w) { kc[i][w] = kn[i][w]; vc[i][w] = vn[i][w]; }
+        const int v = NF * (c >> DUP) + j;
+        s_p[wave][row][v] = pj[j];
+        if (v < G) s_p[wave][row][NV + v] = alj[j];
       }
     }
+    wave_sync();
+    float pp[NV], alpha[G];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) pp[v] = s_p[wave][row][v];
+#pragma unroll
+    for (int h = 0; h < G; ++h) alpha[h] = s_p[wave][row][NV + h];
+    wave_sync();
+
+    bool rescale = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) rescale |= alpha[h] != 1.f;
+    if (__any(rescale)) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] *= alpha[h];
+    }
+
+    // --- P.V -------------------------------------------------------------
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        if (cbase + i * ROWS + row >= pend) {
+#pragma unroll
+          for (int w = 0; w < KDW; ++w) vr[i][w] = 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[VEC];
+#pragma unroll
+      for (int w = 0; w < KDW; ++w) Widen<KV>::run(vr[i][w], vf + w * Widen<KV>::per_word);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = pp[i * G + h];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[h][e] = __builtin_fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+
+  };
+
+  if (!bad_tbl && wave < nchunks) {
+    // Ping-pong register buffers: the loads of the next chunk are in flight
+    // while the current one is processed. The prefetch is unconditional (its
+    // chunk index is clamped to the last chunk, which is in bounds and cached)
+    // so every iteration has the same loads outstanding and the compiler's
+    // wait counts stay tight; no register copy forces an early wait.
+    uint32_t ka[NL][KDW], va[NL][KDW], kb[NL][KDW], vb[NL][KDW];
+    const int last = nchunks - 1;
+    int k = wave;
+    int n = (nchunks - wave + NW - 1) / NW;       // chunks of this wave (>= 1)
+    load_chunk(k, ka, va);
+    for (; n >= 2; n -= 2) {
+      load_chunk(min(k + NW, last), kb, vb);
+      process_chunk(k, ka, va);
+      k += NW;
+      load_chunk(min(k + NW, last), ka, va);
+      process_chunk(k, kb, vb);
+      k += NW;
+    }
+    if (n == 1) process_chunk(k, ka, va);
   }
 
   // --- merge the 4 rows of each wave ---------------------------------------
@@ -449,8 +465,8 @@ attend_kernel(const DecodeParams a) {
 template <Ty QT, int D>
 __global__ void __launch_bounds__(64)
 merge_kernel(const DecodeParams a) {
-  const int hq = blockIdx.x;
-  const int seq = blockIdx.y;
+  const int seq = blockIdx.x;
+  const int hq = blockIdx.y;
   const int ctx = a.context_lens[seq];
   if (ctx_status(a, ctx) || ctx == 0) return;
   const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
@@ -484,7 +500,7 @@ constexpr int NWAVES = 4;
 
 template <Ty KV, Ty QT, int D, int G>
 static hipError_t launch_attend_t(const DecodeParams& a, hipStream_t st) {
-  dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
+  dim3 grid(a.num_seqs, a.num_kv_heads, a.num_parts);
   hipLaunchKernelGGL((attend_kernel<KV, QT, D, G, NWAVES>), grid, dim3(NWAVES * 64), 0, st, a);
   return hipGetLastError();
 }
@@ -525,7 +541,7 @@ hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipS
 
 template <Ty QT>
 static hipError_t launch_merge_q(const DecodeParams& a, hipStream_t st) {
-  dim3 grid(a.num_q_heads, a.num_seqs);
+  dim3 grid(a.num_seqs, a.num_q_heads);
   if (a.head_dim == 64)
     hipLaunchKernelGGL((merge_kernel<QT, 64>), grid, dim3(64), 0, st, a);
   else if (a.head_dim == 128)

@@ -74,6 +74,8 @@ struct CopyParams {
 
 hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& a, int q_ty, hipStream_t st);
+bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g);
+hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st);
 hipError_t launch_write(const WriteParams& a, int src_ty, int dst_ty, hipStream_t st);
 hipError_t launch_copy(const CopyParams& a, hipStream_t st);
 
