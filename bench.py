@@ -33,7 +33,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_44_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h")]
+                  for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_device.h", "pa_internal.h")]
+
+
+def attend_kernel_name(wl) -> str:
+    """Which attention kernel the library runs for this workload: the matrix
+    core kernel for 16-bit / FP8 pools with 16-bit queries, the VALU kernel
+    otherwise."""
+    mfma = (wl.pool_dtype in ("f16", "bf16", "fp8_e4m3") and wl.q_dtype in ("f16", "bf16")
+            and (wl.pool_dtype == wl.q_dtype or wl.pool_dtype == "fp8_e4m3")
+            and wl.head_dim in (64, 128) and wl.num_q_heads // wl.num_kv_heads in (1, 2, 4, 8, 16))
+    return "attend_mfma_kernel" if mfma else "attend_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -54,6 +64,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target seconds of CPU oracle work for the baseline sample")
     ap.add_argument("--flush-iters", type=int, default=20)
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the hash of the attention kernel sources and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) a few times: the "
                          "reference kernel for scaling HBM byte counters")
@@ -161,6 +173,9 @@ def cpu_baseline(wl, target_s: float):
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
@@ -251,7 +266,8 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     ab = attend_bytes(wl)
     achieved = ab / (attend_ms * 1e-3) / 1e9
-    traffic = load_traffic("attend", wl.name)
+    kname = attend_kernel_name(wl)
+    traffic = load_traffic(kname, wl.name)
     rec = {
         "metric": "paged-decode KV GB/s and % of MI355X HBM peak; sequences/s at 1 GPU",
         "value": round(value, 2),
@@ -279,7 +295,7 @@ def main():
         "decode_flushed_ms": ({"median": round(float(np.median(fl)), 5),
                                "p10": round(float(np.percentile(fl, 10)), 5),
                                "p90": round(float(np.percentile(fl, 90)), 5)} if fl else None),
-        "roofline": {"kernel": "attend_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+        "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab,
