@@ -202,14 +202,19 @@ pa_status pa_decode_merge(const pa_kv_cache* cache, int32_t layer,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* Tokens per context partition that pa_decode will use for these sizes     */
-/* (a multiple of the per-wave chunk); 0 if the arguments are invalid.      */
+/* Granularity at which pa_decode may split one sequence's context between  */
+/* work units for these sizes: the partition length of the VALU kernel     */
+/* (fp32 pools, fp32 queries), or 16 for the matrix-core kernel, which      */
+/* splits the total work into equal runs of 16-token chunks per wave. 0 if  */
+/* the arguments are invalid. Informational; callers need not use it.       */
 int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs,
                                    int32_t num_q_heads,
                                    int32_t max_context_len);
 
-/* Workspace bytes pa_decode needs for these sizes (0 if none is needed or   */
-/* the arguments are invalid).                                               */
+/* Workspace bytes pa_decode needs for these sizes with any query dtype the  */
+/* pool accepts (0 if none is needed or the arguments are invalid). The     */
+/* size depends on the current device's compute-unit count; query it with   */
+/* that device current.                                                      */
 size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t max_context_len);
 

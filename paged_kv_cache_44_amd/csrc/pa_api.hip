@@ -68,10 +68,29 @@ pa_status check_cache(const pa_kv_cache* c, bool need_ptrs) {
 // ---------------------------------------------------------------------------
 struct DecodePlan {
   int g;
-  int part_tokens;
-  int num_parts;
-  size_t ws_bytes;     // 0 when no sequence can need a merge
+  bool mfma;           // evenly split matrix-core kernel (else the VALU kernel)
+  int sk_blocks;       // matrix-core path: workgroups launched
+  int part_tokens;     // VALU path: tokens per partition; matrix-core path: 16
+  int num_parts;       // VALU path: partitions in the launch grid
+  size_t ws_bytes;     // 0 when no workspace is needed
 };
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace regions, in order: o, m, l (fp32), then the chunk prefix sums.
+struct WsLayout {
+  size_t o, m, l, cum, total;
+};
+
+WsLayout ws_layout(size_t rows, int head_dim, size_t cum_entries) {
+  WsLayout w;
+  w.o = 0;
+  w.m = align256(rows * head_dim * sizeof(float));
+  w.l = w.m + align256(rows * sizeof(float));
+  w.cum = w.l + align256(rows * sizeof(float));
+  w.total = w.cum + align256(cum_entries * sizeof(int32_t));
+  return w;
+}
 
 pa_status decode_supported(const pa_kv_cache* c, int num_q_heads, pa_dtype q_dtype, int* g_out) {
   if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads) return PA_ERR_INVALID_ARG;
@@ -115,15 +134,25 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
   st = decode_supported(c, num_q_heads, q_dtype, &g);
   if (st != PA_OK) return st;
   plan->g = g;
+  plan->mfma = pa::mfma_supported((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
+  if (plan->mfma) {
+    // evenly split work: partial slots for every (wave, segment) pair that
+    // can exist, plus the chunk prefix sums
+    plan->sk_blocks = pa::sk_blocks((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
+    plan->part_tokens = 16;
+    plan->num_parts = 1;
+    const size_t waves = (size_t)plan->sk_blocks * 4;
+    const size_t rows = (waves + (size_t)num_seqs * c->num_kv_heads) * g;
+    plan->ws_bytes = ws_layout(rows, c->head_dim, (size_t)num_seqs + 1).total;
+    return PA_OK;
+  }
+  plan->sk_blocks = 0;
   plan->part_tokens = choose_part_tokens(c, g, num_seqs, max_ctx);
   plan->num_parts = std::max(1, (max_ctx + plan->part_tokens - 1) / plan->part_tokens);
   if (plan->num_parts > 65535) return PA_ERR_UNSUPPORTED;   // grid z limit
   if (plan->num_parts > 1) {
     const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
-    const size_t o = rows * c->head_dim * sizeof(float);
-    const size_t ml = rows * sizeof(float);
-    // three 256-byte aligned regions: o, m, l
-    plan->ws_bytes = ((o + 255) & ~(size_t)255) + 2 * ((ml + 255) & ~(size_t)255);
+    plan->ws_bytes = ws_layout(rows, c->head_dim, 0).total;
   } else {
     plan->ws_bytes = 0;
   }
@@ -184,23 +213,30 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
   a.part_tokens = plan.part_tokens;
   a.num_parts = plan.num_parts;
   if (plan.ws_bytes > 0) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * plan.num_parts;
-    const size_t o = ((rows * cache->head_dim * sizeof(float)) + 255) & ~(size_t)255;
-    const size_t ml = ((rows * sizeof(float)) + 255) & ~(size_t)255;
+    const size_t rows = plan.mfma
+        ? ((size_t)plan.sk_blocks * 4 + (size_t)num_seqs * cache->num_kv_heads) * plan.g
+        : (size_t)num_seqs * num_q_heads * plan.num_parts;
+    const WsLayout L = ws_layout(rows, cache->head_dim, plan.mfma ? (size_t)num_seqs + 1 : 0);
     char* w = reinterpret_cast<char*>(workspace);
-    a.ws_o = reinterpret_cast<float*>(w);
-    a.ws_m = reinterpret_cast<float*>(w + o);
-    a.ws_l = reinterpret_cast<float*>(w + o + ml);
+    a.ws_o = reinterpret_cast<float*>(w + L.o);
+    a.ws_m = reinterpret_cast<float*>(w + L.m);
+    a.ws_l = reinterpret_cast<float*>(w + L.l);
+    a.ws_cum = reinterpret_cast<int32_t*>(w + L.cum);
   }
   if (phases & PHASE_ATTEND) {
     const hipError_t e =
-        pa::mfma_supported((int)cache->dtype, (int)q_dtype, cache->head_dim, plan.g)
-            ? pa::launch_attend_mfma(a, (int)cache->dtype, (int)q_dtype, plan.g, stream)
-            : pa::launch_attend(a, (int)cache->dtype, (int)q_dtype, plan.g, stream);
+        plan.mfma ? pa::launch_attend_mfma(a, (int)cache->dtype, (int)q_dtype, plan.g,
+                                           plan.sk_blocks, stream)
+                  : pa::launch_attend(a, (int)cache->dtype, (int)q_dtype, plan.g, stream);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
-  if ((phases & PHASE_MERGE) && plan.num_parts > 1) {
-    if (pa::launch_merge(a, (int)q_dtype, stream) != hipSuccess) return PA_ERR_HIP;
+  if (phases & PHASE_MERGE) {
+    if (plan.mfma) {
+      if (pa::launch_merge_mfma(a, (int)q_dtype, plan.g, plan.sk_blocks, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    } else if (plan.num_parts > 1) {
+      if (pa::launch_merge(a, (int)q_dtype, stream) != hipSuccess) return PA_ERR_HIP;
+    }
   }
   return PA_OK;
 }
@@ -252,11 +288,16 @@ pa_status pa_write_kv(const pa_kv_cache* cache, int32_t layer, const void* k, co
 
 size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                 int32_t max_context_len) {
-  DecodePlan plan;
+  // the largest need over the query dtypes a pool of this dtype accepts
   if (!cache) return 0;
-  pa_dtype qd = cache->dtype == PA_FP8_E4M3 ? PA_BF16 : cache->dtype;
-  if (plan_decode(cache, num_seqs, num_q_heads, qd, max_context_len, &plan) != PA_OK) return 0;
-  return plan.ws_bytes;
+  size_t best = 0;
+  const pa_dtype qs[3] = {PA_F32, PA_F16, PA_BF16};
+  for (pa_dtype qd : qs) {
+    DecodePlan plan;
+    if (plan_decode(cache, num_seqs, num_q_heads, qd, max_context_len, &plan) == PA_OK)
+      best = std::max(best, plan.ws_bytes);
+  }
+  return best;
 }
 
 int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,

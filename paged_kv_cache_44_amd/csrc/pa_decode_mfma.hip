@@ -1,5 +1,5 @@
 // pa_decode_mfma.hip — paged decode attention with the grouped-query tile on
-// the gfx950 matrix cores.
+// the gfx950 matrix cores, work split evenly over the resident waves.
 //
 // Same result as the VALU kernel ("Efficient Memory Management for Large
 // Language Model Serving with PagedAttention", kernel paragraph: fetch each
@@ -10,35 +10,43 @@
 //   O[G heads][D]        += P[G][16] . V[16][D]    (v_mfma_f32_16x16x16)
 // G <= 16 fills the 16 columns of the tile.
 //
+// Work split ("stream-K"): the (sequence, KV head) segments, sequence-major,
+// each a run of ceil(context / 16) chunks, are laid end to end; wave w of the
+// W resident waves takes chunks [w*C/W, (w+1)*C/W) of the C total. Every wave
+// gets the same number of chunks whatever the length mix, and there are no
+// empty workgroups. A segment cut by range boundaries leaves one partial
+// (running max m, sum l, unnormalised o) per piece, stored at slot
+// (wave + segment); merge_sk_kernel combines them in wave order.
+//
 // Layout facts used (CDNA 16x16xK MFMA, checked on gfx950): lane l holds
 // A[row l%16][k in (l/16)*KL ..], B[k in (l/16)*KL ..][col l%16] and
 // C[rows 4*(l/16) .. +3][col l%16].
 //  * K: lane l loads token l%16, dims 32c + 8(l/16) .. +8 of step c: the A
-//    operand of the score MFMA straight from memory (16 tokens x 64 B per
-//    load instruction).
+//    operand of the score MFMA straight from memory.
 //  * The score tile comes out as lane l = (tokens 4(l/16)..+3, head l%16),
-//    which is exactly the A-operand layout of the P.V MFMA: probabilities never
-//    leave their lane.
-//  * V: lane (g, n) loads the full 16-byte slice [VPL*n, +VPL) of tokens
-//    4g..4g+3 (four whole 256-byte rows per load instruction); P.V MFMA m then
-//    uses output column n for dim VPL*n + m and takes element m of each of the
-//    four vectors (two byte permutes).
-//  * Online softmax with a lazily moved reference maximum per head: the
-//    reference only moves (exact cross-lane max, rescale) when a score exceeds
-//    it by more than 2^TAU, so probabilities stay <= 2^8 and most chunks need
-//    no cross-lane traffic at all.
-//  * One wave owns one (sequence, KV head, partition); a workgroup holds the
-//    4 KV heads of one (sequence, partition) and shares their block-table
-//    slice through LDS. No other LDS traffic and no atomics.
+//    exactly the A-operand layout of the P.V MFMA: probabilities never leave
+//    their lane.
+//  * V: lane (g, n) loads the slice [VPL*n, +VPL) of tokens 4g..4g+3 (whole
+//    256-byte rows per load instruction); P.V MFMA m uses output column n for
+//    dim VPL*n + m and takes element m of the four vectors (two byte permutes).
+//  * Online softmax with a lazily moved reference maximum per head: it moves
+//    (exact cross-lane max, rescale) only when a score exceeds it by more than
+//    2^TAU, so probabilities stay <= 2^8 and most chunks need no cross-lane
+//    traffic.
+//  * Block ids come from a 64-entry window of the block table held in one
+//    register (lane i = entry i), read with readlane / a lane shuffle.
+//  * Workgroups are dealt to the 8 XCDs round-robin; wave ranges are assigned
+//    so that each XCD works through one contiguous stretch of sequences.
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-constexpr int NWM = 4;          // waves (KV heads) per workgroup
+constexpr int NWM = 4;          // waves per workgroup
 constexpr int CH = 16;          // tokens per chunk
 constexpr float TAU = 8.0f;     // lazy rescale threshold (log2 units)
+constexpr int NXCD = 8;         // XCDs of an MI355X
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -63,23 +71,19 @@ __device__ __forceinline__ void ld(const uint32_t* __restrict__ p, uint32_t* w) 
   }
 }
 
-// Operand type of a matrix product: bf16 or f16 (both exact for the inputs
-// that reach them: 16-bit codes as stored, E4M3 codes widened).
+// Operand type of a matrix product: bf16 or f16 (exact for the inputs that
+// reach them: 16-bit codes as stored, E4M3 codes widened).
 enum class Op { BF16, F16 };
 
-// fp32 pair -> packed 16-bit pair, round to nearest even
 template <Op O>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
+__device__ __forceinline__ uint32_t pack2(float a, float b) {   // RNE
   if constexpr (O == Op::BF16) {
-    bf16x2_t v = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
   } else {
-    half2_t v = __builtin_convertvector((f32x2_t){a, b}, half2_t);
-    return __builtin_bit_cast(uint32_t, v);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, half2_t));
   }
 }
 
-// Packed 16-bit pair -> fp32 pair
 template <Op O>
 __device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b) {
   if constexpr (O == Op::BF16) {
@@ -98,11 +102,10 @@ __device__ __forceinline__ void fp8x4_to(uint32_t w, uint32_t& lo, uint32_t& hi)
   auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
   auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
   if constexpr (O == Op::BF16) {
-    // the values fit bf16 exactly: keep the upper halves of the fp32 words
-    lo = __builtin_amdgcn_perm(f2u(a[1]), f2u(a[0]), 0x07060302u);
+    lo = __builtin_amdgcn_perm(f2u(a[1]), f2u(a[0]), 0x07060302u);   // upper halves
     hi = __builtin_amdgcn_perm(f2u(b[1]), f2u(b[0]), 0x07060302u);
   } else {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));  // exact
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1]));
   }
 }
@@ -131,28 +134,41 @@ __device__ __forceinline__ f32x4_t mfma_k16(uint32_t a0, uint32_t a1, uint32_t b
 }
 
 template <Ty QT>
-__device__ __forceinline__ void store_row(void* out, int64_t idx, const float* x, int n) {
-  // n consecutive outputs starting at element idx
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
   if constexpr (QT == Ty::F32) {
-    float* o = reinterpret_cast<float*>(out) + idx;
-    for (int i = 0; i < n; ++i) o[i] = x[i];
+    reinterpret_cast<float*>(out)[idx] = x;
+  } else if constexpr (QT == Ty::BF16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(x);
   } else {
-    uint16_t* o = reinterpret_cast<uint16_t*>(out) + idx;
-    for (int i = 0; i < n; ++i) o[i] = (QT == Ty::BF16) ? f32_to_bf16_rne(x[i]) : f32_to_f16_rne(x[i]);
+    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_rne(x);
   }
 }
 
-__device__ __forceinline__ int ctx_bad(const DecodeParams& a, int ctx) {
-  if (ctx < 0 || ctx > a.max_context_len) return 1;
-  int64_t nb = ((int64_t)ctx + a.block_size - 1) >> a.log2_block_size;
-  return nb > a.max_blocks_per_seq ? 1 : 0;
+// Chunks of a sequence: 0 when its context is empty or invalid (those rows
+// are written by the merge kernel).
+__device__ __forceinline__ int seq_chunks(const DecodeParams& a, int ctx) {
+  if (ctx <= 0 || ctx > a.max_context_len) return 0;
+  const int64_t nb = ((int64_t)ctx + a.block_size - 1) >> a.log2_block_size;
+  if (nb > a.max_blocks_per_seq) return 0;
+  return (ctx + CH - 1) / CH;
+}
+
+// Wave that owns global chunk c when C chunks are split over W waves.
+__device__ __forceinline__ int64_t wave_of(int64_t c, int64_t C, int64_t W) {
+  return ((c + 1) * W - 1) / C;
 }
 
 }  // namespace
 
+// Occupancy: FP8 pools fit 3 waves per SIMD without spilling; 16-bit pools
+// at D = 128 would spill there and run at 2.
+template <Ty KV, int D>
+constexpr int sk_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
+
 template <Ty KV, Ty QT, int D, int G>
 __global__ void __launch_bounds__(NWM * 64)
-attend_mfma_kernel(const DecodeParams a) {
+__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D>())))
+attend_sk_kernel(const DecodeParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
   static_assert(D == 64 || D == 128, "head_dim");
@@ -164,276 +180,489 @@ attend_mfma_kernel(const DecodeParams a) {
   constexpr int KDW = 8 * EB / 4;         // raw K dwords per lane per step
   constexpr int VDW = VPL * EB / 4;       // raw V dwords per lane per token
 
-  __shared__ int s_tbl[PA_MAX_PART_BLOCKS];
-  __shared__ int s_bad;
+  extern __shared__ int s_cum[];          // [num_seqs + 1] chunk prefix sums
+  // per wave: the q B-operand of the current segment, [step][lane] x 16 bytes
+  __shared__ uint4 s_q[NWM][KS][64];
 
-  // Grid (sequence, KV-head group, partition). Workgroups are dealt to the
-  // 8 XCDs round-robin by linear id, i.e. by blockIdx.x here; rotating the
-  // sequence by the partition index spreads the partitions of one sequence
-  // over all XCDs instead of tying partition p to one XCD.
-  const int part = blockIdx.z;
-  const int seq = (int)((blockIdx.x + (unsigned)part) % (unsigned)a.num_seqs);
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;                // row group
   const int n = lane & 15;                // column: head (scores) / dim slice (values)
-  const int kvh = blockIdx.y * NWM + wave;
-  const bool kv_ok = kvh < a.num_kv_heads;
+  const int S = a.num_seqs;
+  const int H = a.num_kv_heads;
 
-  const int ctx = a.context_lens[seq];
-  const int P = a.part_tokens;
-  const int bad_ctx = ctx_bad(a, ctx);
-  const int nparts = (bad_ctx || ctx == 0) ? 1 : (ctx + P - 1) / P;
-  if (part >= nparts) return;
-  const int hq0 = kvh * G;
-  const int64_t out_row0 = ((int64_t)seq * a.num_q_heads + hq0) * D;
-  if (bad_ctx || ctx == 0) {
-    if (kv_ok) {
-      const float fill = bad_ctx ? __builtin_nanf("") : 0.f;
-      for (int i = lane; i < G * D; i += 64) store_row<QT>(a.out, out_row0 + i, &fill, 1);
-    }
-    return;
-  }
-
-  const int p0 = part * P;
-  const int pend = min(p0 + P, ctx);
-  const int lg = a.log2_block_size;
-  const int lb0 = p0 >> lg;
-  const int nlb = ((pend - 1) >> lg) - lb0 + 1;
-
-  // q as the B operand of the score MFMA: lane l holds head l%16, dims
-  // 32c + 8(l/16) .. +8 for step c (zero columns beyond the group)
-  uint32_t qb[KS][4];
+  // ---- chunk prefix sums over sequences (every workgroup, in LDS) ---------
   {
-    const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
+    int carry = 0;
+    for (int base = 0; base < S; base += NWM * 64) {
+      const int s = base + tid;
+      int v = (s < S) ? seq_chunks(a, a.context_lens[s]) : 0;
+      // inclusive scan inside the workgroup: wave scan, then across waves
+      int x = v;
 #pragma unroll
-    for (int c = 0; c < KS; ++c) {
-      if (kv_ok && n < G) {
-        ld<4>(qw + ((out_row0 + (int64_t)n * D + 32 * c + 8 * g) >> 1), qb[c]);
-      } else {
-        qb[c][0] = qb[c][1] = qb[c][2] = qb[c][3] = 0u;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
       }
+      __shared__ int s_wsum[NWM];
+      if (lane == 63) s_wsum[wave] = x;
+      __syncthreads();
+      int before = carry;
+      for (int w = 0; w < wave; ++w) before += s_wsum[w];
+      if (s < S) s_cum[s] = before + x - v;                   // exclusive
+      int tot = 0;
+      for (int w = 0; w < NWM; ++w) tot += s_wsum[w];
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) s_cum[S] = carry;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int s = tid; s <= S; s += NWM * 64) a.ws_cum[s] = s_cum[s];
     }
   }
-
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  const int32_t* trow = a.block_tables + (int64_t)seq * a.max_blocks_per_seq + lb0;
-  for (int i = tid; i < nlb; i += NWM * 64) {
-    int id = trow[i];
-    if (id < 0 || id >= a.num_blocks) { s_bad = 1; id = 0; }
-    s_tbl[i] = id;
-  }
-  __syncthreads();
-  if (!kv_ok) return;
-  const bool bad_tbl = s_bad != 0;
+  const int64_t CS = s_cum[S];                                  // chunks per KV head
+  const int64_t C = CS * H;
+  const int64_t W = (int64_t)gridDim.x * NWM;
+  // XCD-contiguous wave numbering: workgroup b runs on XCD b % 8; give each
+  // XCD one contiguous stretch of the chunk space (gridDim.x is a multiple of 8)
+  const int per_xcd = gridDim.x / NXCD;
+  const int vb = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  const int64_t w = (int64_t)vb * NWM + wave;
+  int64_t c = (w * C) / W;
+  const int64_t c_end = ((w + 1) * C) / W;
+  if (c >= c_end) return;
 
   const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
   const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
-  const int64_t head_off = a.layer_offset + (int64_t)kvh * a.block_size * D;
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
+  const int lg = a.log2_block_size;
   const int bmask = a.block_size - 1;
+  const bool big_blocks = a.block_size >= CH;                   // one block per chunk
   const float qk_scale = a.qk_scale_log2;
 
-  f32x4_t acc[VPL];
-#pragma unroll
-  for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m_ref = -__builtin_inff();        // reference max of head n (log2 units)
-  float l_sum = 0.f;                      // sum of this lane's probabilities (head n)
+  while (c < c_end) {
+    // ---- locate the segment holding chunk c -------------------------------
+    int lo = 0, hi = S - 1;                 // last s with s_cum[s] * H <= c
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)s_cum[mid] * H <= c) lo = mid; else hi = mid - 1;
+    }
+    const int seq = lo;
+    const int nc = s_cum[seq + 1] - s_cum[seq];
+    const int64_t rel = c - (int64_t)s_cum[seq] * H;
+    const int kvh = (int)(rel / nc);
+    const int j0 = (int)(rel - (int64_t)kvh * nc);              // first chunk of the piece
+    const int j1 = (int)min<int64_t>(nc, j0 + (c_end - c));     // one past its last
+    const int ctx = a.context_lens[seq];
+    const int seg = seq * H + kvh;
+    const int hq0 = kvh * G;
+    const int64_t out_row0 = ((int64_t)seq * a.num_q_heads + hq0) * D;
+    const int64_t head_off = a.layer_offset + (int64_t)kvh * a.block_size * D;
+    const int32_t* trow = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
 
-  const int ntok = pend - p0;
-  const int nchunks = (ntok + CH - 1) / CH;
+    // q as the B operand (lane l: head l%16, dims 32k + 8(l/16) .. +8),
+    // parked in this wave's LDS slot and re-read per chunk
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint32_t qv[4] = {0u, 0u, 0u, 0u};
+      if (n < G) ld<4>(qw + ((out_row0 + (int64_t)n * D + 32 * k + 8 * g) >> 1), qv);
+      s_q[wave][k][lane] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+    }
 
-  auto elem_of = [&](int t) -> int64_t {  // element index of token t, dim 0
-    t = min(t, pend - 1);
-    return (int64_t)s_tbl[(t >> lg) - lb0] * a.block_stride + head_off + (int64_t)(t & bmask) * D;
-  };
-  auto load_chunk = [&](int k, uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
-    const int cb = p0 + k * CH;
-    const int64_t ek = elem_of(cb + n) + 8 * g;
-    int64_t ev[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
-#pragma unroll
-    for (int c = 0; c < KS; ++c) ld<KDW>(kpool + (ek + 32 * c) * EB / 4, kr[c]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
-  };
-
-  auto process_chunk = [&](int k, uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
-    const int cb = p0 + k * CH;
-    // ---- scores: S[token 4g + r][head n] --------------------------------
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KS; ++c) {
-      uint32_t ka[4];
-      if constexpr (KV == Ty::FP8) {
-        fp8x4_to<OQK>(kr[c][0], ka[0], ka[1]);
-        fp8x4_to<OQK>(kr[c][1], ka[2], ka[3]);
+    // block-table window: lane i holds entry win0 + i
+    int win0 = -(1 << 30);                 // empty window: the first chunk loads it
+    int wreg = 0;
+    bool bad = false;
+    auto load_window = [&](int blk) {       // entries blk .. blk+63 (those in use)
+      win0 = blk;
+      const int e = blk + lane;
+      const int last = (ctx - 1) >> lg;
+      int id = (e <= last) ? trow[e] : 0;
+      if (id < 0 || id >= a.num_blocks) { id = 0; if (e <= last) bad = true; }
+      wreg = id;
+    };
+    auto elem_of = [&](int t) -> int64_t {  // element of token t (< ctx), dim 0
+      t = min(t, ctx - 1);
+      int id;
+      if (big_blocks) {
+        id = __builtin_amdgcn_readlane(wreg, ((t >> lg) - win0));
       } else {
-        ka[0] = kr[c][0]; ka[1] = kr[c][1]; ka[2] = kr[c][2]; ka[3] = kr[c][3];
+        id = __shfl(wreg, (t >> lg) - win0);
       }
-      s = mfma_k32<OQK>(ka, qb[c], s);
-    }
-    const bool tail = cb + CH > pend;
-    float z[4];
+      return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
+    };
+    auto load_chunk = [&](int j, uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
+      const int cb = j * CH;
+      const int fb = cb >> lg;
+      const int lb = (min(cb + CH, ctx) - 1) >> lg;
+      if (fb < win0 || lb >= win0 + 64) load_window(fb);
+      int64_t ek, ev[4];
+      if (big_blocks) {
+        const int64_t base = elem_of(cb);                   // uniform block
+        ek = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool valid = (n < G) && (cb + 4 * g + r < pend);
-      z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
-    }
-    const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    if (__any(lmax > m_ref + TAU)) {
-      // move the reference to the exact running max of each head
-      float hm = fmaxf(lmax, __shfl_xor(lmax, 16));
-      hm = fmaxf(hm, __shfl_xor(hm, 32));
-      const float mn = fmaxf(m_ref, hm);
-      const float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
-      m_ref = mn;
-      l_sum *= al;
+        for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
+      } else {
+        ek = elem_of(cb + n) + 8 * g;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
+      }
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+    };
+
+    f32x4_t acc[VPL];
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float m_ref = -__builtin_inff();        // reference max of head n (log2 units)
+    float l_sum = 0.f;                      // this lane's probability sum (head n)
+
+    auto process_chunk = [&](int j, uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
+      const int cb = j * CH;
+      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        uint32_t ka[4];
+        if constexpr (KV == Ty::FP8) {
+          fp8x4_to<OQK>(kr[k][0], ka[0], ka[1]);
+          fp8x4_to<OQK>(kr[k][1], ka[2], ka[3]);
+        } else {
+          ka[0] = kr[k][0]; ka[1] = kr[k][1]; ka[2] = kr[k][2]; ka[3] = kr[k][3];
+        }
+        const uint4 q4 = s_q[wave][k][lane];
+        const uint32_t qb[4] = {q4.x, q4.y, q4.z, q4.w};
+        s = mfma_k32<OQK>(ka, qb, s);
+      }
+      const bool tail = cb + CH > ctx;
+      float z[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(al, 4 * g + r);      // factor of accumulator row 4g + r
-#pragma unroll
-        for (int m = 0; m < VPL; ++m) acc[m][r] *= ar;
+        const bool valid = (n < G) && (cb + 4 * g + r < ctx);
+        z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
       }
-    }
-    float p[4];
+      const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      if (__any(lmax > m_ref + TAU)) {
+        float hm = fmaxf(lmax, __shfl_xor(lmax, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float mn = fmaxf(m_ref, hm);
+        const float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
+        m_ref = mn;
+        l_sum *= al;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = (z[r] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-    const uint32_t pa0 = pack2<OPV>(p[0], p[1]);
-    const uint32_t pa1 = pack2<OPV>(p[2], p[3]);
-    {
-      // the normaliser sums exactly the rounded weights the matrix core uses
-      float q0, q1, q2, q3;
-      unpack2<OPV>(pa0, q0, q1);
-      unpack2<OPV>(pa1, q2, q3);
-      l_sum += (q0 + q1) + (q2 + q3);
-    }
-    // ---- values: zero tokens past the context, widen FP8 -------------------
-    if (tail) {
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(al, 4 * g + r);      // factor of accumulator row 4g + r
+#pragma unroll
+          for (int m = 0; m < VPL; ++m) acc[m][r] *= ar;
+        }
+      }
+      float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (cb + 4 * g + r >= pend)
+        p[r] = (z[r] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+      const uint32_t pa0 = pack2<OPV>(p[0], p[1]);
+      const uint32_t pa1 = pack2<OPV>(p[2], p[3]);
+      {
+        // the normaliser sums exactly the rounded weights the matrix core uses
+        float q0, q1, q2, q3;
+        unpack2<OPV>(pa0, q0, q1);
+        unpack2<OPV>(pa1, q2, q3);
+        l_sum += (q0 + q1) + (q2 + q3);
+      }
+      if (tail) {                           // tokens past the context: zero values
 #pragma unroll
-          for (int w = 0; w < VDW; ++w) vr[r][w] = 0u;
+        for (int r = 0; r < 4; ++r)
+          if (cb + 4 * g + r >= ctx)
+#pragma unroll
+            for (int x = 0; x < VDW; ++x) vr[r][x] = 0u;
+      }
+      uint32_t vw[4][VPL / 2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (KV == Ty::FP8) {
+#pragma unroll
+          for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(vr[r][x], vw[r][2 * x], vw[r][2 * x + 1]);
+        } else {
+#pragma unroll
+          for (int x = 0; x < VPL / 2; ++x) vw[r][x] = vr[r][x];
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) {
+        const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t b0 = __builtin_amdgcn_perm(vw[1][m >> 1], vw[0][m >> 1], sel);
+        const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
+        acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
+      }
+    };
+
+    {
+      uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb[4][VDW];
+      const int last = j1 - 1;
+      int j = j0;
+      int left = j1 - j0;
+      load_chunk(j, ka, va);
+      for (; left >= 2; left -= 2) {
+        load_chunk(min(j + 1, last), kb, vb);
+        process_chunk(j, ka, va);
+        ++j;
+        load_chunk(min(j + 1, last), ka, va);
+        process_chunk(j, kb, vb);
+        ++j;
+      }
+      if (left == 1) process_chunk(j, ka, va);
     }
-    uint32_t vw[4][VPL / 2];                   // value words of operand type OPV
+    bad = __any(bad);
+
+    // ---- finish the piece -------------------------------------------------
+    float lt = l_sum + __shfl_xor(l_sum, 16);
+    lt += __shfl_xor(lt, 32);
+    const bool whole = (j0 == 0) && (j1 == nc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr (KV == Ty::FP8) {
+      const int h = 4 * g + r;                      // accumulator row = head
+      const float lh = __shfl(lt, h);
+      const float mh = __shfl(m_ref, h);
+      if (h < G) {
+        if (whole) {
+          const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
+          const int64_t o = out_row0 + (int64_t)h * D + VPL * n;
 #pragma unroll
-        for (int w = 0; w < VDW; ++w) fp8x4_to<OPV>(vr[r][w], vw[r][2 * w], vw[r][2 * w + 1]);
-      } else {
+          for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm);
+        } else {
+          const int64_t slot = ((w + seg) * G + h);
+          float* wo = a.ws_o + slot * D + VPL * n;
 #pragma unroll
-        for (int w = 0; w < VPL / 2; ++w) vw[r][w] = vr[r][w];
-      }
-    }
-    // ---- P.V: MFMA m covers dims VPL*n + m -------------------------------
-#pragma unroll
-    for (int m = 0; m < VPL; ++m) {
-      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t b0 = __builtin_amdgcn_perm(vw[1][m >> 1], vw[0][m >> 1], sel);
-      const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
-      acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
-    }
-  };
-
-  if (!bad_tbl) {
-    uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb[4][VDW];
-    const int last = nchunks - 1;
-    int k = 0;
-    int left = nchunks;
-    load_chunk(0, ka, va);
-    for (; left >= 2; left -= 2) {
-      load_chunk(min(k + 1, last), kb, vb);
-      process_chunk(k, ka, va);
-      ++k;
-      load_chunk(min(k + 1, last), ka, va);
-      process_chunk(k, kb, vb);
-      ++k;
-    }
-    if (left == 1) process_chunk(k, ka, va);
-  }
-
-  // ---- finish: per-head sums over the 4 row groups, then write -------------
-  float lt = l_sum + __shfl_xor(l_sum, 16);
-  lt += __shfl_xor(lt, 32);
-  const bool single = nparts == 1;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * g + r;                        // accumulator row = head
-    const float lh = __shfl(lt, h);
-    const float mh = __shfl(m_ref, h);
-    if (h < G) {
-      float o[VPL];
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) o[m] = acc[m][r];
-      if (bad_tbl) {
-#pragma unroll
-        for (int m = 0; m < VPL; ++m) o[m] = __builtin_nanf("");
-      }
-      if (single) {
-        const float norm = a.v_scale / lh;
-#pragma unroll
-        for (int m = 0; m < VPL; ++m) o[m] *= norm;
-        store_row<QT>(a.out, out_row0 + (int64_t)h * D + VPL * n, o, VPL);
-      } else {
-        const int64_t pr = ((int64_t)seq * a.num_q_heads + hq0 + h) * a.num_parts + part;
-        float* wo = a.ws_o + pr * D + VPL * n;
-#pragma unroll
-        for (int m = 0; m < VPL; ++m) wo[m] = o[m];
-        if (n == 0) {
-          a.ws_m[pr] = bad_tbl ? 0.f : mh;
-          a.ws_l[pr] = bad_tbl ? __builtin_nanf("") : lh;
+          for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[m][r];
+          if (n == 0) {
+            a.ws_m[slot] = bad ? 0.f : mh;
+            a.ws_l[slot] = bad ? __builtin_nanf("") : lh;
+          }
         }
       }
     }
+    c += j1 - j0;
   }
+}
+
+// Rows of empty / invalid sequences, and the merge of segments split over
+// several waves: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// One workgroup per (sequence, KV head) segment; its threads form PG groups,
+// each covering all G x D outputs (4 dims per thread) over every PG-th piece
+// with a running (online) combination, then the groups are combined in LDS.
+template <Ty QT, int D, int G>
+__global__ void __launch_bounds__(256)
+merge_sk_kernel(const DecodeParams a, int64_t W) {
+  constexpr int DPT = (G * D > 1024) ? 8 : 4;         // dims per thread
+  constexpr int NV4 = DPT / 4;
+  constexpr int TPG = G * D / DPT;                    // threads per group
+  static_assert(TPG <= 256 && 256 % TPG == 0, "group size");
+  constexpr int PG = 256 / TPG;                       // piece groups
+  __shared__ float s_m[PG][G], s_l[PG][G];
+  __shared__ float s_o[PG > 1 ? PG : 1][G * D];
+
+  const int seq = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int H = a.num_kv_heads;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPG;
+  const int t = tid - grp * TPG;
+  const int h = t / (D / DPT);
+  const int d0 = (t - h * (D / DPT)) * DPT;
+  const int ctx = a.context_lens[seq];
+  const int64_t orow = ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h) * D + d0;
+  const int nc = seq_chunks(a, ctx);
+  if (nc == 0) {
+    if (grp == 0) {
+      const float fill = (ctx == 0) ? 0.f : __builtin_nanf("");
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, fill);
+    }
+    return;
+  }
+  const int64_t C = (int64_t)a.ws_cum[a.num_seqs] * H;
+  const int64_t off = (int64_t)a.ws_cum[seq] * H + (int64_t)kvh * nc;
+  const int64_t w0 = wave_of(off, C, W);
+  const int64_t w1 = wave_of(off + nc - 1, C, W);
+  if (w0 == w1) return;                               // written whole by its wave
+  const int64_t seg = (int64_t)seq * H + kvh;
+
+  float M = -__builtin_inff(), L = 0.f, O[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) O[e] = 0.f;
+  auto combine = [&](float m, float l, const float4* o) {
+    const float mn = fmaxf(M, m);
+    if (mn == -__builtin_inff()) return;
+    const float f1 = __builtin_amdgcn_exp2f(M - mn);   // 0 when M = -inf
+    const float f2 = __builtin_amdgcn_exp2f(m - mn);
+    L = L * f1 + l * f2;
+#pragma unroll
+    for (int v = 0; v < NV4; ++v) {
+      O[4 * v + 0] = O[4 * v + 0] * f1 + o[v].x * f2;
+      O[4 * v + 1] = O[4 * v + 1] * f1 + o[v].y * f2;
+      O[4 * v + 2] = O[4 * v + 2] * f1 + o[v].z * f2;
+      O[4 * v + 3] = O[4 * v + 3] * f1 + o[v].w * f2;
+    }
+    M = mn;
+  };
+  // pieces w0 + grp, w0 + grp + PG, ...; four loads in flight per step
+  constexpr int U = 4;
+  for (int64_t wb = w0 + grp; wb <= w1; wb += (int64_t)PG * U) {
+    float mv[U], lv[U];
+    float4 ov[U][NV4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t w = wb + (int64_t)u * PG;
+      const bool ok = w <= w1 && (w * C) / W != ((w + 1) * C) / W;   // empty ranges wrote nothing
+      const int64_t slot = (w + seg) * G + h;
+      mv[u] = ok ? a.ws_m[slot] : -__builtin_inff();
+      lv[u] = ok ? a.ws_l[slot] : 0.f;
+#pragma unroll
+      for (int v = 0; v < NV4; ++v)
+        ov[u][v] = ok ? reinterpret_cast<const float4*>(a.ws_o + slot * D + d0)[v]
+                      : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) combine(mv[u], lv[u], ov[u]);
+  }
+  if constexpr (PG > 1) {
+    if (d0 == 0) { s_m[grp][h] = M; s_l[grp][h] = L; }
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) s_o[grp][h * D + d0 + e] = O[e];
+    __syncthreads();
+    if (grp != 0) return;
+    M = -__builtin_inff(); L = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) O[e] = 0.f;
+#pragma unroll
+    for (int q = 0; q < PG; ++q)
+      combine(s_m[q][h], s_l[q][h], reinterpret_cast<const float4*>(&s_o[q][h * D + d0]));
+  }
+  const float norm = a.v_scale / L;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, O[e] * norm);
 }
 
 // ---------------------------------------------------------------------------
 template <Ty KV, Ty QT, int D, int G>
-static hipError_t launch_t(const DecodeParams& a, hipStream_t st) {
-  dim3 grid(a.num_seqs, (a.num_kv_heads + NWM - 1) / NWM, a.num_parts);
-  hipLaunchKernelGGL((attend_mfma_kernel<KV, QT, D, G>), grid, dim3(NWM * 64), 0, st, a);
+static hipError_t launch_t(const DecodeParams& a, int blocks, hipStream_t st) {
+  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+  hipLaunchKernelGGL((attend_sk_kernel<KV, QT, D, G>), dim3(blocks), dim3(NWM * 64), lds, st, a);
   return hipGetLastError();
 }
 
 template <Ty KV, Ty QT, int D>
-static hipError_t launch_g(const DecodeParams& a, int g, hipStream_t st) {
+static hipError_t launch_g(const DecodeParams& a, int g, int blocks, hipStream_t st) {
   switch (g) {
-    case 1: return launch_t<KV, QT, D, 1>(a, st);
-    case 2: return launch_t<KV, QT, D, 2>(a, st);
-    case 4: return launch_t<KV, QT, D, 4>(a, st);
-    case 8: return launch_t<KV, QT, D, 8>(a, st);
-    case 16: return launch_t<KV, QT, D, 16>(a, st);
+    case 1: return launch_t<KV, QT, D, 1>(a, blocks, st);
+    case 2: return launch_t<KV, QT, D, 2>(a, blocks, st);
+    case 4: return launch_t<KV, QT, D, 4>(a, blocks, st);
+    case 8: return launch_t<KV, QT, D, 8>(a, blocks, st);
+    case 16: return launch_t<KV, QT, D, 16>(a, blocks, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <Ty KV, Ty QT>
-static hipError_t launch_d(const DecodeParams& a, int g, hipStream_t st) {
-  if (a.head_dim == 64) return launch_g<KV, QT, 64>(a, g, st);
-  if (a.head_dim == 128) return launch_g<KV, QT, 128>(a, g, st);
+static hipError_t launch_d(const DecodeParams& a, int g, int blocks, hipStream_t st) {
+  if (a.head_dim == 64) return launch_g<KV, QT, 64>(a, g, blocks, st);
+  if (a.head_dim == 128) return launch_g<KV, QT, 128>(a, g, blocks, st);
   return hipErrorInvalidValue;
 }
 
-bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g) {
+bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {
   const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
   const bool types = (kv == Ty::BF16 && q == Ty::BF16) || (kv == Ty::F16 && q == Ty::F16) ||
                      (kv == Ty::FP8 && (q == Ty::BF16 || q == Ty::F16));
   return types && (head_dim == 64 || head_dim == 128) &&
-         (g == 1 || g == 2 || g == 4 || g == 8 || g == 16);
+         (g == 1 || g == 2 || g == 4 || g == 8 || g == 16) && num_seqs <= PA_SK_MAX_SEQS;
 }
 
-hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st) {
+// Workgroups to launch: exactly the number that are resident at once (every
+// wave's range is processed concurrently), a multiple of the XCD count.
+template <Ty KV, Ty QT, int D, int G>
+static int sk_blocks_t(int num_seqs) {
+  int dev = 0, cus = 256, per_cu = 0;
+  const size_t lds = (size_t)(num_seqs + 1) * sizeof(int);
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&attend_sk_kernel<KV, QT, D, G>), NWM * 64,
+            lds) != hipSuccess)
+      per_cu = 0;
+  }
+  if (per_cu <= 0) per_cu = sk_waves_per_simd<KV, D>();   // no device: the compiled occupancy
+  const int b = cus * per_cu;
+  return b >= NXCD ? b / NXCD * NXCD : NXCD;
+}
+
+template <Ty KV, Ty QT, int D>
+static int sk_blocks_g(int g, int num_seqs) {
+  switch (g) {
+    case 1: return sk_blocks_t<KV, QT, D, 1>(num_seqs);
+    case 2: return sk_blocks_t<KV, QT, D, 2>(num_seqs);
+    case 4: return sk_blocks_t<KV, QT, D, 4>(num_seqs);
+    case 8: return sk_blocks_t<KV, QT, D, 8>(num_seqs);
+    default: return sk_blocks_t<KV, QT, D, 16>(num_seqs);
+  }
+}
+
+template <Ty KV, Ty QT>
+static int sk_blocks_d(int head_dim, int g, int num_seqs) {
+  return head_dim == 64 ? sk_blocks_g<KV, QT, 64>(g, num_seqs) : sk_blocks_g<KV, QT, 128>(g, num_seqs);
+}
+
+int sk_blocks(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {
   const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
-  if (kv == Ty::BF16 && q == Ty::BF16) return launch_d<Ty::BF16, Ty::BF16>(a, g, st);
-  if (kv == Ty::F16 && q == Ty::F16) return launch_d<Ty::F16, Ty::F16>(a, g, st);
-  if (kv == Ty::FP8 && q == Ty::BF16) return launch_d<Ty::FP8, Ty::BF16>(a, g, st);
-  if (kv == Ty::FP8 && q == Ty::F16) return launch_d<Ty::FP8, Ty::F16>(a, g, st);
+  if (kv == Ty::BF16) return sk_blocks_d<Ty::BF16, Ty::BF16>(head_dim, g, num_seqs);
+  if (kv == Ty::F16) return sk_blocks_d<Ty::F16, Ty::F16>(head_dim, g, num_seqs);
+  if (q == Ty::F16) return sk_blocks_d<Ty::FP8, Ty::F16>(head_dim, g, num_seqs);
+  return sk_blocks_d<Ty::FP8, Ty::BF16>(head_dim, g, num_seqs);
+}
+
+hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
+                              hipStream_t st) {
+  const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
+  if (kv == Ty::BF16 && q == Ty::BF16) return launch_d<Ty::BF16, Ty::BF16>(a, g, blocks, st);
+  if (kv == Ty::F16 && q == Ty::F16) return launch_d<Ty::F16, Ty::F16>(a, g, blocks, st);
+  if (kv == Ty::FP8 && q == Ty::BF16) return launch_d<Ty::FP8, Ty::BF16>(a, g, blocks, st);
+  if (kv == Ty::FP8 && q == Ty::F16) return launch_d<Ty::FP8, Ty::F16>(a, g, blocks, st);
   return hipErrorInvalidValue;
+}
+
+template <Ty QT, int D>
+static hipError_t launch_merge_sk_d(const DecodeParams& a, int64_t W, int g, hipStream_t st) {
+  dim3 grid(a.num_seqs, a.num_kv_heads);
+  switch (g) {
+    case 1: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 1>), grid, dim3(256), 0, st, a, W); break;
+    case 2: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 2>), grid, dim3(256), 0, st, a, W); break;
+    case 4: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 4>), grid, dim3(256), 0, st, a, W); break;
+    case 8: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 8>), grid, dim3(256), 0, st, a, W); break;
+    case 16: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 16>), grid, dim3(256), 0, st, a, W); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <Ty QT>
+static hipError_t launch_merge_sk_q(const DecodeParams& a, int64_t W, int g, hipStream_t st) {
+  if (a.head_dim == 64) return launch_merge_sk_d<QT, 64>(a, W, g, st);
+  if (a.head_dim == 128) return launch_merge_sk_d<QT, 128>(a, W, g, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st) {
+  const int64_t W = (int64_t)blocks * NWM;
+  switch ((Ty)q_ty) {
+    case Ty::BF16: return launch_merge_sk_q<Ty::BF16>(a, W, g, st);
+    case Ty::F16: return launch_merge_sk_q<Ty::F16>(a, W, g, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace pa

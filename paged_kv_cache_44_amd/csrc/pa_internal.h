@@ -9,6 +9,9 @@ namespace pa {
 
 // Largest number of block-table entries one decode partition may span.
 constexpr int PA_MAX_PART_BLOCKS = 1024;
+// Largest batch the evenly split matrix-core decode takes (its per-workgroup
+// chunk prefix sums live in LDS).
+constexpr int PA_SK_MAX_SEQS = 8192;
 
 struct DecodeParams {
   const void* k_pool;
@@ -35,6 +38,7 @@ struct DecodeParams {
   float* ws_o;               // [num_seqs][num_q_heads][num_parts][head_dim]
   float* ws_m;               // [num_seqs][num_q_heads][num_parts]
   float* ws_l;               // [num_seqs][num_q_heads][num_parts]
+  int32_t* ws_cum;           // matrix-core path: chunk prefix sums [num_seqs + 1]
 };
 
 struct WriteParams {
@@ -74,8 +78,11 @@ struct CopyParams {
 
 hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& a, int q_ty, hipStream_t st);
-bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g);
-hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st);
+bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
+int sk_blocks(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
+hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
+                              hipStream_t st);
+hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st);
 hipError_t launch_write(const WriteParams& a, int src_ty, int dst_ty, hipStream_t st);
 hipError_t launch_copy(const CopyParams& a, hipStream_t st);
 

@@ -43,15 +43,21 @@ def _cache(dtype=B.PA_BF16, blocks=100, layers=1, heads=8, bs=16, dim=128, ks=1.
 
 
 def test_workspace_and_partition_queries(pa_lib):
+    # matrix-core path (bf16 pool, bf16 queries): splits at 16-token chunks and
+    # always needs a workspace (partials + chunk prefix sums)
     c = _cache()
-    p = pa_lib.pa_decode_partition_tokens(ctypes.byref(c), 256, 32, 4000)
+    assert pa_lib.pa_decode_partition_tokens(ctypes.byref(c), 256, 32, 4000) == 16
+    ws = pa_lib.pa_decode_workspace_size(ctypes.byref(c), 256, 32, 4000)
+    assert ws >= (256 * 8 * 4) * (128 + 2) * 4 + 257 * 4
+    assert pa_lib.pa_decode_workspace_size(ctypes.byref(c), 4, 32, 16) > 0
+    # VALU path (fp32 pool): fixed partitions; one partition needs no workspace
+    f = _cache(dtype=B.PA_F32, dim=64, heads=4)
+    p = pa_lib.pa_decode_partition_tokens(ctypes.byref(f), 64, 4, 4000)
     assert p >= 64 and p % 64 == 0
     parts = -(-4000 // p)
-    ws = pa_lib.pa_decode_workspace_size(ctypes.byref(c), 256, 32, 4000)
-    if parts > 1:
-        assert ws >= 256 * 32 * parts * (128 + 2) * 4
-    # one partition only: no workspace needed
-    assert pa_lib.pa_decode_workspace_size(ctypes.byref(c), 4, 32, 16) == 0
+    ws = pa_lib.pa_decode_workspace_size(ctypes.byref(f), 64, 4, 4000)
+    assert parts > 1 and ws >= 64 * 4 * parts * (64 + 2) * 4
+    assert pa_lib.pa_decode_workspace_size(ctypes.byref(f), 4, 4, 16) == 0
     # invalid geometry -> 0
     bad = _cache(bs=12)
     assert pa_lib.pa_decode_partition_tokens(ctypes.byref(bad), 4, 32, 100) == 0
@@ -73,6 +79,7 @@ def test_decode_argument_errors(pa_lib):
     assert _decode(pa_lib, c, q=None) == B.PA_ERR_INVALID_ARG
     assert _decode(pa_lib, c, scale=float("inf")) == B.PA_ERR_INVALID_ARG
     assert _decode(pa_lib, c, max_ctx=5000) == B.PA_ERR_WORKSPACE     # needs a workspace
+    assert _decode(pa_lib, c, max_ctx=5, ws=FAKE, ws_bytes=64) == B.PA_ERR_WORKSPACE
     assert _decode(pa_lib, _cache(dim=96)) == B.PA_ERR_UNSUPPORTED
     assert _decode(pa_lib, _cache(dtype=B.PA_F32, dim=128), q_dtype=B.PA_F32) == B.PA_ERR_UNSUPPORTED
     assert _decode(pa_lib, _cache(ks=0.5)) == B.PA_ERR_INVALID_ARG    # scale on a bf16 pool

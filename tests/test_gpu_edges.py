@@ -43,7 +43,7 @@ COMBOS = [
 
 def _edge_ctx(P, B):
     c = {1, 2, 15, 16, 17, B - 1, B, B + 1, 63, 64, 65, P - 1, P, P + 1, 2 * P - 1, 2 * P + 1,
-         3 * P + 5}
+         3 * P + 5, 255, 256, 257, 1000, 1500}
     return sorted(x for x in c if x >= 1)
 
 
