@@ -43,7 +43,7 @@ def attend_kernel_name(wl) -> str:
     mfma = (wl.pool_dtype in ("f16", "bf16", "fp8_e4m3") and wl.q_dtype in ("f16", "bf16")
             and (wl.pool_dtype == wl.q_dtype or wl.pool_dtype == "fp8_e4m3")
             and wl.head_dim in (64, 128) and wl.num_q_heads // wl.num_kv_heads in (1, 2, 4, 8, 16))
-    return "attend_mfma_kernel" if mfma else "attend_kernel"
+    return "attend_sk_kernel" if mfma else "attend_kernel"
 
 
 def kernel_source_hash() -> str:

@@ -242,185 +242,210 @@ attend_sk_kernel(const DecodeParams a) {
   const bool big_blocks = a.block_size >= CH;                   // one block per chunk
   const float qk_scale = a.qk_scale_log2;
 
-  while (c < c_end) {
-    // ---- locate the segment holding chunk c -------------------------------
-    int lo = 0, hi = S - 1;                 // last s with s_cum[s] * H <= c
+  // ---- the chunk stream [c, c_end): a load cursor one chunk ahead of the
+  // process cursor. Segment = (sequence, KV head), sequence-major.
+  struct Seg {
+    int seq, kvh, nc, ctx;
+  };
+  auto seg_at = [&](int64_t cg, int& j) __attribute__((always_inline)) -> Seg {     // segment holding global chunk cg
+    int lo = 0, hi = S - 1;                          // last s with s_cum[s] * H <= cg
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)s_cum[mid] * H <= c) lo = mid; else hi = mid - 1;
+      if ((int64_t)s_cum[mid] * H <= cg) lo = mid; else hi = mid - 1;
     }
-    const int seq = lo;
-    const int nc = s_cum[seq + 1] - s_cum[seq];
-    const int64_t rel = c - (int64_t)s_cum[seq] * H;
-    const int kvh = (int)(rel / nc);
-    const int j0 = (int)(rel - (int64_t)kvh * nc);              // first chunk of the piece
-    const int j1 = (int)min<int64_t>(nc, j0 + (c_end - c));     // one past its last
-    const int ctx = a.context_lens[seq];
-    const int seg = seq * H + kvh;
-    const int hq0 = kvh * G;
-    const int64_t out_row0 = ((int64_t)seq * a.num_q_heads + hq0) * D;
-    const int64_t head_off = a.layer_offset + (int64_t)kvh * a.block_size * D;
-    const int32_t* trow = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+    Seg sg;
+    sg.seq = lo;
+    sg.nc = s_cum[lo + 1] - s_cum[lo];
+    const int64_t rel = cg - (int64_t)s_cum[lo] * H;
+    sg.kvh = (int)(rel / sg.nc);
+    j = (int)(rel - (int64_t)sg.kvh * sg.nc);
+    sg.ctx = a.context_lens[lo];
+    return sg;
+  };
+  auto next_seg = [&](const Seg& sg, int64_t cg_next) __attribute__((always_inline)) -> Seg {   // segment after sg
+    if (sg.kvh + 1 < H) {
+      Seg n2 = sg;
+      n2.kvh = sg.kvh + 1;
+      return n2;
+    }
+    int j;
+    return seg_at(cg_next, j);
+  };
 
-    // q as the B operand (lane l: head l%16, dims 32k + 8(l/16) .. +8),
-    // parked in this wave's LDS slot and re-read per chunk
+  // load cursor: segment, chunk, block-table window (lane i = entry win0 + i)
+  int lj = 0;
+  Seg ls = seg_at(c, lj);
+  int win0 = -(1 << 30);                             // empty window: first use loads it
+  int wseq = -1;                                     // sequence the window belongs to
+  int wreg = 0;
+  bool lbad = false;                                 // bad block id in the load segment
+  int64_t lc = c;                                    // global index of the next chunk to load
+  auto load_window = [&](int blk) __attribute__((always_inline)) {
+    win0 = blk;
+    wseq = ls.seq;
+    const int e = blk + lane;
+    const int last = (ls.ctx - 1) >> lg;
+    const int32_t* trow = a.block_tables + (int64_t)ls.seq * a.max_blocks_per_seq;
+    int id = (e <= last) ? trow[e] : 0;
+    if (id < 0 || id >= a.num_blocks) { id = 0; if (e <= last) lbad = true; }
+    wreg = id;
+  };
+  // q of a segment as the B operand (lane l: head l%16, dims 32k + 8(l/16) .. +8)
+  auto load_q = [&](const Seg& sg, uint32_t (&qr)[KS][4]) {
+    const int64_t row = ((int64_t)sg.seq * a.num_q_heads + (int64_t)sg.kvh * G + n) * D;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      uint32_t qv[4] = {0u, 0u, 0u, 0u};
-      if (n < G) ld<4>(qw + ((out_row0 + (int64_t)n * D + 32 * k + 8 * g) >> 1), qv);
-      s_q[wave][k][lane] = make_uint4(qv[0], qv[1], qv[2], qv[3]);
-    }
-
-    // block-table window: lane i holds entry win0 + i
-    int win0 = -(1 << 30);                 // empty window: the first chunk loads it
-    int wreg = 0;
-    bool bad = false;
-    auto load_window = [&](int blk) {       // entries blk .. blk+63 (those in use)
-      win0 = blk;
-      const int e = blk + lane;
-      const int last = (ctx - 1) >> lg;
-      int id = (e <= last) ? trow[e] : 0;
-      if (id < 0 || id >= a.num_blocks) { id = 0; if (e <= last) bad = true; }
-      wreg = id;
-    };
-    auto elem_of = [&](int t) -> int64_t {  // element of token t (< ctx), dim 0
-      t = min(t, ctx - 1);
-      int id;
-      if (big_blocks) {
-        id = __builtin_amdgcn_readlane(wreg, ((t >> lg) - win0));
+      if (n < G) {
+        ld<4>(qw + ((row + 32 * k + 8 * g) >> 1), qr[k]);
       } else {
-        id = __shfl(wreg, (t >> lg) - win0);
+        qr[k][0] = qr[k][1] = qr[k][2] = qr[k][3] = 0u;
       }
+    }
+  };
+  auto store_q = [&](const uint32_t (&qr)[KS][4]) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) s_q[wave][k][lane] = make_uint4(qr[k][0], qr[k][1], qr[k][2], qr[k][3]);
+  };
+  uint32_t qn[KS][4];                                // q of the load cursor's segment
+  bool prev_bad = false;                             // bad flag of the segment the load cursor left
+
+  // Issue the loads of chunk lj of segment ls, then advance the load cursor.
+  auto load_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
+    const int ctx = ls.ctx;
+    const int cb = lj * CH;
+    const int fb = cb >> lg;
+    const int lb = (min(cb + CH, ctx) - 1) >> lg;
+    if (wseq != ls.seq || fb < win0 || lb >= win0 + 64) load_window(fb);
+    const int64_t head_off = a.layer_offset + (int64_t)ls.kvh * a.block_size * D;
+    auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {          // element of token t (< ctx), dim 0
+      t = min(t, ctx - 1);
+      const int id = big_blocks ? __builtin_amdgcn_readlane(wreg, (t >> lg) - win0)
+                                : __shfl(wreg, (t >> lg) - win0);
       return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
     };
-    auto load_chunk = [&](int j, uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
-      const int cb = j * CH;
-      const int fb = cb >> lg;
-      const int lb = (min(cb + CH, ctx) - 1) >> lg;
-      if (fb < win0 || lb >= win0 + 64) load_window(fb);
-      int64_t ek, ev[4];
-      if (big_blocks) {
-        const int64_t base = elem_of(cb);                   // uniform block
-        ek = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
+    int64_t ek, ev[4];
+    if (big_blocks) {
+      const int64_t base = elem_of(cb);                      // one block per chunk
+      ek = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
+      for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
+    } else {
+      ek = elem_of(cb + n) + 8 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+    // advance; entering a new segment fetches its q now (used one chunk later)
+    ++lc;
+    if (++lj == ls.nc && lc < c_end) {
+      prev_bad = lbad;
+      lbad = false;
+      ls = next_seg(ls, lc);
+      lj = 0;
+      load_q(ls, qn);
+    }
+  };
+
+  // process cursor
+  Seg ps = ls;
+  int pj = lj;
+  int pj0 = lj;                                      // first chunk of the current piece
+  f32x4_t acc[VPL];
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m_ref = -__builtin_inff();                   // reference max of head n (log2 units)
+  float l_sum = 0.f;                                 // this lane's probability sum (head n)
+
+  auto process_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
+    const int ctx = ps.ctx;
+    const int cb = pj * CH;
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      uint32_t ka[4];
+      if constexpr (KV == Ty::FP8) {
+        fp8x4_to<OQK>(kr[k][0], ka[0], ka[1]);
+        fp8x4_to<OQK>(kr[k][1], ka[2], ka[3]);
       } else {
-        ek = elem_of(cb + n) + 8 * g;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
+        ka[0] = kr[k][0]; ka[1] = kr[k][1]; ka[2] = kr[k][2]; ka[3] = kr[k][3];
       }
+      const uint4 q4 = s_q[wave][k][lane];
+      const uint32_t qb[4] = {q4.x, q4.y, q4.z, q4.w};
+      s = mfma_k32<OQK>(ka, qb, s);
+    }
+    const bool tail = cb + CH > ctx;
+    float z[4];
 #pragma unroll
-      for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
-    };
-
-    f32x4_t acc[VPL];
-#pragma unroll
-    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float m_ref = -__builtin_inff();        // reference max of head n (log2 units)
-    float l_sum = 0.f;                      // this lane's probability sum (head n)
-
-    auto process_chunk = [&](int j, uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
-      const int cb = j * CH;
-      f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        uint32_t ka[4];
-        if constexpr (KV == Ty::FP8) {
-          fp8x4_to<OQK>(kr[k][0], ka[0], ka[1]);
-          fp8x4_to<OQK>(kr[k][1], ka[2], ka[3]);
-        } else {
-          ka[0] = kr[k][0]; ka[1] = kr[k][1]; ka[2] = kr[k][2]; ka[3] = kr[k][3];
-        }
-        const uint4 q4 = s_q[wave][k][lane];
-        const uint32_t qb[4] = {q4.x, q4.y, q4.z, q4.w};
-        s = mfma_k32<OQK>(ka, qb, s);
-      }
-      const bool tail = cb + CH > ctx;
-      float z[4];
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = (n < G) && (cb + 4 * g + r < ctx);
+      z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
+    }
+    const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    if (__any(lmax > m_ref + TAU)) {
+      float hm = fmaxf(lmax, __shfl_xor(lmax, 16));
+      hm = fmaxf(hm, __shfl_xor(hm, 32));
+      const float mn = fmaxf(m_ref, hm);
+      const float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
+      m_ref = mn;
+      l_sum *= al;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = (n < G) && (cb + 4 * g + r < ctx);
-        z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
-      }
-      const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      if (__any(lmax > m_ref + TAU)) {
-        float hm = fmaxf(lmax, __shfl_xor(lmax, 16));
-        hm = fmaxf(hm, __shfl_xor(hm, 32));
-        const float mn = fmaxf(m_ref, hm);
-        const float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
-        m_ref = mn;
-        l_sum *= al;
+        const float ar = __shfl(al, 4 * g + r);      // factor of accumulator row 4g + r
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(al, 4 * g + r);      // factor of accumulator row 4g + r
-#pragma unroll
-          for (int m = 0; m < VPL; ++m) acc[m][r] *= ar;
-        }
+        for (int m = 0; m < VPL; ++m) acc[m][r] *= ar;
       }
-      float p[4];
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      p[r] = (z[r] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+    const uint32_t pa0 = pack2<OPV>(p[0], p[1]);
+    const uint32_t pa1 = pack2<OPV>(p[2], p[3]);
+    {
+      // the normaliser sums exactly the rounded weights the matrix core uses
+      float q0, q1, q2, q3;
+      unpack2<OPV>(pa0, q0, q1);
+      unpack2<OPV>(pa1, q2, q3);
+      l_sum += (q0 + q1) + (q2 + q3);
+    }
+    if (tail) {                           // tokens past the context: zero values
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        p[r] = (z[r] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-      const uint32_t pa0 = pack2<OPV>(p[0], p[1]);
-      const uint32_t pa1 = pack2<OPV>(p[2], p[3]);
-      {
-        // the normaliser sums exactly the rounded weights the matrix core uses
-        float q0, q1, q2, q3;
-        unpack2<OPV>(pa0, q0, q1);
-        unpack2<OPV>(pa1, q2, q3);
-        l_sum += (q0 + q1) + (q2 + q3);
-      }
-      if (tail) {                           // tokens past the context: zero values
+        if (cb + 4 * g + r >= ctx)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (cb + 4 * g + r >= ctx)
-#pragma unroll
-            for (int x = 0; x < VDW; ++x) vr[r][x] = 0u;
-      }
-      uint32_t vw[4][VPL / 2];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (KV == Ty::FP8) {
-#pragma unroll
-          for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(vr[r][x], vw[r][2 * x], vw[r][2 * x + 1]);
-        } else {
-#pragma unroll
-          for (int x = 0; x < VPL / 2; ++x) vw[r][x] = vr[r][x];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < VPL; ++m) {
-        const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t b0 = __builtin_amdgcn_perm(vw[1][m >> 1], vw[0][m >> 1], sel);
-        const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
-        acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
-      }
-    };
-
-    {
-      uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb[4][VDW];
-      const int last = j1 - 1;
-      int j = j0;
-      int left = j1 - j0;
-      load_chunk(j, ka, va);
-      for (; left >= 2; left -= 2) {
-        load_chunk(min(j + 1, last), kb, vb);
-        process_chunk(j, ka, va);
-        ++j;
-        load_chunk(min(j + 1, last), ka, va);
-        process_chunk(j, kb, vb);
-        ++j;
-      }
-      if (left == 1) process_chunk(j, ka, va);
+          for (int x = 0; x < VDW; ++x) vr[r][x] = 0u;
     }
-    bad = __any(bad);
+    uint32_t vw[4][VPL / 2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (KV == Ty::FP8) {
+#pragma unroll
+        for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(vr[r][x], vw[r][2 * x], vw[r][2 * x + 1]);
+      } else {
+#pragma unroll
+        for (int x = 0; x < VPL / 2; ++x) vw[r][x] = vr[r][x];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) {
+      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b0 = __builtin_amdgcn_perm(vw[1][m >> 1], vw[0][m >> 1], sel);
+      const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
+      acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
+    }
+  };
 
-    // ---- finish the piece -------------------------------------------------
+  // Write the current piece (final rows or a partial) and reset the state.
+  auto finish_piece = [&](bool bad) __attribute__((always_inline)) {
+    bad = __any(bad);
     float lt = l_sum + __shfl_xor(l_sum, 16);
     lt += __shfl_xor(lt, 32);
-    const bool whole = (j0 == 0) && (j1 == nc);
+    const bool whole = (pj0 == 0) && (pj == ps.nc);
+    const int64_t out_row0 = ((int64_t)ps.seq * a.num_q_heads + (int64_t)ps.kvh * G) * D;
+    const int64_t seg = (int64_t)ps.seq * H + ps.kvh;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * g + r;                      // accumulator row = head
@@ -433,7 +458,7 @@ attend_sk_kernel(const DecodeParams a) {
 #pragma unroll
           for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm);
         } else {
-          const int64_t slot = ((w + seg) * G + h);
+          const int64_t slot = (w + seg) * G + h;
           float* wo = a.ws_o + slot * D + VPL * n;
 #pragma unroll
           for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[m][r];
@@ -444,7 +469,53 @@ attend_sk_kernel(const DecodeParams a) {
         }
       }
     }
-    c += j1 - j0;
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    m_ref = -__builtin_inff();
+    l_sum = 0.f;
+  };
+
+  // After processing chunk pj of ps: close the piece at a segment end and
+  // switch the process cursor to the load cursor's segment.
+  auto advance = [&]() __attribute__((always_inline)) {
+    ++pj;
+    if (pj == ps.nc) {
+      // the load cursor has moved on (its flag is prev_bad) unless the wave's
+      // range ended here
+      finish_piece((ls.seq == ps.seq && ls.kvh == ps.kvh) ? lbad : prev_bad);
+      ps = ls;
+      pj = 0;
+      pj0 = 0;
+      store_q(qn);
+    }
+  };
+
+  {
+    uint32_t q0[KS][4];
+    load_q(ls, q0);
+    store_q(q0);
+    uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb[4][VDW];
+    int64_t left = c_end - c;                        // chunks still to process
+    load_chunk(ka, va);
+    // each step prefetches the next chunk (a harmless reload of the last one
+    // at the end of the range) and processes the current one
+    auto step = [&](uint32_t (&kc)[KS][KDW], uint32_t (&vc)[4][VDW],
+                    uint32_t (&kn)[KS][KDW], uint32_t (&vn)[4][VDW]) __attribute__((always_inline)) {
+      if (lc < c_end) {
+        load_chunk(kn, vn);
+      }
+      process_chunk(kc, vc);
+      --left;
+      if (left > 0) advance();
+    };
+    while (left >= 2) {
+      step(ka, va, kb, vb);
+      step(kb, vb, ka, va);
+    }
+    if (left == 1) step(ka, va, kb, vb);
+    // close the last piece (ends inside or at the end of its segment)
+    ++pj;
+    finish_piece((ls.seq == ps.seq && ls.kvh == ps.kvh) ? lbad : prev_bad);
   }
 }
 
@@ -596,7 +667,11 @@ static int sk_blocks_t(int num_seqs) {
             lds) != hipSuccess)
       per_cu = 0;
   }
-  if (per_cu <= 0) per_cu = sk_waves_per_simd<KV, D>();   // no device: the compiled occupancy
+  // More resident workgroups than the compiled target adds no bandwidth (the
+  // slab reads already keep the memory system full at that occupancy) and
+  // only shortens each wave's range, raising the merge's share of the work.
+  const int target = sk_waves_per_simd<KV, D>();
+  if (per_cu <= 0 || per_cu > target) per_cu = target;
   const int b = cus * per_cu;
   return b >= NXCD ? b / NXCD * NXCD : NXCD;
 }
