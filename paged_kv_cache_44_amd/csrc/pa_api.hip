@@ -77,7 +77,8 @@ struct DecodePlan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace regions, in order: o, m, l (fp32), then the chunk prefix sums.
+// Workspace regions, in order: o, m, l (fp32), then (matrix-core path) the
+// chunk prefix sums.
 struct WsLayout {
   size_t o, m, l, cum, total;
 };
@@ -90,6 +91,12 @@ WsLayout ws_layout(size_t rows, int head_dim, size_t cum_entries) {
   w.cum = w.l + align256(rows * sizeof(float));
   w.total = w.cum + align256(cum_entries * sizeof(int32_t));
   return w;
+}
+
+// fp32 partial rows of the workspace
+size_t ws_rows(const DecodePlan& p, int num_seqs, int num_q_heads, int num_kv_heads) {
+  return p.mfma ? pa::sk_slots(p.sk_blocks, num_seqs, num_kv_heads) * p.g
+                : (size_t)num_seqs * num_q_heads * p.num_parts;
 }
 
 pa_status decode_supported(const pa_kv_cache* c, int num_q_heads, pa_dtype q_dtype, int* g_out) {
@@ -136,14 +143,14 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
   plan->g = g;
   plan->mfma = pa::mfma_supported((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
   if (plan->mfma) {
-    // evenly split work: partial slots for every (wave, segment) pair that
-    // can exist, plus the chunk prefix sums
+    // split chunk stream: partial slots for every piece that can exist, and
+    // the chunk prefix sums
     plan->sk_blocks = pa::sk_blocks((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
     plan->part_tokens = 16;
     plan->num_parts = 1;
-    const size_t waves = (size_t)plan->sk_blocks * 4;
-    const size_t rows = (waves + (size_t)num_seqs * c->num_kv_heads) * g;
-    plan->ws_bytes = ws_layout(rows, c->head_dim, (size_t)num_seqs + 1).total;
+    const size_t rows = ws_rows(*plan, num_seqs, num_q_heads, c->num_kv_heads);
+    plan->ws_bytes =
+        ws_layout(rows, c->head_dim, (size_t)num_seqs + 1).total;
     return PA_OK;
   }
   plan->sk_blocks = 0;
@@ -151,8 +158,8 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
   plan->num_parts = std::max(1, (max_ctx + plan->part_tokens - 1) / plan->part_tokens);
   if (plan->num_parts > 65535) return PA_ERR_UNSUPPORTED;   // grid z limit
   if (plan->num_parts > 1) {
-    const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
-    plan->ws_bytes = ws_layout(rows, c->head_dim, 0).total;
+    plan->ws_bytes = ws_layout(ws_rows(*plan, num_seqs, num_q_heads, c->num_kv_heads),
+                               c->head_dim, 0).total;
   } else {
     plan->ws_bytes = 0;
   }
@@ -212,16 +219,18 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
   a.num_kv_heads = cache->num_kv_heads;
   a.part_tokens = plan.part_tokens;
   a.num_parts = plan.num_parts;
+  a.team = plan.mfma ? pa::sk_team(cache->num_kv_heads) : 1;
   if (plan.ws_bytes > 0) {
-    const size_t rows = plan.mfma
-        ? ((size_t)plan.sk_blocks * 4 + (size_t)num_seqs * cache->num_kv_heads) * plan.g
-        : (size_t)num_seqs * num_q_heads * plan.num_parts;
-    const WsLayout L = ws_layout(rows, cache->head_dim, plan.mfma ? (size_t)num_seqs + 1 : 0);
+    const size_t rows = ws_rows(plan, num_seqs, num_q_heads, cache->num_kv_heads);
+    const WsLayout L = plan.mfma
+        ? ws_layout(rows, cache->head_dim, (size_t)num_seqs + 1)
+        : ws_layout(rows, cache->head_dim, 0);
     char* w = reinterpret_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(w + L.o);
     a.ws_m = reinterpret_cast<float*>(w + L.m);
     a.ws_l = reinterpret_cast<float*>(w + L.l);
     a.ws_cum = reinterpret_cast<int32_t*>(w + L.cum);
+
   }
   if (phases & PHASE_ATTEND) {
     const hipError_t e =

@@ -10,13 +10,18 @@
 //   O[G heads][D]        += P[G][16] . V[16][D]    (v_mfma_f32_16x16x16)
 // G <= 16 fills the 16 columns of the tile.
 //
-// Work split ("stream-K"): the (sequence, KV head) segments, sequence-major,
-// each a run of ceil(context / 16) chunks, are laid end to end; wave w of the
-// W resident waves takes chunks [w*C/W, (w+1)*C/W) of the C total. Every wave
-// gets the same number of chunks whatever the length mix, and there are no
-// empty workgroups. A segment cut by range boundaries leaves one partial
-// (running max m, sum l, unnormalised o) per piece, stored at slot
-// (wave + segment); merge_sk_kernel combines them in wave order.
+// Work split ("stream-K"): the W resident waves form teams of T waves (T =
+// the largest power of two up to 8 dividing the KV head count). Segments are
+// (sequence, head group of T KV heads), sequence-major, each a run of
+// ceil(context / 16) column chunks; team t takes columns [t*Cc/Wt,
+// (t+1)*Cc/Wt) of the Cc total, wave i of the team the i-th KV head of each
+// group. So every team gets the same amount of work whatever the length mix,
+// and the T waves of a team read the T head slices of the same KV block (one
+// contiguous stretch of the pool) at about the same time, which the memory
+// system serves markedly faster than the same number of scattered slices. A
+// segment cut by range boundaries leaves one partial (running max m, sum l,
+// unnormalised o) per piece and head, stored at slot ((team + segment) * T +
+// i); merge_sk_kernel combines them in team order.
 //
 // Layout facts used (CDNA 16x16xK MFMA, checked on gfx950): lane l holds
 // A[row l%16][k in (l/16)*KL ..], B[k in (l/16)*KL ..][col l%16] and
@@ -35,8 +40,11 @@
 //    traffic.
 //  * Block ids come from a 64-entry window of the block table held in one
 //    register (lane i = entry i), read with readlane / a lane shuffle.
-//  * Workgroups are dealt to the 8 XCDs round-robin; wave ranges are assigned
+//  * Workgroups are dealt to the 8 XCDs round-robin; team ranges are assigned
 //    so that each XCD works through one contiguous stretch of sequences.
+//  * Each loaded chunk travels with a descriptor (segment, chunk, piece
+//    boundaries), so pieces of any length, down to one chunk, are handled
+//    while the next chunk is already in flight.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -153,21 +161,24 @@ __device__ __forceinline__ int seq_chunks(const DecodeParams& a, int ctx) {
   return (ctx + CH - 1) / CH;
 }
 
-// Wave that owns global chunk c when C chunks are split over W waves.
-__device__ __forceinline__ int64_t wave_of(int64_t c, int64_t C, int64_t W) {
-  return ((c + 1) * W - 1) / C;
+// Team of a range: the W resident waves form W / T teams of T consecutive
+// (XCD-contiguous) waves; team t takes column chunks [t*Cc/Wt, (t+1)*Cc/Wt)
+// of the Cc total, one KV head of the group per wave. Owner of column chunk c:
+__device__ __forceinline__ int64_t team_of(int64_t c, int64_t Cc, int64_t Wt) {
+  return ((c + 1) * Wt - 1) / Cc;
 }
 
 }  // namespace
 
-// Occupancy: FP8 pools fit 3 waves per SIMD without spilling; 16-bit pools
-// at D = 128 would spill there and run at 2.
-template <Ty KV, int D>
-constexpr int sk_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
+// Occupancy: FP8 pools fit 3 waves per SIMD without spilling (except one
+// query head per KV head at D = 128); 16-bit pools at D = 128 would spill
+// there and run at 2.
+template <Ty KV, int D, int G>
+constexpr int sk_waves_per_simd() { return ((KV == Ty::FP8 && G > 1) || D == 64) ? 3 : 2; }
 
 template <Ty KV, Ty QT, int D, int G>
 __global__ void __launch_bounds__(NWM * 64)
-__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D>())))
+__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G>())))
 attend_sk_kernel(const DecodeParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
@@ -181,7 +192,7 @@ attend_sk_kernel(const DecodeParams a) {
   constexpr int VDW = VPL * EB / 4;       // raw V dwords per lane per token
 
   extern __shared__ int s_cum[];          // [num_seqs + 1] chunk prefix sums
-  // per wave: the q B-operand of the current segment, [step][lane] x 16 bytes
+  // per wave: the q B-operand of the current piece, [step][lane] x 16 bytes
   __shared__ uint4 s_q[NWM][KS][64];
 
   const int tid = threadIdx.x;
@@ -190,7 +201,8 @@ attend_sk_kernel(const DecodeParams a) {
   const int g = lane >> 4;                // row group
   const int n = lane & 15;                // column: head (scores) / dim slice (values)
   const int S = a.num_seqs;
-  const int H = a.num_kv_heads;
+  const int T = a.team;                   // waves per team = KV heads per head group
+  const int HG = a.num_kv_heads / T;      // head groups
 
   // ---- chunk prefix sums over sequences (every workgroup, in LDS) ---------
   {
@@ -222,17 +234,20 @@ attend_sk_kernel(const DecodeParams a) {
       for (int s = tid; s <= S; s += NWM * 64) a.ws_cum[s] = s_cum[s];
     }
   }
-  const int64_t CS = s_cum[S];                                  // chunks per KV head
-  const int64_t C = CS * H;
-  const int64_t W = (int64_t)gridDim.x * NWM;
+  const int64_t CS = __builtin_amdgcn_readfirstlane(s_cum[S]);   // chunks per KV head
+  const int64_t Cc = CS * HG;                                   // column chunks
   // XCD-contiguous wave numbering: workgroup b runs on XCD b % 8; give each
-  // XCD one contiguous stretch of the chunk space (gridDim.x is a multiple of 8)
+  // XCD one contiguous stretch of the column stream (gridDim.x is a multiple
+  // of 8, and T divides the 4 waves of a workgroup pair)
   const int per_xcd = gridDim.x / NXCD;
   const int vb = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
   const int64_t w = (int64_t)vb * NWM + wave;
-  int64_t c = (w * C) / W;
-  const int64_t c_end = ((w + 1) * C) / W;
-  if (c >= c_end) return;
+  const int64_t Wt = (int64_t)gridDim.x * NWM / T;              // teams
+  const int64_t team = w / T;
+  const int ti = (int)(w - team * T);                           // KV head within the group
+  int64_t lc = (team * Cc) / Wt;                                // next column chunk to load
+  const int64_t c_end = ((team + 1) * Cc) / Wt;
+  if (lc >= c_end) return;
 
   const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
   const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
@@ -242,44 +257,43 @@ attend_sk_kernel(const DecodeParams a) {
   const bool big_blocks = a.block_size >= CH;                   // one block per chunk
   const float qk_scale = a.qk_scale_log2;
 
-  // ---- the chunk stream [c, c_end): a load cursor one chunk ahead of the
-  // process cursor. Segment = (sequence, KV head), sequence-major.
+  // ---- the load cursor walks the team's range chunk by chunk, one chunk
+  // ahead of the processing; each loaded chunk travels with a descriptor.
+  // Segment = (sequence, head group), sequence-major; this wave's KV head in
+  // it is hg * T + ti.
   struct Seg {
-    int seq, kvh, nc, ctx;
+    int seq, hg, nc, ctx;
   };
-  auto seg_at = [&](int64_t cg, int& j) __attribute__((always_inline)) -> Seg {     // segment holding global chunk cg
-    int lo = 0, hi = S - 1;                          // last s with s_cum[s] * H <= cg
+  struct Desc {                     // one chunk in flight
+    int seq, hg, nc, ctx, j;        // segment and chunk index within it
+    bool first, last, bad;          // piece boundaries; bad block id seen in the piece
+  };
+  auto seg_at = [&](int64_t cg, int& j) __attribute__((always_inline)) -> Seg {     // segment holding column chunk cg
+    int lo = 0, hi = S - 1;                          // last s with s_cum[s] * HG <= cg
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)s_cum[mid] * H <= cg) lo = mid; else hi = mid - 1;
+      if ((int64_t)s_cum[mid] * HG <= cg) lo = mid; else hi = mid - 1;
     }
+    lo = __builtin_amdgcn_readfirstlane(lo);
     Seg sg;
     sg.seq = lo;
-    sg.nc = s_cum[lo + 1] - s_cum[lo];
-    const int64_t rel = cg - (int64_t)s_cum[lo] * H;
-    sg.kvh = (int)(rel / sg.nc);
-    j = (int)(rel - (int64_t)sg.kvh * sg.nc);
+    sg.nc = __builtin_amdgcn_readfirstlane(s_cum[lo + 1] - s_cum[lo]);
+    const int64_t rel = cg - (int64_t)__builtin_amdgcn_readfirstlane(s_cum[lo]) * HG;
+    sg.hg = (int)(rel / sg.nc);
+    j = (int)(rel - (int64_t)sg.hg * sg.nc);
     sg.ctx = a.context_lens[lo];
     return sg;
   };
-  auto next_seg = [&](const Seg& sg, int64_t cg_next) __attribute__((always_inline)) -> Seg {   // segment after sg
-    if (sg.kvh + 1 < H) {
-      Seg n2 = sg;
-      n2.kvh = sg.kvh + 1;
-      return n2;
-    }
-    int j;
-    return seg_at(cg_next, j);
-  };
-
-  // load cursor: segment, chunk, block-table window (lane i = entry win0 + i)
   int lj = 0;
-  Seg ls = seg_at(c, lj);
+  Seg ls = seg_at(lc, lj);
+  bool lfirst = true;                                // next loaded chunk starts a piece
+  bool lbad = false;                                 // bad block id seen in the load piece
+
+  // block-table window: lane i = entry win0 + i of sequence wseq
   int win0 = -(1 << 30);                             // empty window: first use loads it
-  int wseq = -1;                                     // sequence the window belongs to
+  int wseq = -1;
   int wreg = 0;
-  bool lbad = false;                                 // bad block id in the load segment
-  int64_t lc = c;                                    // global index of the next chunk to load
+  bool wbad = false;                                 // the window holds a bad id within the context
   auto load_window = [&](int blk) __attribute__((always_inline)) {
     win0 = blk;
     wseq = ls.seq;
@@ -287,12 +301,15 @@ attend_sk_kernel(const DecodeParams a) {
     const int last = (ls.ctx - 1) >> lg;
     const int32_t* trow = a.block_tables + (int64_t)ls.seq * a.max_blocks_per_seq;
     int id = (e <= last) ? trow[e] : 0;
-    if (id < 0 || id >= a.num_blocks) { id = 0; if (e <= last) lbad = true; }
-    wreg = id;
+    const bool badl = id < 0 || id >= a.num_blocks;
+    wbad = __any(badl);
+    wreg = badl ? 0 : id;
   };
-  // q of a segment as the B operand (lane l: head l%16, dims 32k + 8(l/16) .. +8)
-  auto load_q = [&](const Seg& sg, uint32_t (&qr)[KS][4]) {
-    const int64_t row = ((int64_t)sg.seq * a.num_q_heads + (int64_t)sg.kvh * G + n) * D;
+  // q of this wave's KV head in a segment as the B operand (lane l: head
+  // l%16, dims 32k + 8(l/16) .. +8)
+  auto load_q = [&](const Seg& sg, uint32_t (&qr)[KS][4]) __attribute__((always_inline)) {
+    const int kvh = sg.hg * T + ti;
+    const int64_t row = ((int64_t)sg.seq * a.num_q_heads + (int64_t)kvh * G + n) * D;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       if (n < G) {
@@ -302,21 +319,30 @@ attend_sk_kernel(const DecodeParams a) {
       }
     }
   };
-  auto store_q = [&](const uint32_t (&qr)[KS][4]) {
+  // q of the newest piece, fetched when its first chunk is loaded and put
+  // into LDS when the next chunk is loaded (or before the first chunk is
+  // processed, whichever comes first); the piece before it is finished by then.
+  uint32_t qn[KS][4];
+  bool qpend = false;
+  auto flush_q = [&]() __attribute__((always_inline)) {
+    if (qpend) {
 #pragma unroll
-    for (int k = 0; k < KS; ++k) s_q[wave][k][lane] = make_uint4(qr[k][0], qr[k][1], qr[k][2], qr[k][3]);
+      for (int k = 0; k < KS; ++k) s_q[wave][k][lane] = make_uint4(qn[k][0], qn[k][1], qn[k][2], qn[k][3]);
+      qpend = false;
+    }
   };
-  uint32_t qn[KS][4];                                // q of the load cursor's segment
-  bool prev_bad = false;                             // bad flag of the segment the load cursor left
 
-  // Issue the loads of chunk lj of segment ls, then advance the load cursor.
-  auto load_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
+  // Issue the loads of the load cursor's chunk (and of q when the chunk
+  // starts a piece), fill its descriptor, then advance the load cursor.
+  auto load_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW],
+                        Desc& ds) __attribute__((always_inline)) {
     const int ctx = ls.ctx;
     const int cb = lj * CH;
     const int fb = cb >> lg;
     const int lb = (min(cb + CH, ctx) - 1) >> lg;
     if (wseq != ls.seq || fb < win0 || lb >= win0 + 64) load_window(fb);
-    const int64_t head_off = a.layer_offset + (int64_t)ls.kvh * a.block_size * D;
+    lbad = lbad || wbad;
+    const int64_t head_off = a.layer_offset + (int64_t)(ls.hg * T + ti) * a.block_size * D;
     auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {          // element of token t (< ctx), dim 0
       t = min(t, ctx - 1);
       const int id = big_blocks ? __builtin_amdgcn_readlane(wreg, (t >> lg) - win0)
@@ -338,30 +364,86 @@ attend_sk_kernel(const DecodeParams a) {
     for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
-    // advance; entering a new segment fetches its q now (used one chunk later)
-    ++lc;
-    if (++lj == ls.nc && lc < c_end) {
-      prev_bad = lbad;
-      lbad = false;
-      ls = next_seg(ls, lc);
-      lj = 0;
+    flush_q();
+    if (lfirst) {
       load_q(ls, qn);
+      qpend = true;
+    }
+    ds.seq = ls.seq;
+    ds.hg = ls.hg;
+    ds.nc = ls.nc;
+    ds.ctx = ctx;
+    ds.j = lj;
+    ds.first = lfirst;
+    ++lc;
+    ++lj;
+    const bool seg_end = lj == ls.nc;
+    ds.last = seg_end || lc == c_end;
+    ds.bad = lbad;
+    lfirst = ds.last;
+    if (ds.last) lbad = false;
+    if (seg_end && lc < c_end) {
+      if (ls.hg + 1 < HG) {
+        ++ls.hg;
+      } else {
+        ls = seg_at(lc, lj);
+      }
+      lj = 0;
     }
   };
 
-  // process cursor
-  Seg ps = ls;
-  int pj = lj;
-  int pj0 = lj;                                      // first chunk of the current piece
+  // ---- processing state of the current piece
+  int pj0 = 0;                                       // first chunk of the piece
   f32x4_t acc[VPL];
 #pragma unroll
   for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   float m_ref = -__builtin_inff();                   // reference max of head n (log2 units)
   float l_sum = 0.f;                                 // this lane's probability sum (head n)
 
-  auto process_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW]) {
-    const int ctx = ps.ctx;
-    const int cb = pj * CH;
+  // Write the piece that ends with chunk ds (final rows or a partial) and
+  // reset the state.
+  auto finish_piece = [&](const Desc& ds) __attribute__((always_inline)) {
+    const bool bad = ds.bad;
+    float lt = l_sum + __shfl_xor(l_sum, 16);
+    lt += __shfl_xor(lt, 32);
+    const bool whole = (pj0 == 0) && (ds.j + 1 == ds.nc);
+    const int kvh = ds.hg * T + ti;
+    const int64_t out_row0 = ((int64_t)ds.seq * a.num_q_heads + (int64_t)kvh * G) * D;
+    const int64_t cseg = (int64_t)ds.seq * HG + ds.hg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;                      // accumulator row = head
+      const float lh = __shfl(lt, h);
+      const float mh = __shfl(m_ref, h);
+      if (h < G) {
+        if (whole) {
+          const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
+          const int64_t o = out_row0 + (int64_t)h * D + VPL * n;
+#pragma unroll
+          for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm);
+        } else {
+          const int64_t slot = ((team + cseg) * T + ti) * G + h;
+          float* wo = a.ws_o + slot * D + VPL * n;
+#pragma unroll
+          for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[m][r];
+          if (n == 0) {
+            a.ws_m[slot] = bad ? 0.f : mh;
+            a.ws_l[slot] = bad ? __builtin_nanf("") : lh;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    m_ref = -__builtin_inff();
+    l_sum = 0.f;
+  };
+
+  auto process_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW],
+                           const Desc& ds) __attribute__((always_inline)) {
+    if (ds.first) pj0 = ds.j;
+    const int ctx = ds.ctx;
+    const int cb = ds.j * CH;
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -436,94 +518,30 @@ attend_sk_kernel(const DecodeParams a) {
       const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
       acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
     }
+    if (ds.last) finish_piece(ds);
   };
 
-  // Write the current piece (final rows or a partial) and reset the state.
-  auto finish_piece = [&](bool bad) __attribute__((always_inline)) {
-    bad = __any(bad);
-    float lt = l_sum + __shfl_xor(l_sum, 16);
-    lt += __shfl_xor(lt, 32);
-    const bool whole = (pj0 == 0) && (pj == ps.nc);
-    const int64_t out_row0 = ((int64_t)ps.seq * a.num_q_heads + (int64_t)ps.kvh * G) * D;
-    const int64_t seg = (int64_t)ps.seq * H + ps.kvh;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;                      // accumulator row = head
-      const float lh = __shfl(lt, h);
-      const float mh = __shfl(m_ref, h);
-      if (h < G) {
-        if (whole) {
-          const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
-          const int64_t o = out_row0 + (int64_t)h * D + VPL * n;
-#pragma unroll
-          for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm);
-        } else {
-          const int64_t slot = (w + seg) * G + h;
-          float* wo = a.ws_o + slot * D + VPL * n;
-#pragma unroll
-          for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[m][r];
-          if (n == 0) {
-            a.ws_m[slot] = bad ? 0.f : mh;
-            a.ws_l[slot] = bad ? __builtin_nanf("") : lh;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    m_ref = -__builtin_inff();
-    l_sum = 0.f;
-  };
-
-  // After processing chunk pj of ps: close the piece at a segment end and
-  // switch the process cursor to the load cursor's segment.
-  auto advance = [&]() __attribute__((always_inline)) {
-    ++pj;
-    if (pj == ps.nc) {
-      // the load cursor has moved on (its flag is prev_bad) unless the wave's
-      // range ended here
-      finish_piece((ls.seq == ps.seq && ls.kvh == ps.kvh) ? lbad : prev_bad);
-      ps = ls;
-      pj = 0;
-      pj0 = 0;
-      store_q(qn);
-    }
-  };
-
-  {
-    uint32_t q0[KS][4];
-    load_q(ls, q0);
-    store_q(q0);
-    uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb[4][VDW];
-    int64_t left = c_end - c;                        // chunks still to process
-    load_chunk(ka, va);
-    // each step prefetches the next chunk (a harmless reload of the last one
-    // at the end of the range) and processes the current one
-    auto step = [&](uint32_t (&kc)[KS][KDW], uint32_t (&vc)[4][VDW],
-                    uint32_t (&kn)[KS][KDW], uint32_t (&vn)[4][VDW]) __attribute__((always_inline)) {
-      if (lc < c_end) {
-        load_chunk(kn, vn);
-      }
-      process_chunk(kc, vc);
-      --left;
-      if (left > 0) advance();
-    };
-    while (left >= 2) {
-      step(ka, va, kb, vb);
-      step(kb, vb, ka, va);
-    }
-    if (left == 1) step(ka, va, kb, vb);
-    // close the last piece (ends inside or at the end of its segment)
-    ++pj;
-    finish_piece((ls.seq == ps.seq && ls.kvh == ps.kvh) ? lbad : prev_bad);
+  // ---- ping-pong: load chunk i+1 while processing chunk i
+  uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb2[4][VDW];
+  Desc da, db;
+  load_chunk(ka, va, da);
+  while (true) {
+    const bool more_b = lc < c_end;
+    if (more_b) load_chunk(kb, vb2, db); else flush_q();
+    process_chunk(ka, va, da);
+    if (!more_b) break;
+    const bool more_a = lc < c_end;
+    if (more_a) load_chunk(ka, va, da); else flush_q();
+    process_chunk(kb, vb2, db);
+    if (!more_a) break;
   }
 }
 
-// Rows of empty / invalid sequences, and the merge of segments split over
-// several waves: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// One workgroup per (sequence, KV head) segment; its threads form PG groups,
-// each covering all G x D outputs (4 dims per thread) over every PG-th piece
-// with a running (online) combination, then the groups are combined in LDS.
+// Rows of empty / invalid sequences, and the merge of segments cut by team
+// range boundaries: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// One workgroup per (sequence, KV head); its threads form PG groups, each
+// covering all G x D outputs (4 dims per thread) over every PG-th piece with
+// a running (online) combination, then the groups are combined in LDS.
 template <Ty QT, int D, int G>
 __global__ void __launch_bounds__(256)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
@@ -537,7 +555,10 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
 
   const int seq = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int H = a.num_kv_heads;
+  const int T = a.team;
+  const int HG = a.num_kv_heads / T;
+  const int hg = kvh / T;
+  const int ti = kvh - hg * T;
   const int tid = threadIdx.x;
   const int grp = tid / TPG;
   const int t = tid - grp * TPG;
@@ -554,12 +575,13 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     }
     return;
   }
-  const int64_t C = (int64_t)a.ws_cum[a.num_seqs] * H;
-  const int64_t off = (int64_t)a.ws_cum[seq] * H + (int64_t)kvh * nc;
-  const int64_t w0 = wave_of(off, C, W);
-  const int64_t w1 = wave_of(off + nc - 1, C, W);
-  if (w0 == w1) return;                               // written whole by its wave
-  const int64_t seg = (int64_t)seq * H + kvh;
+  const int64_t Cc = (int64_t)a.ws_cum[a.num_seqs] * HG;
+  const int64_t Wt = W / T;
+  const int64_t off = (int64_t)a.ws_cum[seq] * HG + (int64_t)hg * nc;
+  const int64_t t0 = team_of(off, Cc, Wt);
+  const int64_t t1 = team_of(off + nc - 1, Cc, Wt);
+  if (t0 == t1) return;                               // written whole by its wave
+  const int64_t cseg = (int64_t)seq * HG + hg;
 
   float M = -__builtin_inff(), L = 0.f, O[DPT];
 #pragma unroll
@@ -579,16 +601,17 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     }
     M = mn;
   };
-  // pieces w0 + grp, w0 + grp + PG, ...; four loads in flight per step
+  // pieces of teams t0 + grp, t0 + grp + PG, ...; four loads in flight per step
   constexpr int U = 4;
-  for (int64_t wb = w0 + grp; wb <= w1; wb += (int64_t)PG * U) {
+  for (int64_t tb = t0 + grp; tb <= t1; tb += (int64_t)PG * U) {
     float mv[U], lv[U];
     float4 ov[U][NV4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t w = wb + (int64_t)u * PG;
-      const bool ok = w <= w1 && (w * C) / W != ((w + 1) * C) / W;   // empty ranges wrote nothing
-      const int64_t slot = (w + seg) * G + h;
+      const int64_t tm = tb + (int64_t)u * PG;
+      // empty team ranges wrote nothing
+      const bool ok = tm <= t1 && (tm * Cc) / Wt != ((tm + 1) * Cc) / Wt;
+      const int64_t slot = ((tm + cseg) * T + ti) * G + h;
       mv[u] = ok ? a.ws_m[slot] : -__builtin_inff();
       lv[u] = ok ? a.ws_l[slot] : 0.f;
 #pragma unroll
@@ -670,7 +693,7 @@ static int sk_blocks_t(int num_seqs) {
   // More resident workgroups than the compiled target adds no bandwidth (the
   // slab reads already keep the memory system full at that occupancy) and
   // only shortens each wave's range, raising the merge's share of the work.
-  const int target = sk_waves_per_simd<KV, D>();
+  const int target = sk_waves_per_simd<KV, D, G>();
   if (per_cu <= 0 || per_cu > target) per_cu = target;
   const int b = cus * per_cu;
   return b >= NXCD ? b / NXCD * NXCD : NXCD;
@@ -690,6 +713,19 @@ static int sk_blocks_g(int g, int num_seqs) {
 template <Ty KV, Ty QT>
 static int sk_blocks_d(int head_dim, int g, int num_seqs) {
   return head_dim == 64 ? sk_blocks_g<KV, QT, 64>(g, num_seqs) : sk_blocks_g<KV, QT, 128>(g, num_seqs);
+}
+
+// Partial slots: one per (team, column segment, head in the group) that can
+// hold a piece: (W / T + S * H / T) * T.
+size_t sk_slots(int blocks, int num_seqs, int num_kv_heads) {
+  return (size_t)blocks * NWM + (size_t)num_seqs * num_kv_heads;
+}
+
+// Waves per team: the largest power of two up to 8 that divides the KV heads.
+int sk_team(int num_kv_heads) {
+  int t = 8;
+  while (num_kv_heads % t) t >>= 1;
+  return t;
 }
 
 int sk_blocks(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {

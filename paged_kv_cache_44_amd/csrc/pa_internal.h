@@ -39,6 +39,7 @@ struct DecodeParams {
   float* ws_m;               // [num_seqs][num_q_heads][num_parts]
   float* ws_l;               // [num_seqs][num_q_heads][num_parts]
   int32_t* ws_cum;           // matrix-core path: chunk prefix sums [num_seqs + 1]
+  int32_t team;              // matrix-core path: waves per team (KV heads per head group)
 };
 
 struct WriteParams {
@@ -80,6 +81,8 @@ hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipS
 hipError_t launch_merge(const DecodeParams& a, int q_ty, hipStream_t st);
 bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
 int sk_blocks(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
+size_t sk_slots(int blocks, int num_seqs, int num_kv_heads);
+int sk_team(int num_kv_heads);
 hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
                               hipStream_t st);
 hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st);

@@ -124,3 +124,26 @@ def max_err(gpu, ref, rows=None):
     if rows is not None:
         gpu, ref = gpu[rows], ref[rows]
     return float(np.max(np.abs(gpu - ref), initial=0.0))
+
+
+# explicit mantissa bits and smallest normal exponent of the output formats
+_FMT = {"bf16": (7, -126), "f16": (10, -14), "f32": (23, -126)}
+
+
+def half_ulp(x, out_dtype):
+    """Half the spacing of the output format around |x| (subnormals: the
+    fixed spacing of the smallest binade)."""
+    mant, emin = _FMT[out_dtype]
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** emin)
+    return np.ldexp(1.0, (np.floor(np.log2(a)) - mant - 1).astype(np.int64))
+
+
+def max_err_stored(gpu, ref, out_dtype, rows=None):
+    """Largest error beyond the output format's own rounding: max |gpu - ref|
+    - half_ulp(gpu). An output stored in bf16 or f16 is the kernel's value
+    rounded once more; for large outputs that rounding alone can exceed a
+    fixed absolute tolerance (half a bf16 ulp is 1/64 on [4, 8))."""
+    if rows is not None:
+        gpu, ref = gpu[rows], ref[rows]
+    ex = np.abs(gpu - ref) - half_ulp(gpu, out_dtype)
+    return float(np.max(ex, initial=0.0))

@@ -13,8 +13,8 @@ import torch
 import paged_kv_cache_44_amd as pa
 import workloads
 from oracle import blocks as ob, codecs, paged
-from tests.gpu_helpers import (DeviceState, TOL, codes_to_tensor, max_err, say,
-                               tensor_codes)
+from tests.gpu_helpers import (DeviceState, TOL, codes_to_tensor, max_err, max_err_stored,
+                               say, tensor_codes)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +109,53 @@ def test_invalid_device_data_gives_nan_rows_only():
     assert np.all(np.isnan(got[2])) and np.all(np.isnan(got[3]))
     ref = st.oracle_decode(seqs=[0, 4])
     assert max_err(got, ref, rows=[0, 4]) <= TOL["f16"]
+
+
+def _short_heavy_contexts(rng, n):
+    """Mostly single-chunk contexts, some up to a few blocks, a few longer."""
+    u = rng.random(n)
+    return np.where(u < 0.6, rng.integers(1, 17, n),
+                    np.where(u < 0.9, rng.integers(17, 65, n), rng.integers(65, 601, n)))
+
+
+@pytest.mark.parametrize("pool,q,D,G,B,HKV,S", [
+    ("bf16", "bf16", 128, 4, 16, 8, 3000),
+    ("fp8_e4m3", "f16", 64, 2, 8, 4, 2000),
+])
+def test_many_short_segments_and_bad_ids(pool, q, D, G, B, HKV, S):
+    """Thousands of sequences, most of one 16-token chunk: every wave walks
+    through many single-chunk segments and the run-time claimed items are in
+    use. A few longer sequences carry an out-of-pool block id late in their
+    table; their rows (every KV head) must be NaN, all others exact."""
+    rng = np.random.default_rng(1000 + S)
+    ctx = _short_heavy_contexts(rng, S)
+    wl = workloads.custom(S, ctx, pool_dtype=pool, q_dtype=q, num_q_heads=G * HKV,
+                          num_kv_heads=HKV, head_dim=D, block_size=B)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    tables = wl.block_tables.copy()
+    long_seqs = np.nonzero(ctx > 8 * B)[0]
+    bad = sorted(rng.choice(long_seqs, size=min(5, len(long_seqs)), replace=False).tolist())
+    for s in bad:
+        last_blk = (int(ctx[s]) - 1) // B
+        tables[s, last_blk - 1] = -3 if s % 2 else wl.num_blocks + 7
+    say(f"{S} sequences, {int(np.sum((ctx + 15) // 16)) * HKV} chunks, bad rows {bad}")
+    got = st.decode(tables=tables)
+    good = [s for s in range(S) if s not in set(bad)]
+    for s in bad:
+        assert np.all(np.isnan(got[s])), s
+    assert np.all(np.isfinite(got[good]))
+    ref = st.oracle_decode(tables=tables, seqs=good)
+    # outputs of short contexts are close to single values, some beyond 4 in
+    # magnitude: the bound is the tolerance on top of the stored format's
+    # rounding of the output
+    err = max_err(got, ref, rows=good)
+    ex = max_err_stored(got, ref, q, rows=good)
+    say(f"max abs err {err:.3e}, beyond output rounding {ex:.3e}")
+    assert ex <= TOL[pool]
+    got2 = st.decode(tables=tables, split=True)
+    assert np.array_equal(np.isnan(got), np.isnan(got2))
+    assert np.array_equal(got[good], got2[good])
 
 
 @pytest.mark.parametrize("pool", ["f32", "f16", "bf16"])
