@@ -77,19 +77,19 @@ struct DecodePlan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace regions, in order: o, m, l (fp32), then (matrix-core path) the
-// chunk prefix sums.
+// Workspace regions, in order: o, m, l (fp32), then (matrix-core path) one
+// 16-byte merge descriptor per team.
 struct WsLayout {
-  size_t o, m, l, cum, total;
+  size_t o, m, l, team, total;
 };
 
-WsLayout ws_layout(size_t rows, int head_dim, size_t cum_entries) {
+WsLayout ws_layout(size_t rows, int head_dim, size_t teams) {
   WsLayout w;
   w.o = 0;
   w.m = align256(rows * head_dim * sizeof(float));
   w.l = w.m + align256(rows * sizeof(float));
-  w.cum = w.l + align256(rows * sizeof(float));
-  w.total = w.cum + align256(cum_entries * sizeof(int32_t));
+  w.team = w.l + align256(rows * sizeof(float));
+  w.total = w.team + align256(teams * 16);
   return w;
 }
 
@@ -144,13 +144,13 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
   plan->mfma = pa::mfma_supported((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
   if (plan->mfma) {
     // split chunk stream: partial slots for every piece that can exist, and
-    // the chunk prefix sums
+    // the teams' merge descriptors (at most one team per wave)
     plan->sk_blocks = pa::sk_blocks((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
     plan->part_tokens = 16;
     plan->num_parts = 1;
     const size_t rows = ws_rows(*plan, num_seqs, num_q_heads, c->num_kv_heads);
     plan->ws_bytes =
-        ws_layout(rows, c->head_dim, (size_t)num_seqs + 1).total;
+        ws_layout(rows, c->head_dim, (size_t)plan->sk_blocks * 4).total;
     return PA_OK;
   }
   plan->sk_blocks = 0;
@@ -223,13 +223,13 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
   if (plan.ws_bytes > 0) {
     const size_t rows = ws_rows(plan, num_seqs, num_q_heads, cache->num_kv_heads);
     const WsLayout L = plan.mfma
-        ? ws_layout(rows, cache->head_dim, (size_t)num_seqs + 1)
+        ? ws_layout(rows, cache->head_dim, (size_t)plan.sk_blocks * 4)
         : ws_layout(rows, cache->head_dim, 0);
     char* w = reinterpret_cast<char*>(workspace);
     a.ws_o = reinterpret_cast<float*>(w + L.o);
     a.ws_m = reinterpret_cast<float*>(w + L.m);
     a.ws_l = reinterpret_cast<float*>(w + L.l);
-    a.ws_cum = reinterpret_cast<int32_t*>(w + L.cum);
+    a.ws_team = reinterpret_cast<int32_t*>(w + L.team);
 
   }
   if (phases & PHASE_ATTEND) {

@@ -161,20 +161,42 @@ __device__ __forceinline__ int seq_chunks(const DecodeParams& a, int ctx) {
   return (ctx + CH - 1) / CH;
 }
 
-// Team of a range: the W resident waves form W / T teams of T consecutive
-// (XCD-contiguous) waves; team t takes column chunks [t*Cc/Wt, (t+1)*Cc/Wt)
-// of the Cc total, one KV head of the group per wave. Owner of column chunk c:
+// Team ranges. The W resident waves form Wt = W / T teams of T consecutive
+// (XCD-contiguous) waves, one KV head of the group per wave; team t takes
+// columns [t*Cc/Wt, (t+1)*Cc/Wt) of the Cc total.
+__device__ __forceinline__ int64_t team_begin(int64_t t, int64_t Cc, int64_t Wt) {
+  return t * Cc / Wt;
+}
+
+// Team whose range holds column c (the last team starting at or before c).
 __device__ __forceinline__ int64_t team_of(int64_t c, int64_t Cc, int64_t Wt) {
   return ((c + 1) * Wt - 1) / Cc;
 }
 
+// Dynamic LDS of the attention kernel: prefix sums and last-chunk lengths.
+inline size_t sk_lds_bytes(int num_seqs) {
+  return (size_t)(num_seqs + 1) * sizeof(int) + (((size_t)num_seqs + 3) & ~(size_t)3);
+}
+
 }  // namespace
 
-// Occupancy: FP8 pools fit 3 waves per SIMD without spilling (except one
-// query head per KV head at D = 128); 16-bit pools at D = 128 would spill
-// there and run at 2.
+// First of the 8 dims that lane group a (= lane / 16) holds in MFMA step k
+// of the score product, for K rows of D * EB bytes: whole-line loads put
+// dims 16a + {0, 8, 64, 72} (16-bit, D = 128), 16a + {0, 8} (16-bit, D = 64)
+// and 32a + 8k (FP8, D = 128) there; otherwise the operand layout puts dims
+// 32k + 8a.
+template <int D, int EB>
+__device__ __forceinline__ int kdim_t(int k, int a) {
+  if constexpr (D * EB == 256) return 16 * a + (k & 1) * 8 + (k >> 1) * 64;
+  else if constexpr (D * EB == 128 && EB == 2) return 16 * a + 8 * k;
+  else if constexpr (D * EB == 128) return 32 * a + 8 * k;
+  else return 32 * k + 8 * a;
+}
+
+// Occupancy: FP8 pools and D = 64 fit 3 waves per SIMD without spilling;
+// 16-bit pools at D = 128 run at 2.
 template <Ty KV, int D, int G>
-constexpr int sk_waves_per_simd() { return ((KV == Ty::FP8 && G > 1) || D == 64) ? 3 : 2; }
+constexpr int sk_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
 
 template <Ty KV, Ty QT, int D, int G>
 __global__ void __launch_bounds__(NWM * 64)
@@ -190,9 +212,21 @@ attend_sk_kernel(const DecodeParams a) {
   constexpr int VPL = D / 16;             // value elements per lane per token = P.V MFMAs
   constexpr int KDW = 8 * EB / 4;         // raw K dwords per lane per step
   constexpr int VDW = VPL * EB / 4;       // raw V dwords per lane per token
+  // K is read in whole 128-byte lines when a row has at least one: load u,
+  // lane l takes token row (l&7) + 8(u&1), 16-byte column (l>>3) + 8(u>>1);
+  // a row-rotation exchange with lane l^8 then gives lane l its MFMA row,
+  // token l%16. (Reading the operand layout directly, 64 bytes of 16 rows
+  // per load, streams markedly slower.) Otherwise lane l loads token l%16,
+  // dims 32k + 8(l/16) of step k.
+  constexpr bool KFULL = D * EB >= 128;
+  auto kdim = [](int k, int a) { return kdim_t<D, EB>(k, a); };
+  constexpr int KR = KFULL ? D * EB / 64 : KS;     // K loads per chunk
+  constexpr int KW = KFULL ? 4 : KDW;              // dwords per lane per K load
 
-  extern __shared__ int s_cum[];          // [num_seqs + 1] chunk prefix sums
-  // per wave: the q B-operand of the current piece, [step][lane] x 16 bytes
+  // [num_seqs + 1] chunk prefix sums, then [num_seqs] bytes: tokens in each
+  // sequence's last chunk (1..16), so a context length is 16 (chunks - 1) + tail
+  extern __shared__ int s_cum[];
+  // per wave: the q B-operand of the piece being processed, [step][lane]
   __shared__ uint4 s_q[NWM][KS][64];
 
   const int tid = threadIdx.x;
@@ -203,13 +237,16 @@ attend_sk_kernel(const DecodeParams a) {
   const int S = a.num_seqs;
   const int T = a.team;                   // waves per team = KV heads per head group
   const int HG = a.num_kv_heads / T;      // head groups
+  uint8_t* const s_tail = reinterpret_cast<uint8_t*>(s_cum + S + 1);
 
   // ---- chunk prefix sums over sequences (every workgroup, in LDS) ---------
   {
     int carry = 0;
     for (int base = 0; base < S; base += NWM * 64) {
       const int s = base + tid;
-      int v = (s < S) ? seq_chunks(a, a.context_lens[s]) : 0;
+      const int ctx = (s < S) ? a.context_lens[s] : 0;
+      int v = (s < S) ? seq_chunks(a, ctx) : 0;
+      if (s < S) s_tail[s] = (uint8_t)(v ? ctx - CH * (v - 1) : 0);
       // inclusive scan inside the workgroup: wave scan, then across waves
       int x = v;
 #pragma unroll
@@ -230,24 +267,28 @@ attend_sk_kernel(const DecodeParams a) {
     }
     if (tid == 0) s_cum[S] = carry;
     __syncthreads();
-    if (blockIdx.x == 0) {
-      for (int s = tid; s <= S; s += NWM * 64) a.ws_cum[s] = s_cum[s];
+  }
+  // rows of sequences with nothing to attend to: zeros for an empty context,
+  // NaN for an invalid one (negative, beyond max_context_len or the table)
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    if (s_cum[s + 1] == s_cum[s]) {
+      const float fill = a.context_lens[s] == 0 ? 0.f : __builtin_nanf("");
+      const int64_t base = (int64_t)s * a.num_q_heads * D;
+      for (int e = tid; e < a.num_q_heads * D; e += NWM * 64) store_out<QT>(a.out, base + e, fill);
     }
   }
   const int64_t CS = __builtin_amdgcn_readfirstlane(s_cum[S]);   // chunks per KV head
   const int64_t Cc = CS * HG;                                   // column chunks
+  if (Cc == 0) return;
   // XCD-contiguous wave numbering: workgroup b runs on XCD b % 8; give each
   // XCD one contiguous stretch of the column stream (gridDim.x is a multiple
-  // of 8, and T divides the 4 waves of a workgroup pair)
+  // of 8, and T divides the 8 waves of a workgroup pair)
   const int per_xcd = gridDim.x / NXCD;
   const int vb = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
   const int64_t w = (int64_t)vb * NWM + wave;
   const int64_t Wt = (int64_t)gridDim.x * NWM / T;              // teams
   const int64_t team = w / T;
   const int ti = (int)(w - team * T);                           // KV head within the group
-  int64_t lc = (team * Cc) / Wt;                                // next column chunk to load
-  const int64_t c_end = ((team + 1) * Cc) / Wt;
-  if (lc >= c_end) return;
 
   const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
   const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
@@ -257,73 +298,117 @@ attend_sk_kernel(const DecodeParams a) {
   const bool big_blocks = a.block_size >= CH;                   // one block per chunk
   const float qk_scale = a.qk_scale_log2;
 
-  // ---- the load cursor walks the team's range chunk by chunk, one chunk
-  // ahead of the processing; each loaded chunk travels with a descriptor.
+  // ---- three-stage pipeline over this wave's ranges: the index stage walks
+  // the column stream and fetches the block ids of chunk i+2, the load stage
+  // issues the K/V loads of chunk i+1, the compute stage processes chunk i.
   // Segment = (sequence, head group), sequence-major; this wave's KV head in
   // it is hg * T + ti.
   struct Seg {
     int seq, hg, nc, ctx;
   };
-  struct Desc {                     // one chunk in flight
+  // flags of a chunk in flight
+  constexpr int F_VALID = 1;        // a real chunk (else a placeholder past the wave's last)
+  constexpr int F_FIRST = 2;        // first chunk of a piece
+  constexpr int F_LAST = 4;         // last chunk of a piece
+  constexpr int F_BAD = 8;          // a bad block id was seen in the piece (set at its last chunk)
+  struct Desc {
     int seq, hg, nc, ctx, j;        // segment and chunk index within it
-    bool first, last, bad;          // piece boundaries; bad block id seen in the piece
+    int f;                          // F_* flags
   };
   auto seg_at = [&](int64_t cg, int& j) __attribute__((always_inline)) -> Seg {     // segment holding column chunk cg
     int lo = 0, hi = S - 1;                          // last s with s_cum[s] * HG <= cg
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)s_cum[mid] * HG <= cg) lo = mid; else hi = mid - 1;
+      if ((int64_t)__builtin_amdgcn_readfirstlane(s_cum[mid]) * HG <= cg) lo = mid; else hi = mid - 1;
     }
-    lo = __builtin_amdgcn_readfirstlane(lo);
     Seg sg;
     sg.seq = lo;
     sg.nc = __builtin_amdgcn_readfirstlane(s_cum[lo + 1] - s_cum[lo]);
     const int64_t rel = cg - (int64_t)__builtin_amdgcn_readfirstlane(s_cum[lo]) * HG;
     sg.hg = (int)(rel / sg.nc);
     j = (int)(rel - (int64_t)sg.hg * sg.nc);
-    sg.ctx = a.context_lens[lo];
+    sg.ctx = CH * (sg.nc - 1) + __builtin_amdgcn_readfirstlane(s_tail[lo]);
     return sg;
   };
-  int lj = 0;
-  Seg ls = seg_at(lc, lj);
-  bool lfirst = true;                                // next loaded chunk starts a piece
-  bool lbad = false;                                 // bad block id seen in the load piece
 
-  // block-table window: lane i = entry win0 + i of sequence wseq
-  int win0 = -(1 << 30);                             // empty window: first use loads it
-  int wseq = -1;
-  int wreg = 0;
-  bool wbad = false;                                 // the window holds a bad id within the context
-  auto load_window = [&](int blk) __attribute__((always_inline)) {
-    win0 = blk;
-    wseq = ls.seq;
-    const int e = blk + lane;
-    const int last = (ls.ctx - 1) >> lg;
-    const int32_t* trow = a.block_tables + (int64_t)ls.seq * a.max_blocks_per_seq;
-    int id = (e <= last) ? trow[e] : 0;
-    const bool badl = id < 0 || id >= a.num_blocks;
-    wbad = __any(badl);
-    wreg = badl ? 0 : id;
-  };
-  // q of this wave's KV head in a segment as the B operand (lane l: head
-  // l%16, dims 32k + 8(l/16) .. +8)
-  auto load_q = [&](const Seg& sg, uint32_t (&qr)[KS][4]) __attribute__((always_inline)) {
-    const int kvh = sg.hg * T + ti;
-    const int64_t row = ((int64_t)sg.seq * a.num_q_heads + (int64_t)kvh * G + n) * D;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      if (n < G) {
-        ld<4>(qw + ((row + 32 * k + 8 * g) >> 1), qr[k]);
-      } else {
-        qr[k][0] = qr[k][1] = qr[k][2] = qr[k][3] = 0u;
+  // -- index stage state: next column ic of the team's range [.., ie)
+  int64_t ic = team_begin(team, Cc, Wt);
+  const int64_t ie = team_begin(team + 1, Cc, Wt);
+  bool iact = ic < ie;                               // the index stage has chunks left
+  if (ti == 0) {
+    // merge descriptor of the team: the segment its range ends in, when that
+    // segment starts in this range and continues past it: {last team it
+    // reaches, sequence, head group, Cc when some team ranges are empty (Cc <
+    // Wt) else 0}; else {-1}
+    int4 md = make_int4(-1, 0, 0, 0);
+    if (iact) {
+      int j;
+      const Seg sg = seg_at(ie - 1, j);
+      const int64_t s0 = ie - 1 - j;                 // the segment's first column
+      if (s0 >= ic && s0 + sg.nc > ie)
+        md = make_int4((int)team_of(s0 + sg.nc - 1, Cc, Wt), sg.seq, sg.hg, Cc < Wt ? (int)Cc : 0);
+    }
+    if (lane == 0) reinterpret_cast<int4*>(a.ws_team)[team] = md;
+  }
+  if (!iact) return;
+  int ij = 0;
+  Seg is = seg_at(ic, ij);
+  bool ifirst = true;                                // next indexed chunk starts a piece
+
+  // Descriptor and block ids of the index stage's chunk; then advance. Lane
+  // i fetches the id of the chunk's i-th block (lanes past its last block
+  // repeat the last one); out-of-context entries are never read. Once the
+  // wave's chunks are exhausted it yields placeholders and repeats its last
+  // (in-bounds) id fetch, so every pipeline step issues the same loads.
+  const int32_t* irow = a.block_tables;              // table row of the last indexed chunk
+  int ifb = 0, ilb = 0;                              // its first and last block
+  auto index_chunk = [&](Desc& d, int& idr) __attribute__((always_inline)) {
+    d.f = 0;
+    if (iact) {
+      const int cb = ij * CH;
+      ifb = cb >> lg;
+      ilb = (min(cb + CH, is.ctx) - 1) >> lg;
+      irow = a.block_tables + (int64_t)is.seq * a.max_blocks_per_seq;
+      d.seq = is.seq;
+      d.hg = is.hg;
+      d.nc = is.nc;
+      d.ctx = is.ctx;
+      d.j = ij;
+      ++ic;
+      ++ij;
+      const bool seg_end = ij == is.nc;
+      const bool rng_end = ic == ie;
+      d.f = F_VALID | (ifirst ? F_FIRST : 0) | ((seg_end || rng_end) ? F_LAST : 0);
+      ifirst = seg_end || rng_end;
+      if (rng_end) {
+        iact = false;
+      } else if (seg_end) {
+        if (is.hg + 1 < HG) {
+          ++is.hg;
+        } else {
+          is = seg_at(ic, ij);
+        }
+        ij = 0;
       }
     }
+    idr = irow[min(ifb + lane, ilb)];
   };
-  // q of the newest piece, fetched when its first chunk is loaded and put
-  // into LDS when the next chunk is loaded (or before the first chunk is
-  // processed, whichever comes first); the piece before it is finished by then.
+
+  // q of this wave's KV head in chunk d's segment as the B operand (lane l:
+  // head l%16, dims 32k + 8(l/16) .. +8), fetched into qn with a piece's
+  // first chunk and put into LDS at the start of the next pipeline step,
+  // after the piece before it has been processed. Columns past the G heads
+  // repeat a real head's row: their scores are masked out.
   uint32_t qn[KS][4];
   bool qpend = false;
+  auto load_q = [&](const Desc& d) __attribute__((always_inline)) {
+    if ((d.f & (F_VALID | F_FIRST)) == (F_VALID | F_FIRST)) {
+      const int64_t row = ((int64_t)d.seq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G + (n % G)) * D;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim(k, g)) >> 1), qn[k]);
+      qpend = true;
+    }
+  };
   auto flush_q = [&]() __attribute__((always_inline)) {
     if (qpend) {
 #pragma unroll
@@ -332,67 +417,63 @@ attend_sk_kernel(const DecodeParams a) {
     }
   };
 
-  // Issue the loads of the load cursor's chunk (and of q when the chunk
-  // starts a piece), fill its descriptor, then advance the load cursor.
-  auto load_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW],
-                        Desc& ds) __attribute__((always_inline)) {
-    const int ctx = ls.ctx;
-    const int cb = lj * CH;
+  // -- load stage: issue the K/V loads of chunk d (a placeholder reloads
+  // the start of the pool)
+  bool lbad = false;                                 // bad block id seen in the load piece
+  auto load_chunk = [&](Desc& d, int idr, uint32_t (&kr)[KR][KW],
+                        uint32_t (&vr)[4][VDW]) __attribute__((always_inline)) {
+    const bool ok = d.f & F_VALID;
+    const int ctx = ok ? d.ctx : 1;
+    const int cb = ok ? d.j * CH : 0;
     const int fb = cb >> lg;
-    const int lb = (min(cb + CH, ctx) - 1) >> lg;
-    if (wseq != ls.seq || fb < win0 || lb >= win0 + 64) load_window(fb);
-    lbad = lbad || wbad;
-    const int64_t head_off = a.layer_offset + (int64_t)(ls.hg * T + ti) * a.block_size * D;
+    const bool badl = idr < 0 || idr >= a.num_blocks;
+    const bool bad = __any(badl);
+    const int idv = (badl || !ok) ? 0 : idr;
+    const int64_t head_off = ok ? a.layer_offset + (int64_t)(d.hg * T + ti) * a.block_size * D : 0;
     auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {          // element of token t (< ctx), dim 0
       t = min(t, ctx - 1);
-      const int id = big_blocks ? __builtin_amdgcn_readlane(wreg, (t >> lg) - win0)
-                                : __shfl(wreg, (t >> lg) - win0);
+      const int id = big_blocks ? __builtin_amdgcn_readfirstlane(idv) : __shfl(idv, (t >> lg) - fb);
       return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
     };
-    int64_t ek, ev[4];
+    int64_t ek[KFULL ? 2 : 1], ev[4];
     if (big_blocks) {
       const int64_t base = elem_of(cb);                      // one block per chunk
-      ek = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
+      if constexpr (KFULL) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          ek[hf] = base + (int64_t)min((lane & 7) + 8 * hf, ctx - 1 - cb) * D + (lane >> 3) * (16 / EB);
+      } else {
+        ek[0] = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
     } else {
-      ek = elem_of(cb + n) + 8 * g;
+      if constexpr (KFULL) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) ek[hf] = elem_of(cb + (lane & 7) + 8 * hf) + (lane >> 3) * (16 / EB);
+      } else {
+        ek[0] = elem_of(cb + n) + 8 * g;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
     }
+    if constexpr (KFULL) {
 #pragma unroll
-    for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
+      for (int u = 0; u < KR; ++u) ld<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
-    flush_q();
-    if (lfirst) {
-      load_q(ls, qn);
-      qpend = true;
-    }
-    ds.seq = ls.seq;
-    ds.hg = ls.hg;
-    ds.nc = ls.nc;
-    ds.ctx = ctx;
-    ds.j = lj;
-    ds.first = lfirst;
-    ++lc;
-    ++lj;
-    const bool seg_end = lj == ls.nc;
-    ds.last = seg_end || lc == c_end;
-    ds.bad = lbad;
-    lfirst = ds.last;
-    if (ds.last) lbad = false;
-    if (seg_end && lc < c_end) {
-      if (ls.hg + 1 < HG) {
-        ++ls.hg;
-      } else {
-        ls = seg_at(lc, lj);
-      }
-      lj = 0;
+    if (ok) {
+      lbad = lbad || bad;
+      if (lbad && (d.f & F_LAST)) d.f |= F_BAD;
+      if (d.f & F_LAST) lbad = false;
     }
   };
 
-  // ---- processing state of the current piece
+  // ---- compute stage state of the current piece
   int pj0 = 0;                                       // first chunk of the piece
   f32x4_t acc[VPL];
 #pragma unroll
@@ -400,16 +481,16 @@ attend_sk_kernel(const DecodeParams a) {
   float m_ref = -__builtin_inff();                   // reference max of head n (log2 units)
   float l_sum = 0.f;                                 // this lane's probability sum (head n)
 
-  // Write the piece that ends with chunk ds (final rows or a partial) and
+  // Write the piece that ends with chunk d (final rows or a partial) and
   // reset the state.
-  auto finish_piece = [&](const Desc& ds) __attribute__((always_inline)) {
-    const bool bad = ds.bad;
+  auto finish_piece = [&](const Desc& d) __attribute__((always_inline)) {
+    const bool bad = d.f & F_BAD;
     float lt = l_sum + __shfl_xor(l_sum, 16);
     lt += __shfl_xor(lt, 32);
-    const bool whole = (pj0 == 0) && (ds.j + 1 == ds.nc);
-    const int kvh = ds.hg * T + ti;
-    const int64_t out_row0 = ((int64_t)ds.seq * a.num_q_heads + (int64_t)kvh * G) * D;
-    const int64_t cseg = (int64_t)ds.seq * HG + ds.hg;
+    const bool whole = (pj0 == 0) && (d.j + 1 == d.nc);
+    const int kvh = d.hg * T + ti;
+    const int64_t out_row0 = ((int64_t)d.seq * a.num_q_heads + (int64_t)kvh * G) * D;
+    const int64_t cseg = (int64_t)d.seq * HG + d.hg;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * g + r;                      // accumulator row = head
@@ -439,20 +520,54 @@ attend_sk_kernel(const DecodeParams a) {
     l_sum = 0.f;
   };
 
-  auto process_chunk = [&](uint32_t (&kr)[KS][KDW], uint32_t (&vr)[4][VDW],
-                           const Desc& ds) __attribute__((always_inline)) {
-    if (ds.first) pj0 = ds.j;
-    const int ctx = ds.ctx;
-    const int cb = ds.j * CH;
+  auto process_chunk = [&](const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW],
+                           const Desc& d) __attribute__((always_inline)) {
+    if (d.f & F_FIRST) pj0 = d.j;
+    const int ctx = d.ctx;
+    const int cb = d.j * CH;
+    // raw K of MFMA step k for this lane's token (l % 16)
+    uint32_t kraw[KS][KDW];
+    if constexpr (KFULL) {
+      const bool hs = (lane >> 3) & 1;                // lane l holds token l%16 half the time
+      if constexpr (EB == 2) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+#pragma unroll
+          for (int v = 0; v < KR / 2; ++v) {
+            // loads 2v, 2v+1 are token rows p and p+8 of the same columns
+            const uint32_t mine0 = kr[2 * v][x], mine1 = kr[2 * v + 1][x];
+            const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(hs ? mine0 : mine1),
+                                                                       0x128, 0xF, 0xF, false);
+            kraw[2 * v][x] = hs ? got : mine0;
+            kraw[2 * v + 1][x] = hs ? mine1 : got;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const uint32_t own = hs ? kr[1][x] : kr[0][x];
+          const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(hs ? kr[0][x] : kr[1][x]),
+                                                                     0x128, 0xF, 0xF, false);
+          const uint32_t lo = hs ? got : own, hi = hs ? own : got;
+          kraw[x >> 1][x & 1] = lo;
+          kraw[2 + (x >> 1)][x & 1] = hi;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+#pragma unroll
+        for (int x = 0; x < KDW; ++x) kraw[k][x] = kr[k][x];
+    }
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       uint32_t ka[4];
       if constexpr (KV == Ty::FP8) {
-        fp8x4_to<OQK>(kr[k][0], ka[0], ka[1]);
-        fp8x4_to<OQK>(kr[k][1], ka[2], ka[3]);
+        fp8x4_to<OQK>(kraw[k][0], ka[0], ka[1]);
+        fp8x4_to<OQK>(kraw[k][1], ka[2], ka[3]);
       } else {
-        ka[0] = kr[k][0]; ka[1] = kr[k][1]; ka[2] = kr[k][2]; ka[3] = kr[k][3];
+        ka[0] = kraw[k][0]; ka[1] = kraw[k][1]; ka[2] = kraw[k][2]; ka[3] = kraw[k][3];
       }
       const uint4 q4 = s_q[wave][k][lane];
       const uint32_t qb[4] = {q4.x, q4.y, q4.z, q4.w};
@@ -493,22 +608,17 @@ attend_sk_kernel(const DecodeParams a) {
       unpack2<OPV>(pa1, q2, q3);
       l_sum += (q0 + q1) + (q2 + q3);
     }
-    if (tail) {                           // tokens past the context: zero values
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (cb + 4 * g + r >= ctx)
-#pragma unroll
-          for (int x = 0; x < VDW; ++x) vr[r][x] = 0u;
-    }
+    // values of tokens past the context are zeroed (they may be NaN codes)
     uint32_t vw[4][VPL / 2];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      const bool live = !tail || cb + 4 * g + r < ctx;
       if constexpr (KV == Ty::FP8) {
 #pragma unroll
-        for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(vr[r][x], vw[r][2 * x], vw[r][2 * x + 1]);
+        for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(live ? vr[r][x] : 0u, vw[r][2 * x], vw[r][2 * x + 1]);
       } else {
 #pragma unroll
-        for (int x = 0; x < VPL / 2; ++x) vw[r][x] = vr[r][x];
+        for (int x = 0; x < VPL / 2; ++x) vw[r][x] = live ? vr[r][x] : 0u;
       }
     }
 #pragma unroll
@@ -518,70 +628,78 @@ attend_sk_kernel(const DecodeParams a) {
       const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
       acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
     }
-    if (ds.last) finish_piece(ds);
+    if (d.f & F_LAST) finish_piece(d);
   };
 
-  // ---- ping-pong: load chunk i+1 while processing chunk i
-  uint32_t ka[KS][KDW], va[4][VDW], kb[KS][KDW], vb2[4][VDW];
-  Desc da, db;
-  load_chunk(ka, va, da);
+  // ---- the pipeline. Chunks alternate between buffers A and B; a chunk's
+  // block ids live in the id register of its buffer from indexing to
+  // loading. Each step: q of the previous step's new piece goes to LDS; q of
+  // chunk i+1 is fetched if it starts a piece (the only conditional load,
+  // issued first so that it cannot shorten the waits that follow); the ids
+  // of chunk i+2 and the K/V of chunk i+1 are fetched; chunk i is processed.
+  // The waits before processing leave every load of the step in flight.
+  uint32_t kA[KR][KW], vA[4][VDW], kB[KR][KW], vB[4][VDW];
+  Desc dA, dB;                                       // chunk in (or bound for) each buffer
+  int iA = 0, iB = 0;
+  index_chunk(dA, iA);
+  load_q(dA);
+  index_chunk(dB, iB);
+  load_chunk(dA, iA, kA, vA);
   while (true) {
-    const bool more_b = lc < c_end;
-    if (more_b) load_chunk(kb, vb2, db); else flush_q();
-    process_chunk(ka, va, da);
-    if (!more_b) break;
-    const bool more_a = lc < c_end;
-    if (more_a) load_chunk(ka, va, da); else flush_q();
-    process_chunk(kb, vb2, db);
-    if (!more_a) break;
+    Desc dn;
+    flush_q();
+    load_q(dB);
+    index_chunk(dn, iA);
+    load_chunk(dB, iB, kB, vB);
+    process_chunk(kA, vA, dA);
+    if (!(dB.f & F_VALID)) break;
+    dA = dn;
+    flush_q();
+    load_q(dA);
+    index_chunk(dn, iB);
+    load_chunk(dA, iA, kA, vA);
+    process_chunk(kB, vB, dB);
+    if (!(dA.f & F_VALID)) break;
+    dB = dn;
   }
 }
 
-// Rows of empty / invalid sequences, and the merge of segments cut by team
-// range boundaries: M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-// One workgroup per (sequence, KV head); its threads form PG groups, each
-// covering all G x D outputs (4 dims per thread) over every PG-th piece with
-// a running (online) combination, then the groups are combined in LDS.
+// Merge of segments cut by team range boundaries: M = max_p m_p,
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p. Workgroup (t, i)
+// merges KV head i of the group of the segment recorded by team t (if any),
+// over its pieces from teams t .. r1. Threads form PG groups, each covering
+// all G x D outputs (DPT dims per thread) over every PG-th piece with a
+// running (online) combination; the groups are combined in LDS.
 template <Ty QT, int D, int G>
 __global__ void __launch_bounds__(256)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
-  constexpr int DPT = (G * D > 1024) ? 8 : 4;         // dims per thread
+  constexpr int GD = G * D;
+  constexpr int DPT = GD >= 1024 ? 16 : (GD >= 512 ? 8 : 4);   // dims per thread
   constexpr int NV4 = DPT / 4;
-  constexpr int TPG = G * D / DPT;                    // threads per group
+  constexpr int TPG = GD / DPT;                        // threads per group
   static_assert(TPG <= 256 && 256 % TPG == 0, "group size");
-  constexpr int PG = 256 / TPG;                       // piece groups
+  constexpr int PG = 256 / TPG;                        // piece groups
   __shared__ float s_m[PG][G], s_l[PG][G];
-  __shared__ float s_o[PG > 1 ? PG : 1][G * D];
+  __shared__ float s_o[PG > 1 ? PG : 1][GD];
 
-  const int seq = blockIdx.x;
-  const int kvh = blockIdx.y;
+  const int64_t t0 = blockIdx.x;
+  const int ti = blockIdx.y;
+  const int4 md = reinterpret_cast<const int4*>(a.ws_team)[t0];
+  const int64_t t1 = md.x;
+  if (t1 <= t0) return;                                // no segment to merge here
   const int T = a.team;
   const int HG = a.num_kv_heads / T;
-  const int hg = kvh / T;
-  const int ti = kvh - hg * T;
+  const int64_t Wt = W / T;
+  const int seq = md.y, hg = md.z;
+  const int kvh = hg * T + ti;
   const int tid = threadIdx.x;
   const int grp = tid / TPG;
   const int t = tid - grp * TPG;
   const int h = t / (D / DPT);
   const int d0 = (t - h * (D / DPT)) * DPT;
-  const int ctx = a.context_lens[seq];
   const int64_t orow = ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h) * D + d0;
-  const int nc = seq_chunks(a, ctx);
-  if (nc == 0) {
-    if (grp == 0) {
-      const float fill = (ctx == 0) ? 0.f : __builtin_nanf("");
-#pragma unroll
-      for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, fill);
-    }
-    return;
-  }
-  const int64_t Cc = (int64_t)a.ws_cum[a.num_seqs] * HG;
-  const int64_t Wt = W / T;
-  const int64_t off = (int64_t)a.ws_cum[seq] * HG + (int64_t)hg * nc;
-  const int64_t t0 = team_of(off, Cc, Wt);
-  const int64_t t1 = team_of(off + nc - 1, Cc, Wt);
-  if (t0 == t1) return;                               // written whole by its wave
   const int64_t cseg = (int64_t)seq * HG + hg;
+  const int64_t Cs = md.w;                             // nonzero: some team ranges are empty
 
   float M = -__builtin_inff(), L = 0.f, O[DPT];
 #pragma unroll
@@ -601,7 +719,8 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     }
     M = mn;
   };
-  // pieces of teams t0 + grp, t0 + grp + PG, ...; four loads in flight per step
+  // pieces of teams t0 + grp, t0 + grp + PG, ...; U loads in flight per group
+  // (every nonempty team in t0 .. t1 holds a piece: the segment covers it)
   constexpr int U = 4;
   for (int64_t tb = t0 + grp; tb <= t1; tb += (int64_t)PG * U) {
     float mv[U], lv[U];
@@ -609,8 +728,7 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t tm = tb + (int64_t)u * PG;
-      // empty team ranges wrote nothing
-      const bool ok = tm <= t1 && (tm * Cc) / Wt != ((tm + 1) * Cc) / Wt;
+      const bool ok = tm <= t1 && (Cs == 0 || team_begin(tm, Cs, Wt) != team_begin(tm + 1, Cs, Wt));
       const int64_t slot = ((tm + cseg) * T + ti) * G + h;
       mv[u] = ok ? a.ws_m[slot] : -__builtin_inff();
       lv[u] = ok ? a.ws_l[slot] : 0.f;
@@ -643,7 +761,7 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
 // ---------------------------------------------------------------------------
 template <Ty KV, Ty QT, int D, int G>
 static hipError_t launch_t(const DecodeParams& a, int blocks, hipStream_t st) {
-  const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+  const size_t lds = sk_lds_bytes(a.num_seqs);
   hipLaunchKernelGGL((attend_sk_kernel<KV, QT, D, G>), dim3(blocks), dim3(NWM * 64), lds, st, a);
   return hipGetLastError();
 }
@@ -680,7 +798,7 @@ bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {
 template <Ty KV, Ty QT, int D, int G>
 static int sk_blocks_t(int num_seqs) {
   int dev = 0, cus = 256, per_cu = 0;
-  const size_t lds = (size_t)(num_seqs + 1) * sizeof(int);
+  const size_t lds = sk_lds_bytes(num_seqs);
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
@@ -748,7 +866,7 @@ hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g,
 
 template <Ty QT, int D>
 static hipError_t launch_merge_sk_d(const DecodeParams& a, int64_t W, int g, hipStream_t st) {
-  dim3 grid(a.num_seqs, a.num_kv_heads);
+  dim3 grid((unsigned)(W / a.team), (unsigned)a.team);
   switch (g) {
     case 1: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 1>), grid, dim3(256), 0, st, a, W); break;
     case 2: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 2>), grid, dim3(256), 0, st, a, W); break;

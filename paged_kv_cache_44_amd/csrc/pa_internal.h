@@ -38,8 +38,8 @@ struct DecodeParams {
   float* ws_o;               // [num_seqs][num_q_heads][num_parts][head_dim]
   float* ws_m;               // [num_seqs][num_q_heads][num_parts]
   float* ws_l;               // [num_seqs][num_q_heads][num_parts]
-  int32_t* ws_cum;           // matrix-core path: chunk prefix sums [num_seqs + 1]
   int32_t team;              // matrix-core path: waves per team (KV heads per head group)
+  int32_t* ws_team;          // matrix-core path: merge descriptors, int4 per team
 };
 
 struct WriteParams {
