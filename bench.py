@@ -66,6 +66,10 @@ def parse():
     ap.add_argument("--flush-iters", type=int, default=20)
     ap.add_argument("--print-source-hash", action="store_true",
                     help="print the hash of the attention kernel sources and exit")
+    ap.add_argument("--swap", action="store_true",
+                    help="time the long FP8 workload's swap-victim block moves between pinned "
+                         "host memory and the device (1 layer and a 64-layer stack); one JSON "
+                         "line per case")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) a few times: the "
                          "reference kernel for scaling HBM byte counters")
@@ -135,6 +139,75 @@ def load_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def unique_decode_bytes(wl) -> int:
+    """Bytes a decode call moves when every physical block's used slots are
+    read once however many sequences share it (the shared-prefix workload's
+    prompts): the logical count with each physical slot counted once."""
+    import workloads
+    B = wl.block_size
+    used = {}
+    for s in range(wl.num_seqs):
+        n = int(wl.context_lens[s])
+        for j in range(-(-n // B)):
+            phys = int(wl.block_tables[s, j])
+            used[phys] = max(used.get(phys, 0), min(B, n - j * B))
+    per_tok = workloads.kv_bytes_per_token(1, wl.num_kv_heads, wl.head_dim,
+                                           workloads.ELEM_BYTES[wl.pool_dtype])
+    logical_kv = int(wl.context_lens.sum()) * int(per_tok)
+    return workloads.decode_bytes(wl) - logical_kv + sum(used.values()) * int(per_tok)
+
+
+def swap_bench(reps: int = 20):
+    """Swap out / swap in of the long FP8 workload's 1,500-token victim (94
+    blocks, their device ids shuffled) between pinned host blocks and device
+    blocks ("When KV Capacity Runs Out", section "Restore KV stored outside the
+    GPU"), for one layer and for a 64-layer stack of the same geometry.
+    Bandwidth against the PCIe link the copy crosses."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+    wl = workloads.config5()
+    ex = wl.extra
+    nvb = len(ex["victim_host_blocks"])
+    host_ids = np.asarray(ex["victim_host_blocks"], np.int64)
+    dev_blocks = 2 * ex["host_pool_blocks"]
+    dev_ids = np.random.default_rng(55).permutation(dev_blocks)[:nvb].astype(np.int64)
+    for L in (1, 64):
+        host = pa.KVCache.empty(wl.pool_dtype, ex["host_pool_blocks"], L, wl.num_kv_heads,
+                                wl.block_size, wl.head_dim, pin_memory=True,
+                                k_scale=wl.k_scale, v_scale=wl.v_scale)
+        dev = pa.KVCache.empty(wl.pool_dtype, dev_blocks, L, wl.num_kv_heads, wl.block_size,
+                               wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
+        host.k.fill_(1)
+        host.v.fill_(2)
+        dev.k.fill_(3)
+        dev.v.fill_(4)
+        p_in = torch.from_numpy(np.stack([host_ids, dev_ids], 1).copy())
+        p_out = torch.from_numpy(np.stack([dev_ids, host_ids], 1).copy())
+        nbytes = nvb * 2 * dev.block_stride * workloads.ELEM_BYTES[wl.pool_dtype]
+        res = {}
+        for name, dst, src, pairs, d in (("h2d", dev, host, p_in, "h2d"),
+                                         ("d2h", host, dev, p_out, "d2h")):
+            for _ in range(3):
+                pa.copy_blocks(dst, src, pairs, d)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                pa.copy_blocks(dst, src, pairs, d)
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            ms = float(np.median(ts))
+            res[name] = {"ms": round(ms, 4), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+        print(json.dumps({"metric": "swap block moves, GB/s over PCIe", "workload": "long_fp8 victim",
+                          "blocks": nvb, "layers": L, "bytes_each_way": int(nbytes),
+                          "h2d": res["h2d"], "d2h": res["d2h"],
+                          "pcie_nominal_GBps": 64.0}), flush=True)
+        del host, dev
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle, as it is, on the host cores: its slot write builds the pool
     on the host, then its decode runs sequence by sequence (cycling through
@@ -187,6 +260,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.swap:
+        swap_bench()
         return
     dev = torch.device("cuda:0")
     t_setup = time.perf_counter()
@@ -264,6 +340,7 @@ def main():
 
     step_bytes = workloads.decode_bytes(wl) + workloads.write_bytes(wl, len(step_idx))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    uniq = unique_decode_bytes(wl)
     ab = attend_bytes(wl)
     achieved = ab / (attend_ms * 1e-3) / 1e9
     kname = attend_kernel_name(wl)
@@ -292,6 +369,8 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_per_s": round(S / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
+        "unique_decode_bytes": uniq,
+        "unique_GBps": round((uniq + step_bytes - workloads.decode_bytes(wl)) / (ms_per_step * 1e-3) / 1e9, 2),
         "decode_flushed_ms": ({"median": round(float(np.median(fl)), 5),
                                "p10": round(float(np.percentile(fl, 10)), 5),
                                "p90": round(float(np.percentile(fl, 90)), 5)} if fl else None),
