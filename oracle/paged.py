@@ -236,3 +236,44 @@ def decode(q_codes, q_dtype: str, pool_k, pool_v, geom: Geometry, pool_dtype: st
         v = gather(pool_v, geom, pool_dtype, layer, tables[s], n, v_scale)
         out[s] = attention(q[s], k, v, scale)
     return out
+
+
+def prefill(q_codes, q_dtype: str, pool_k, pool_v, geom: Geometry, pool_dtype: str,
+            layer: int, block_tables, context_lens, query_start_loc, scale: float,
+            k_scale: float = 1.0, v_scale: float = 1.0, seqs=None) -> np.ndarray:
+    """Paged prefill (and chunked prefill, and recompute): causal attention of
+    the newest positions of each sequence, float64.
+
+    Sequence s has n_s = query_start_loc[s+1] - query_start_loc[s] query rows,
+    rows query_start_loc[s] .. +n_s - 1 of q [rows][H_q][D]; row j holds
+    position p = ctx_s - n_s + j and attends to the sequence's positions
+    0 .. p. Recompute runs the prompt and every generated token again as one
+    prefill pass ("When KV Capacity Runs Out", section "Recompute KV from
+    token history"; "Continuous Batching and PagedAttention": prefill is one
+    wide parallel pass over the prompt); the keys and values of all positions
+    are in the pool (written first, as in decode), reached through the block
+    table. n_s = ctx_s is a whole prefill, n_s < ctx_s a later chunk, n_s = 1
+    a decode step. ``seqs`` restricts the work to some sequences (other rows
+    stay NaN).
+    """
+    q = codecs.decode(q_codes, q_dtype)
+    R, Hq, D = q.shape
+    out = np.full((R, Hq, D), np.nan)
+    tables = np.asarray(block_tables)
+    ctx = np.asarray(context_lens)
+    qsl = np.asarray(query_start_loc)
+    S = ctx.shape[0]
+    if qsl.shape[0] != S + 1 or qsl[0] != 0 or qsl[-1] != R or np.any(np.diff(qsl) < 0):
+        raise ValueError("query_start_loc must run from 0 to the row count, nondecreasing")
+    for s in (range(S) if seqs is None else seqs):
+        n = int(ctx[s])
+        nq = int(qsl[s + 1] - qsl[s])
+        if nq > n:
+            raise ValueError("more query rows than context positions")
+        k = gather(pool_k, geom, pool_dtype, layer, tables[s], n, k_scale)
+        v = gather(pool_v, geom, pool_dtype, layer, tables[s], n, v_scale)
+        for j in range(nq):
+            p = n - nq + j
+            out[qsl[s] + j] = attention(q[qsl[s] + j], k[:p + 1], v[:p + 1], scale)
+    return out
+
