@@ -16,6 +16,11 @@
  *                   result is identical to ordinary attention; "Continuous
  *                   Batching and PagedAttention", section "The block table is
  *                   a page table").
+ *   pa_prefill      causal attention of each sequence's newest positions over
+ *                   its paged keys and values: prefill, chunked prefill, and
+ *                   the prefill pass that recomputes a preempted request
+ *                   ("When KV Capacity Runs Out", section "Recompute KV from
+ *                   token history").
  *   pa_copy_blocks  whole-block copies: copy-on-write of a shared block inside
  *                   device memory (summary page, sampling and prefix
  *                   paragraphs) and swap between device and pinned host memory
@@ -217,6 +222,46 @@ int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs,
 /* that device current.                                                      */
 size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t max_context_len);
+
+/* ------------------------------------------------------------------------ */
+/* pa_prefill — paged prefill: causal attention of each sequence's newest    */
+/* positions (a whole prompt, a later chunk of one, or the prompt plus the   */
+/* generated tokens of a recomputed request, which "When KV Capacity Runs    */
+/* Out", section "Recompute KV from token history", runs again as one        */
+/* prefill pass).                                                            */
+/*                                                                           */
+/* Sequence s has n_s = query_start_loc[s+1] - query_start_loc[s] query rows */
+/* (rows query_start_loc[s] .. +n_s-1 of q). Row j is position               */
+/* p = context_lens[s] - n_s + j and, for query head h (KV head h / g),      */
+/*   out[row][h] = sum_{t <= p} softmax(scale * <q[row][h], K[t][kvh]>)_t    */
+/*                 * V[t][kvh]                                               */
+/* with token t read through block_tables[s][t / block_size] as in          */
+/* pa_decode. The keys and values of all positions, the new ones included,   */
+/* must already be in the pool (pa_write_kv first). n_s = context_lens[s] is */
+/* a whole prefill, n_s = 1 a decode step.                                   */
+/*                                                                           */
+/*  q, out           device [num_q_tokens][num_q_heads][head_dim], q_dtype   */
+/*                   PA_F16 or PA_BF16 (out rounded to nearest-even).        */
+/*  query_start_loc  device int32 [num_seqs + 1]: 0, nondecreasing, last =   */
+/*                   num_q_tokens.                                           */
+/*  max_query_len    host bound on the n_s; sizes the launch (rows of a      */
+/*                   sequence beyond it are not computed).                   */
+/*  context_lens, block_tables, max_context_len: as for pa_decode.           */
+/* A sequence whose context is invalid (as for pa_decode), shorter than n_s, */
+/* or whose table names a block outside the pool gets NaN rows. Rows outside */
+/* [0, num_q_tokens) are never written; a sequence whose query_start_loc     */
+/* entries leave that range is skipped. No workspace is needed.             */
+/* Supported: pools PA_F16 / PA_BF16 with the same q_dtype, or PA_FP8_E4M3   */
+/* with either; head_dim 64 or 128; num_q_heads / num_kv_heads in           */
+/* {1, 2, 4, 8, 16}. Others return PA_ERR_UNSUPPORTED.                       */
+/* ------------------------------------------------------------------------ */
+pa_status pa_prefill(const pa_kv_cache* cache, int32_t layer, const void* q,
+                     pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t max_context_len, const int32_t* query_start_loc,
+                     int32_t max_query_len, int32_t num_seqs,
+                     int32_t num_q_tokens, int32_t num_q_heads, float scale,
+                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* pa_copy_blocks — copy whole blocks (K and V, every layer, head and slot). */

@@ -240,7 +240,7 @@ def decode(q_codes, q_dtype: str, pool_k, pool_v, geom: Geometry, pool_dtype: st
 
 def prefill(q_codes, q_dtype: str, pool_k, pool_v, geom: Geometry, pool_dtype: str,
             layer: int, block_tables, context_lens, query_start_loc, scale: float,
-            k_scale: float = 1.0, v_scale: float = 1.0, seqs=None) -> np.ndarray:
+            k_scale: float = 1.0, v_scale: float = 1.0, seqs=None, rows=None) -> np.ndarray:
     """Paged prefill (and chunked prefill, and recompute): causal attention of
     the newest positions of each sequence, float64.
 
@@ -253,8 +253,8 @@ def prefill(q_codes, q_dtype: str, pool_k, pool_v, geom: Geometry, pool_dtype: s
     wide parallel pass over the prompt); the keys and values of all positions
     are in the pool (written first, as in decode), reached through the block
     table. n_s = ctx_s is a whole prefill, n_s < ctx_s a later chunk, n_s = 1
-    a decode step. ``seqs`` restricts the work to some sequences (other rows
-    stay NaN).
+    a decode step. ``seqs`` restricts the work to some sequences and ``rows``
+    to some query rows (the others stay NaN).
     """
     q = codecs.decode(q_codes, q_dtype)
     R, Hq, D = q.shape
@@ -265,14 +265,18 @@ def prefill(q_codes, q_dtype: str, pool_k, pool_v, geom: Geometry, pool_dtype: s
     S = ctx.shape[0]
     if qsl.shape[0] != S + 1 or qsl[0] != 0 or qsl[-1] != R or np.any(np.diff(qsl) < 0):
         raise ValueError("query_start_loc must run from 0 to the row count, nondecreasing")
+    want = None if rows is None else set(int(r) for r in rows)
     for s in (range(S) if seqs is None else seqs):
         n = int(ctx[s])
         nq = int(qsl[s + 1] - qsl[s])
         if nq > n:
             raise ValueError("more query rows than context positions")
+        js = [j for j in range(nq) if want is None or int(qsl[s]) + j in want]
+        if not js:
+            continue
         k = gather(pool_k, geom, pool_dtype, layer, tables[s], n, k_scale)
         v = gather(pool_v, geom, pool_dtype, layer, tables[s], n, v_scale)
-        for j in range(nq):
+        for j in js:
             p = n - nq + j
             out[qsl[s] + j] = attention(q[qsl[s] + j], k[:p + 1], v[:p + 1], scale)
     return out

@@ -215,6 +215,37 @@ def decode_merge(cache, layer, q, block_tables, context_lens, max_context_len, s
                  max_context_len, scale, out, workspace, stream)
 
 
+def prefill(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+            context_lens: torch.Tensor, max_context_len: int, query_start_loc: torch.Tensor,
+            max_query_len: int, scale: float, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    """Paged prefill: causal attention of each sequence's newest positions
+    (pa_prefill). q, out [num_q_tokens][H_q][D]; query_start_loc int32 [S+1]
+    (device): rows query_start_loc[s] .. query_start_loc[s+1]-1 are positions
+    context_lens[s] - n_s .. context_lens[s] - 1 of sequence s."""
+    _need(cache.is_device, "prefill needs a device pool")
+    _need(q.dim() == 3 and q.shape[2] == cache.head_dim, "q must be [T][H_q][head_dim]")
+    T, Hq, D = q.shape
+    _on_device(q, block_tables, context_lens, query_start_loc)
+    S = int(context_lens.shape[0]) if context_lens.dim() == 1 else -1
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1, "context_lens must be int32 [S]")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(query_start_loc.dtype == torch.int32 and tuple(query_start_loc.shape) == (S + 1,),
+          "query_start_loc must be int32 [S + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _on_device(out)
+        _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    c = cache.struct()
+    st = _lib().pa_prefill(ctypes.byref(c), layer, _ptr(q), DTYPES[dtype_name(q)], _ptr(out),
+                           _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+                           int(max_context_len), _ptr(query_start_loc), int(max_query_len), S, T,
+                           Hq, float(scale), _stream(stream))
+    B.check(st, "pa_prefill")
+    return out
+
+
 _DIRS = {"d2d": B.PA_COPY_D2D, "h2d": B.PA_COPY_H2D, "d2h": B.PA_COPY_D2H}
 
 

@@ -250,6 +250,60 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
   return PA_OK;
 }
 
+pa_status prefill_impl(const pa_kv_cache* cache, int32_t layer, const void* q, pa_dtype q_dtype,
+                       void* out, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len,
+                       const int32_t* query_start_loc, int32_t max_query_len, int32_t num_seqs,
+                       int32_t num_q_tokens, int32_t num_q_heads, float scale, hipStream_t stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_q_tokens < 0 || max_context_len < 0 || max_blocks_per_seq < 0 ||
+      max_query_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_q_heads % cache->num_kv_heads) return PA_ERR_INVALID_ARG;
+  if (!(q_dtype == PA_F32 || q_dtype == PA_F16 || q_dtype == PA_BF16)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!q || !out || !context_lens || !query_start_loc || (!block_tables && max_blocks_per_seq > 0))
+    return PA_ERR_INVALID_ARG;
+  if (cache->num_kv_heads > 65535 || num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
+  const int g = num_q_heads / cache->num_kv_heads;
+  if (!pa::prefill_supported((int)cache->dtype, (int)q_dtype, cache->head_dim, g))
+    return PA_ERR_UNSUPPORTED;
+  if (pa::prefill_tiles(g, max_query_len) > 65535) return PA_ERR_UNSUPPORTED;   // grid y limit
+  if ((int64_t)num_seqs * cache->num_kv_heads > (int64_t)4 * 0x7fffffff) return PA_ERR_UNSUPPORTED;   // grid x limit
+  if (!aligned(q, 16) || !aligned(out, 4)) return PA_ERR_UNSUPPORTED;
+  pa::PrefillParams a;
+  memset(&a, 0, sizeof(a));
+  a.k_pool = cache->k;
+  a.v_pool = cache->v;
+  a.block_stride = cache->block_stride;
+  a.layer_offset = (int64_t)layer * cache->layer_stride;
+  a.num_blocks = cache->num_blocks;
+  a.block_size = cache->block_size;
+  a.log2_block_size = ilog2(cache->block_size);
+  a.head_dim = cache->head_dim;
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  a.v_scale = fp8 ? cache->v_scale : 1.0f;
+  const double log2e = 1.4426950408889634;
+  a.qk_scale_log2 = (float)((double)scale * log2e * (fp8 ? (double)cache->k_scale : 1.0));
+  a.q = q;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.query_start_loc = query_start_loc;
+  a.num_q_tokens = num_q_tokens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  if (pa::launch_prefill(a, (int)cache->dtype, (int)q_dtype, g, max_query_len, stream) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
 bool same_shape(const pa_kv_cache* a, const pa_kv_cache* b) {
   return a->dtype == b->dtype && a->num_layers == b->num_layers &&
          a->num_kv_heads == b->num_kv_heads && a->block_size == b->block_size &&
@@ -316,6 +370,16 @@ int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs, i
   pa_dtype qd = cache->dtype == PA_FP8_E4M3 ? PA_BF16 : cache->dtype;
   if (plan_decode(cache, num_seqs, num_q_heads, qd, max_context_len, &plan) != PA_OK) return 0;
   return plan.part_tokens;
+}
+
+pa_status pa_prefill(const pa_kv_cache* cache, int32_t layer, const void* q, pa_dtype q_dtype,
+                     void* out, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len,
+                     const int32_t* query_start_loc, int32_t max_query_len, int32_t num_seqs,
+                     int32_t num_q_tokens, int32_t num_q_heads, float scale, hipStream_t stream) {
+  return prefill_impl(cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
+                      max_context_len, query_start_loc, max_query_len, num_seqs, num_q_tokens,
+                      num_q_heads, scale, stream);
 }
 
 pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q, pa_dtype q_dtype,

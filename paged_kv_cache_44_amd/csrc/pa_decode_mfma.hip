@@ -47,110 +47,14 @@
 //    while the next chunk is already in flight.
 #include "pa_device.h"
 #include "pa_internal.h"
+#include "pa_mfma.h"
 
 namespace pa {
 namespace {
 
 constexpr int NWM = 4;          // waves per workgroup
 constexpr int CH = 16;          // tokens per chunk
-constexpr float TAU = 8.0f;     // lazy rescale threshold (log2 units)
 constexpr int NXCD = 8;         // XCDs of an MI355X
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-template <int DW>
-__device__ __forceinline__ void ld(const uint32_t* __restrict__ p, uint32_t* w) {
-  if constexpr (DW == 1) {
-    w[0] = *p;
-  } else if constexpr (DW == 2) {
-    uint2 x = *reinterpret_cast<const uint2*>(p);
-    w[0] = x.x; w[1] = x.y;
-  } else {
-    static_assert(DW == 4, "load width");
-    uint4 x = *reinterpret_cast<const uint4*>(p);
-    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-  }
-}
-
-// Operand type of a matrix product: bf16 or f16 (exact for the inputs that
-// reach them: 16-bit codes as stored, E4M3 codes widened).
-enum class Op { BF16, F16 };
-
-template <Op O>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {   // RNE
-  if constexpr (O == Op::BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, half2_t));
-  }
-}
-
-template <Op O>
-__device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b) {
-  if constexpr (O == Op::BF16) {
-    a = u2f(w << 16);
-    b = u2f(w & 0xffff0000u);
-  } else {
-    half2_t h = __builtin_bit_cast(half2_t, w);
-    a = (float)h[0];
-    b = (float)h[1];
-  }
-}
-
-// 4 E4M3 codes -> two packed 16-bit pairs of operand type O (exact)
-template <Op O>
-__device__ __forceinline__ void fp8x4_to(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  if constexpr (O == Op::BF16) {
-    lo = __builtin_amdgcn_perm(f2u(a[1]), f2u(a[0]), 0x07060302u);   // upper halves
-    hi = __builtin_amdgcn_perm(f2u(b[1]), f2u(b[0]), 0x07060302u);
-  } else {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1]));
-  }
-}
-
-template <Op O>
-__device__ __forceinline__ f32x4_t mfma_k32(const uint32_t* a, const uint32_t* b, f32x4_t c) {
-  u32x4_t av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
-  if constexpr (O == Op::BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                    __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, av),
-                                                   __builtin_bit_cast(f16x8_t, bv), c, 0, 0, 0);
-}
-
-template <Op O>
-__device__ __forceinline__ f32x4_t mfma_k16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
-                                            f32x4_t c) {
-  u32x2_t av = {a0, a1}, bv = {b0, b1};
-  if constexpr (O == Op::BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, av),
-                                                      __builtin_bit_cast(bf16x4_t, bv), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, av),
-                                                  __builtin_bit_cast(f16x4_t, bv), c, 0, 0, 0);
-}
-
-template <Ty QT>
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
-  if constexpr (QT == Ty::F32) {
-    reinterpret_cast<float*>(out)[idx] = x;
-  } else if constexpr (QT == Ty::BF16) {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_bf16_rne(x);
-  } else {
-    reinterpret_cast<uint16_t*>(out)[idx] = f32_to_f16_rne(x);
-  }
-}
 
 // Chunks of a sequence: 0 when its context is empty or invalid (those rows
 // are written by the merge kernel).
@@ -180,19 +84,6 @@ inline size_t sk_lds_bytes(int num_seqs) {
 
 }  // namespace
 
-// First of the 8 dims that lane group a (= lane / 16) holds in MFMA step k
-// of the score product, for K rows of D * EB bytes: whole-line loads put
-// dims 16a + {0, 8, 64, 72} (16-bit, D = 128), 16a + {0, 8} (16-bit, D = 64)
-// and 32a + 8k (FP8, D = 128) there; otherwise the operand layout puts dims
-// 32k + 8a.
-template <int D, int EB>
-__device__ __forceinline__ int kdim_t(int k, int a) {
-  if constexpr (D * EB == 256) return 16 * a + (k & 1) * 8 + (k >> 1) * 64;
-  else if constexpr (D * EB == 128 && EB == 2) return 16 * a + 8 * k;
-  else if constexpr (D * EB == 128) return 32 * a + 8 * k;
-  else return 32 * k + 8 * a;
-}
-
 // Occupancy: FP8 pools and D = 64 fit 3 waves per SIMD without spilling;
 // 16-bit pools at D = 128 run at 2.
 template <Ty KV, int D, int G>
@@ -205,23 +96,16 @@ attend_sk_kernel(const DecodeParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
   static_assert(D == 64 || D == 128, "head_dim");
-  constexpr Op OQK = (QT == Ty::F16) ? Op::F16 : Op::BF16;          // score operands
-  constexpr Op OPV = (KV == Ty::BF16) ? Op::BF16 : Op::F16;         // P.V operands
   constexpr int EB = TyInfo<KV>::bytes;
   constexpr int KS = D / 32;              // score MFMA steps
   constexpr int VPL = D / 16;             // value elements per lane per token = P.V MFMAs
   constexpr int KDW = 8 * EB / 4;         // raw K dwords per lane per step
   constexpr int VDW = VPL * EB / 4;       // raw V dwords per lane per token
-  // K is read in whole 128-byte lines when a row has at least one: load u,
-  // lane l takes token row (l&7) + 8(u&1), 16-byte column (l>>3) + 8(u>>1);
-  // a row-rotation exchange with lane l^8 then gives lane l its MFMA row,
-  // token l%16. (Reading the operand layout directly, 64 bytes of 16 rows
-  // per load, streams markedly slower.) Otherwise lane l loads token l%16,
-  // dims 32k + 8(l/16) of step k.
-  constexpr bool KFULL = D * EB >= 128;
+  // K loads: whole 128-byte lines where rows have them (see KLayout)
+  constexpr bool KFULL = KLayout<D, EB>::FULL;
+  constexpr int KR = KLayout<D, EB>::KR;           // K loads per chunk
+  constexpr int KW = KLayout<D, EB>::KW;           // dwords per lane per K load
   auto kdim = [](int k, int a) { return kdim_t<D, EB>(k, a); };
-  constexpr int KR = KFULL ? D * EB / 64 : KS;     // K loads per chunk
-  constexpr int KW = KFULL ? 4 : KDW;              // dwords per lane per K load
 
   // [num_seqs + 1] chunk prefix sums, then [num_seqs] bytes: tokens in each
   // sequence's last chunk (1..16), so a context length is 16 (chunks - 1) + tail
@@ -441,7 +325,7 @@ attend_sk_kernel(const DecodeParams a) {
       if constexpr (KFULL) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          ek[hf] = base + (int64_t)min((lane & 7) + 8 * hf, ctx - 1 - cb) * D + (lane >> 3) * (16 / EB);
+          ek[hf] = base + (int64_t)min(k_load_row<D, EB>(hf, lane), ctx - 1 - cb) * D + k_load_col<D, EB>(0, lane);
       } else {
         ek[0] = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
       }
@@ -450,7 +334,7 @@ attend_sk_kernel(const DecodeParams a) {
     } else {
       if constexpr (KFULL) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) ek[hf] = elem_of(cb + (lane & 7) + 8 * hf) + (lane >> 3) * (16 / EB);
+        for (int hf = 0; hf < 2; ++hf) ek[hf] = elem_of(cb + k_load_row<D, EB>(hf, lane)) + k_load_col<D, EB>(0, lane);
       } else {
         ek[0] = elem_of(cb + n) + 8 * g;
       }
@@ -525,109 +409,17 @@ attend_sk_kernel(const DecodeParams a) {
     if (d.f & F_FIRST) pj0 = d.j;
     const int ctx = d.ctx;
     const int cb = d.j * CH;
-    // raw K of MFMA step k for this lane's token (l % 16)
-    uint32_t kraw[KS][KDW];
-    if constexpr (KFULL) {
-      const bool hs = (lane >> 3) & 1;                // lane l holds token l%16 half the time
-      if constexpr (EB == 2) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-#pragma unroll
-          for (int v = 0; v < KR / 2; ++v) {
-            // loads 2v, 2v+1 are token rows p and p+8 of the same columns
-            const uint32_t mine0 = kr[2 * v][x], mine1 = kr[2 * v + 1][x];
-            const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(hs ? mine0 : mine1),
-                                                                       0x128, 0xF, 0xF, false);
-            kraw[2 * v][x] = hs ? got : mine0;
-            kraw[2 * v + 1][x] = hs ? mine1 : got;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const uint32_t own = hs ? kr[1][x] : kr[0][x];
-          const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(hs ? kr[0][x] : kr[1][x]),
-                                                                     0x128, 0xF, 0xF, false);
-          const uint32_t lo = hs ? got : own, hi = hs ? own : got;
-          kraw[x >> 1][x & 1] = lo;
-          kraw[2 + (x >> 1)][x & 1] = hi;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < KS; ++k)
-#pragma unroll
-        for (int x = 0; x < KDW; ++x) kraw[k][x] = kr[k][x];
-    }
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      uint32_t ka[4];
-      if constexpr (KV == Ty::FP8) {
-        fp8x4_to<OQK>(kraw[k][0], ka[0], ka[1]);
-        fp8x4_to<OQK>(kraw[k][1], ka[2], ka[3]);
-      } else {
-        ka[0] = kraw[k][0]; ka[1] = kraw[k][1]; ka[2] = kraw[k][2]; ka[3] = kraw[k][3];
-      }
-      const uint4 q4 = s_q[wave][k][lane];
-      const uint32_t qb[4] = {q4.x, q4.y, q4.z, q4.w};
-      s = mfma_k32<OQK>(ka, qb, s);
-    }
+    const f32x4_t s = chunk_scores<KV, QT, D>(kr, [&](int k) { return s_q[wave][k][lane]; }, lane);
     const bool tail = cb + CH > ctx;
     float z[4];
+    bool live[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool valid = (n < G) && (cb + 4 * g + r < ctx);
       z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
+      live[r] = !tail || cb + 4 * g + r < ctx;
     }
-    const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    if (__any(lmax > m_ref + TAU)) {
-      float hm = fmaxf(lmax, __shfl_xor(lmax, 16));
-      hm = fmaxf(hm, __shfl_xor(hm, 32));
-      const float mn = fmaxf(m_ref, hm);
-      const float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
-      m_ref = mn;
-      l_sum *= al;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(al, 4 * g + r);      // factor of accumulator row 4g + r
-#pragma unroll
-        for (int m = 0; m < VPL; ++m) acc[m][r] *= ar;
-      }
-    }
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      p[r] = (z[r] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
-    const uint32_t pa0 = pack2<OPV>(p[0], p[1]);
-    const uint32_t pa1 = pack2<OPV>(p[2], p[3]);
-    {
-      // the normaliser sums exactly the rounded weights the matrix core uses
-      float q0, q1, q2, q3;
-      unpack2<OPV>(pa0, q0, q1);
-      unpack2<OPV>(pa1, q2, q3);
-      l_sum += (q0 + q1) + (q2 + q3);
-    }
-    // values of tokens past the context are zeroed (they may be NaN codes)
-    uint32_t vw[4][VPL / 2];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool live = !tail || cb + 4 * g + r < ctx;
-      if constexpr (KV == Ty::FP8) {
-#pragma unroll
-        for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(live ? vr[r][x] : 0u, vw[r][2 * x], vw[r][2 * x + 1]);
-      } else {
-#pragma unroll
-        for (int x = 0; x < VPL / 2; ++x) vw[r][x] = live ? vr[r][x] : 0u;
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < VPL; ++m) {
-      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t b0 = __builtin_amdgcn_perm(vw[1][m >> 1], vw[0][m >> 1], sel);
-      const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
-      acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
-    }
+    chunk_softmax_pv<KV, QT, D>(z, vr, live, acc, m_ref, l_sum, lane);
     if (d.f & F_LAST) finish_piece(d);
   };
 

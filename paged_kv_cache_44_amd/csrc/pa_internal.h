@@ -42,6 +42,30 @@ struct DecodeParams {
   int32_t* ws_team;          // matrix-core path: merge descriptors, int4 per team
 };
 
+struct PrefillParams {
+  const void* k_pool;
+  const void* v_pool;
+  int64_t block_stride;      // elements
+  int64_t layer_offset;      // elements: layer * layer_stride
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t log2_block_size;
+  int32_t head_dim;
+  float v_scale;             // applied to the output (1 unless FP8)
+  float qk_scale_log2;       // scale * log2(e) (* k_scale for FP8)
+  const void* q;             // [num_q_tokens][num_q_heads][head_dim]
+  void* out;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;
+  int32_t max_context_len;
+  const int32_t* query_start_loc;   // [num_seqs + 1]
+  int32_t num_q_tokens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+};
+
 struct WriteParams {
   void* k_pool;
   void* v_pool;
@@ -86,6 +110,10 @@ int sk_team(int num_kv_heads);
 hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
                               hipStream_t st);
 hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st);
+bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g);
+int prefill_tiles(int g, int max_query_len);
+hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
+                          hipStream_t st);
 hipError_t launch_write(const WriteParams& a, int src_ty, int dst_ty, hipStream_t st);
 hipError_t launch_copy(const CopyParams& a, hipStream_t st);
 

@@ -1,0 +1,263 @@
+// pa_prefill.hip — paged prefill (whole, chunked, or recompute) attention on
+// the gfx950 matrix cores: causal attention of each sequence's newest
+// positions over the keys and values of all its positions, reached through
+// its block table.
+//
+// A recomputed request runs its prompt and generated tokens again as one
+// prefill pass ("When KV Capacity Runs Out", section "Recompute KV from token
+// history"); the pass's keys and values are first written to the pool, then
+// every position p attends to positions 0 .. p. Query rows are packed
+// sequence by sequence (query_start_loc); the n_s rows of sequence s are its
+// positions ctx_s - n_s .. ctx_s - 1.
+//
+// One wave owns one (sequence, KV head, tile): the tile's 16 columns are 16/G
+// consecutive query positions x the G query heads of the KV head, so each
+// 16-key chunk of K and V is read once for the whole group. Per chunk the
+// score tile S[16 keys][16 columns] and P.V run on the matrix cores exactly as
+// in decode (pa_mfma.h), with the causal mask key <= position(column). A
+// three-stage pipeline keeps the block ids of chunk j+2 and the K/V of chunk
+// j+1 in flight while chunk j is processed; every step issues the same loads.
+// Tiles are launched last-first, so the longest causal ranges start first.
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+constexpr int PW = 4;           // waves per workgroup
+constexpr int PCH = 16;         // keys per chunk
+
+template <Ty KV, int D>
+constexpr int pf_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
+
+template <Ty KV, Ty QT, int D, int G>
+__global__ void __launch_bounds__(PW * 64)
+__attribute__((amdgpu_waves_per_eu(pf_waves_per_simd<KV, D>())))
+prefill_kernel(const PrefillParams a) {
+  static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
+  static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group divides the 16-column tile");
+  constexpr int EB = TyInfo<KV>::bytes;
+  using KL = KLayout<D, EB>;
+  constexpr int KS = KL::KS;
+  constexpr int KR = KL::KR;
+  constexpr int KW = KL::KW;
+  constexpr int VPL = D / 16;
+  constexpr int VDW = VPL * EB / 4;
+  constexpr int QTOK = 16 / G;              // query positions per tile
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;                  // column: position n / G, head n % G
+  const int H = a.num_kv_heads;
+  const int64_t w = (int64_t)blockIdx.x * PW + wave;
+  if (w >= (int64_t)a.num_seqs * H) return;
+  const int s = (int)(w / H);
+  const int kvh = (int)(w - (int64_t)s * H);
+  const int tile = (int)(gridDim.y - 1 - blockIdx.y);
+  const int r0 = a.query_start_loc[s];
+  const int nq = a.query_start_loc[s + 1] - r0;
+  const int t0 = tile * QTOK;
+  // rows outside the packed query array are never touched
+  if (nq <= 0 || t0 >= nq || r0 < 0 || (int64_t)r0 + nq > a.num_q_tokens) return;
+  const int rows = min(QTOK, nq - t0);      // query positions of this tile
+  const int ctx = a.context_lens[s];
+  const int lg = a.log2_block_size;
+  const bool ctx_ok = ctx >= nq && ctx <= a.max_context_len &&
+                      (((int64_t)ctx + a.block_size - 1) >> lg) <= a.max_blocks_per_seq;
+
+  // output rows of this tile: column c = 4g + r of the accumulators
+  auto store_rows = [&](const f32x4_t (&acc)[VPL], const float (&norm)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 4 * g + r;
+      if (c / G < rows) {
+        const int64_t o = (((int64_t)r0 + t0 + c / G) * a.num_q_heads + (int64_t)kvh * G + c % G) * D +
+                          VPL * n;
+#pragma unroll
+        for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm[r]);
+      }
+    }
+  };
+  f32x4_t acc[VPL];
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  if (!ctx_ok) {                            // invalid context or query count: NaN rows
+    const float nan4[4] = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    store_rows(acc, nan4);
+    return;
+  }
+
+  const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
+  const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
+  const int bmask = a.block_size - 1;
+  const bool big_blocks = a.block_size >= PCH;
+  const float qk_scale = a.qk_scale_log2;
+  const int pos0 = ctx - nq + t0;           // position of the tile's first row
+  const int p_last = pos0 + rows - 1;
+  const int nch = p_last / PCH + 1;         // key chunks the tile needs
+  const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int64_t head_off = a.layer_offset + (int64_t)kvh * a.block_size * D;
+
+  // the tile's q as the B operand: lane l holds column l%16 (rows past the
+  // tile repeat its last row; their scores are masked)
+  uint32_t qr[KS][4];
+  {
+    const int64_t row = (((int64_t)r0 + t0 + min(n / G, rows - 1)) * a.num_q_heads +
+                         (int64_t)kvh * G + n % G) * D;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim_t<D, EB>(k, g)) >> 1), qr[k]);
+  }
+
+  // block ids of chunk j (clamped to the last chunk): lane i holds the id of
+  // the chunk's i-th block, lanes past its last block repeat the last one
+  auto fetch_ids = [&](int j) __attribute__((always_inline)) -> int {
+    j = min(j, nch - 1);
+    const int cb = j * PCH;
+    const int fb = cb >> lg;
+    const int lb = (min(cb + PCH, ctx) - 1) >> lg;
+    return trow[min(fb + lane, lb)];
+  };
+  bool bad = false;                         // a bad block id was seen
+  auto load_kv = [&](int j, int idr, uint32_t (&kr)[KR][KW], uint32_t (&vr)[4][VDW])
+      __attribute__((always_inline)) {
+    j = min(j, nch - 1);
+    const int cb = j * PCH;
+    const int fb = cb >> lg;
+    const bool badl = idr < 0 || idr >= a.num_blocks;
+    bad = bad || __any(badl);
+    const int idv = badl ? 0 : idr;
+    auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {   // element of token t, dim 0
+      t = min(t, ctx - 1);
+      const int id = big_blocks ? __builtin_amdgcn_readfirstlane(idv) : __shfl(idv, (t >> lg) - fb);
+      return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
+    };
+    int64_t ek[KL::FULL ? 2 : 1], ev[4];
+    if (big_blocks) {
+      const int64_t base = elem_of(cb);
+      if constexpr (KL::FULL) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          ek[hf] = base + (int64_t)min(k_load_row<D, EB>(hf, lane), ctx - 1 - cb) * D + k_load_col<D, EB>(0, lane);
+      } else {
+        ek[0] = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
+    } else {
+      if constexpr (KL::FULL) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) ek[hf] = elem_of(cb + k_load_row<D, EB>(hf, lane)) + k_load_col<D, EB>(0, lane);
+      } else {
+        ek[0] = elem_of(cb + n) + 8 * g;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
+    }
+    if constexpr (KL::FULL) {
+#pragma unroll
+      for (int u = 0; u < KR; ++u) ld<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ld<KW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+  };
+
+  float m_ref = -__builtin_inff();          // reference max of column n (log2 units)
+  float l_sum = 0.f;
+  const bool col_ok = n / G < rows;
+  const int pcol = pos0 + n / G;            // position of column n
+  auto process = [&](int j, const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW])
+      __attribute__((always_inline)) {
+    const int cb = j * PCH;
+    const f32x4_t sc = chunk_scores<KV, QT, D>(kr, [&](int k) {
+      return make_uint4(qr[k][0], qr[k][1], qr[k][2], qr[k][3]);
+    }, lane);
+    float z[4];
+    bool live[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = cb + 4 * g + r;
+      z[r] = (col_ok && t <= pcol) ? sc[r] * qk_scale : -__builtin_inff();
+      live[r] = t < ctx;
+    }
+    chunk_softmax_pv<KV, QT, D>(z, vr, live, acc, m_ref, l_sum, lane);
+  };
+
+  uint32_t kA[KR][KW], vA[4][VDW], kB[KR][KW], vB[4][VDW];
+  int iA = fetch_ids(0);
+  int iB = fetch_ids(1);
+  load_kv(0, iA, kA, vA);
+  for (int j = 0; j < nch; j += 2) {
+    iA = fetch_ids(j + 2);
+    load_kv(j + 1, iB, kB, vB);
+    process(j, kA, vA);
+    if (j + 1 >= nch) break;
+    iB = fetch_ids(j + 3);
+    load_kv(j + 2, iA, kA, vA);
+    process(j + 1, kB, vB);
+  }
+
+  float lt = l_sum + __shfl_xor(l_sum, 16);
+  lt += __shfl_xor(lt, 32);
+  float norm[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float lh = __shfl(lt, 4 * g + r);
+    norm[r] = bad ? __builtin_nanf("") : a.v_scale / lh;
+  }
+  store_rows(acc, norm);
+}
+
+template <Ty KV, Ty QT, int D>
+hipError_t launch_g(const PrefillParams& a, int g, dim3 grid, hipStream_t st) {
+  switch (g) {
+    case 1: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 1>), grid, dim3(PW * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 2>), grid, dim3(PW * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 4>), grid, dim3(PW * 64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 8>), grid, dim3(PW * 64), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 16>), grid, dim3(PW * 64), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <Ty KV, Ty QT>
+hipError_t launch_d(const PrefillParams& a, int g, dim3 grid, hipStream_t st) {
+  if (a.head_dim == 64) return launch_g<KV, QT, 64>(a, g, grid, st);
+  if (a.head_dim == 128) return launch_g<KV, QT, 128>(a, g, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g) {
+  const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
+  const bool types = (kv == Ty::BF16 && q == Ty::BF16) || (kv == Ty::F16 && q == Ty::F16) ||
+                     (kv == Ty::FP8 && (q == Ty::BF16 || q == Ty::F16));
+  return types && (head_dim == 64 || head_dim == 128) &&
+         (g == 1 || g == 2 || g == 4 || g == 8 || g == 16);
+}
+
+int prefill_tiles(int g, int max_query_len) {
+  const int qtok = 16 / g;
+  return (max_query_len + qtok - 1) / qtok;
+}
+
+hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
+                          hipStream_t st) {
+  const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
+  const dim3 grid((unsigned)((waves + PW - 1) / PW), (unsigned)prefill_tiles(g, max_query_len));
+  const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
+  if (kv == Ty::BF16 && q == Ty::BF16) return launch_d<Ty::BF16, Ty::BF16>(a, g, grid, st);
+  if (kv == Ty::F16 && q == Ty::F16) return launch_d<Ty::F16, Ty::F16>(a, g, grid, st);
+  if (kv == Ty::FP8 && q == Ty::BF16) return launch_d<Ty::FP8, Ty::BF16>(a, g, grid, st);
+  if (kv == Ty::FP8 && q == Ty::F16) return launch_d<Ty::FP8, Ty::F16>(a, g, grid, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -459,3 +459,15 @@ def write_bytes(wl: Workload, num_tokens: int) -> int:
 def copy_bytes(wl: Workload, num_pairs: int) -> int:
     """Bytes a block copy of num_pairs blocks moves (read + write)."""
     return 2 * num_pairs * 2 * wl.block_stride() * ELEM_BYTES[wl.pool_dtype]
+
+
+def prefill_queries(wl: Workload, query_lens, seed: int):
+    """Packed query rows for a prefill over the workload's pool: query_lens[s]
+    rows for sequence s (its newest positions), N(0, 1) rounded to the query
+    dtype. Returns (q codes [rows][H_q][D], query_start_loc int32 [S + 1])."""
+    rng = np.random.default_rng(seed)
+    ql = np.asarray(query_lens, dtype=np.int64)
+    qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    q = normal_codes(rng, (int(qsl[-1]), wl.num_q_heads, wl.head_dim), wl.q_dtype)
+    return q, qsl
+
