@@ -70,6 +70,10 @@ def parse():
                     help="time the long FP8 workload's swap-victim block moves between pinned "
                          "host memory and the device (1 layer and a 64-layer stack); one JSON "
                          "line per case")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time paged prefill: the GQA bf16 workload's contexts prefilled whole, "
+                         "and the long FP8 workload's 1,500-token victim recomputed; one JSON "
+                         "line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) a few times: the "
                          "reference kernel for scaling HBM byte counters")
@@ -208,6 +212,87 @@ def swap_bench(reps: int = 20):
         del host, dev
 
 
+MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 / f16 matrix-core peak
+
+
+def prefill_flops(context_lens, query_lens, num_q_heads: int, head_dim: int) -> int:
+    """Algorithmic FLOPs of a causal prefill: each query row at position p
+    takes p + 1 scores and p + 1 weighted values per head, 2 FLOPs per
+    multiply-add over head_dim."""
+    tot = 0
+    for n, nq in zip(context_lens, query_lens):
+        n, nq = int(n), int(nq)
+        # positions n - nq .. n - 1 attend to p + 1 keys each
+        tot += nq * (n - nq) + nq * (nq + 1) // 2
+    return 4 * num_q_heads * head_dim * tot
+
+
+def prefill_bench(steps: int, warmup: int):
+    """Paged prefill timed with HIP events (median over steps): TFLOP/s
+    against the matrix-core peak, and the key/value bytes it reads."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+    dev = torch.device("cuda:0")
+    cases = [("prefill_gqa_bf16", workloads.make(3), None),
+             ("recompute_fp8_1500", workloads.custom(505, [1500], pool_dtype="fp8_e4m3",
+                                                     q_dtype="bf16", num_q_heads=64, num_kv_heads=8,
+                                                     head_dim=128, block_size=16), None)]
+    for name, wl, _ in cases:
+        pool = wl.empty_pool()
+        cache = pa.KVCache(codes_tensor(pool, wl.pool_dtype, dev), codes_tensor(pool, wl.pool_dtype, dev),
+                           wl.pool_dtype, wl.num_blocks, wl.num_layers, wl.num_kv_heads,
+                           wl.block_size, wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
+        for op in workloads.fill_plan(wl):
+            if op[0] == "write":
+                pa.write_kv(cache, wl.layer, codes_tensor(op[1], wl.src_dtype, dev),
+                            codes_tensor(op[2], wl.src_dtype, dev), torch.from_numpy(op[3]).to(dev))
+            else:
+                pa.copy_blocks(cache, cache, torch.from_numpy(op[1]).to(dev), "d2d")
+        ql = wl.context_lens.copy()                       # whole prefills: every position
+        qc, qsl = workloads.prefill_queries(wl, ql, 77)
+        q = codes_tensor(qc, wl.q_dtype, dev)
+        out = torch.empty_like(q)
+        tables = torch.from_numpy(wl.block_tables).to(dev)
+        ctx = torch.from_numpy(wl.context_lens).to(dev)
+        qs = torch.from_numpy(qsl).to(dev)
+        mq = int(ql.max())
+        call = lambda: pa.prefill(cache, wl.layer, q, tables, ctx, wl.max_context_len, qs, mq,
+                                  wl.scale, out=out)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ms = float(np.median(ts))
+        fl = prefill_flops(wl.context_lens, ql, wl.num_q_heads, wl.head_dim)
+        kv = workloads.decode_bytes(wl) - wl.num_seqs * wl.num_q_heads * wl.head_dim * 2 * \
+            workloads.ELEM_BYTES[wl.q_dtype]
+        qo = int(qsl[-1]) * wl.num_q_heads * wl.head_dim * 2 * workloads.ELEM_BYTES[wl.q_dtype]
+        tf = fl / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "paged prefill TFLOP/s", "workload": name, "value": round(tf, 2),
+            "unit": "TFLOP/s", "ms": round(ms, 4), "p10_ms": round(float(np.percentile(ts, 10)), 4),
+            "p90_ms": round(float(np.percentile(ts, 90)), 4),
+            "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8-e4m3 KV, bf16 q"}[wl.pool_dtype],
+            "config": {"num_seqs": wl.num_seqs, "num_q_heads": wl.num_q_heads,
+                       "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                       "block_size": wl.block_size, "query_rows": int(qsl[-1]),
+                       "context_max": int(wl.max_context_len)},
+            "flops": fl, "bytes": int(kv + qo),
+            "GBps": round((kv + qo) / (ms * 1e-3) / 1e9, 1),
+            "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 2),
+                         "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)}}), flush=True)
+        del cache, q, out
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle, as it is, on the host cores: its slot write builds the pool
     on the host, then its decode runs sequence by sequence (cycling through
@@ -263,6 +348,9 @@ def main():
         return
     if args.swap:
         swap_bench()
+        return
+    if args.prefill:
+        prefill_bench(args.steps if args.steps != 50 else 20, args.warmup if args.warmup != 10 else 3)
         return
     dev = torch.device("cuda:0")
     t_setup = time.perf_counter()

@@ -204,19 +204,16 @@ struct ChunkOps {
 };
 
 // Score tile of a 16-token chunk against 16 columns: S[16 tokens][16 cols] =
-// K[16][D] . X^T[D][16] (D/32 steps of v_mfma_f32_16x16x32). kr are the
-// lane's K loads (KLayout); xb(k) gives the lane's B operand of step k (its
-// column's dims kdim_t(k, lane / 16) .. +8) as 16 bytes. Lane l gets tokens
-// 4(l/16) .. +3 of column l%16.
+// K[16][D] . X^T[D][16] (D/32 steps of v_mfma_f32_16x16x32). kraw is the
+// lane's raw K operand (k_operand); xb(k) gives the lane's B operand of step
+// k (its column's dims kdim_t(k, lane / 16) .. +8) as 16 bytes. Lane l gets
+// tokens 4(l/16) .. +3 of column l%16.
 template <Ty KV, Ty QT, int D, class XB>
-__device__ __forceinline__ f32x4_t chunk_scores(
-    const uint32_t (&kr)[KLayout<D, TyInfo<KV>::bytes>::KR][KLayout<D, TyInfo<KV>::bytes>::KW],
-    XB xb, int lane) {
-  constexpr int EB = TyInfo<KV>::bytes;
-  using L = KLayout<D, EB>;
+__device__ __forceinline__ f32x4_t chunk_scores_raw(
+    const uint32_t (&kraw)[KLayout<D, TyInfo<KV>::bytes>::KS][KLayout<D, TyInfo<KV>::bytes>::KDW],
+    XB xb) {
+  using L = KLayout<D, TyInfo<KV>::bytes>;
   constexpr Op OQK = ChunkOps<KV, QT>::QK;
-  uint32_t kraw[L::KS][L::KDW];
-  k_operand<D, EB>(kr, kraw, lane);
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < L::KS; ++k) {
@@ -234,22 +231,53 @@ __device__ __forceinline__ f32x4_t chunk_scores(
   return s;
 }
 
-// One chunk of online softmax and P.V for the lane's column (l % 16):
-// z[r] = scaled score of token 4(l/16)+r (log2 units; -inf where masked),
-// vr the lane's value loads (slice [VPL*(l%16), +VPL) of tokens 4(l/16)+r),
-// live[r] false for value rows that must read as zero (past the context:
-// they may hold NaN codes). The score tile is exactly the A-operand layout
-// of P[16 cols][16 tokens] . V[16 tokens][D] (v_mfma_f32_16x16x16), so the
-// probabilities never leave their lane; acc[m] holds output rows 4(l/16)+r
-// (columns), dim VPL*(l%16) + m. The row sum adds exactly the rounded
-// 16-bit weights the matrix core multiplies.
+// The same from the lane's K loads (rebuilds the operand first).
+template <Ty KV, Ty QT, int D, class XB>
+__device__ __forceinline__ f32x4_t chunk_scores(
+    const uint32_t (&kr)[KLayout<D, TyInfo<KV>::bytes>::KR][KLayout<D, TyInfo<KV>::bytes>::KW],
+    XB xb, int lane) {
+  constexpr int EB = TyInfo<KV>::bytes;
+  using L = KLayout<D, EB>;
+  uint32_t kraw[L::KS][L::KDW];
+  k_operand<D, EB>(kr, kraw, lane);
+  return chunk_scores_raw<KV, QT, D>(kraw, xb);
+}
+
+// Value operands of a chunk for P.V: the lane's value loads (slice
+// [VPL*(l%16), +VPL) of tokens 4(l/16)+r) as packed 16-bit pairs, element m
+// of the four token vectors gathered with byte permutes later; live[r] false
+// for value rows that must read as zero (past the context: they may hold NaN
+// codes). FP8 codes are widened exactly to f16.
 template <Ty KV, Ty QT, int D>
-__device__ __forceinline__ void chunk_softmax_pv(const float (&z)[4],
-                                                 const uint32_t (&vr)[4][D / 16 * TyInfo<KV>::bytes / 4],
-                                                 const bool (&live)[4], f32x4_t (&acc)[D / 16],
-                                                 float& m_ref, float& l_sum, int lane) {
+__device__ __forceinline__ void v_operand(const uint32_t (&vr)[4][D / 16 * TyInfo<KV>::bytes / 4],
+                                          const bool (&live)[4], uint32_t (&vw)[4][D / 32]) {
   constexpr int VPL = D / 16;
   constexpr int VDW = VPL * TyInfo<KV>::bytes / 4;
+  constexpr Op OPV = ChunkOps<KV, QT>::PV;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (KV == Ty::FP8) {
+#pragma unroll
+      for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(live[r] ? vr[r][x] : 0u, vw[r][2 * x], vw[r][2 * x + 1]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < VPL / 2; ++x) vw[r][x] = live[r] ? vr[r][x] : 0u;
+    }
+  }
+}
+
+// One chunk of online softmax and P.V for the lane's column (l % 16):
+// z[r] = scaled score of token 4(l/16)+r (log2 units; -inf where masked), vw
+// the chunk's value operands (v_operand). The score tile is exactly the
+// A-operand layout of P[16 cols][16 tokens] . V[16 tokens][D]
+// (v_mfma_f32_16x16x16), so the probabilities never leave their lane; acc[m]
+// holds output rows 4(l/16)+r (columns), dim VPL*(l%16) + m. The row sum adds
+// exactly the rounded 16-bit weights the matrix core multiplies.
+template <Ty KV, Ty QT, int D>
+__device__ __forceinline__ void softmax_pv(const float (&z)[4], const uint32_t (&vw)[4][D / 32],
+                                           f32x4_t (&acc)[D / 16], float& m_ref, float& l_sum,
+                                           int lane) {
+  constexpr int VPL = D / 16;
   constexpr Op OPV = ChunkOps<KV, QT>::PV;
   const int g = lane >> 4;
   const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -279,17 +307,6 @@ __device__ __forceinline__ void chunk_softmax_pv(const float (&z)[4],
     unpack2<OPV>(pa1, q2, q3);
     l_sum += (q0 + q1) + (q2 + q3);
   }
-  uint32_t vw[4][VPL / 2];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if constexpr (KV == Ty::FP8) {
-#pragma unroll
-      for (int x = 0; x < VDW; ++x) fp8x4_to<OPV>(live[r] ? vr[r][x] : 0u, vw[r][2 * x], vw[r][2 * x + 1]);
-    } else {
-#pragma unroll
-      for (int x = 0; x < VPL / 2; ++x) vw[r][x] = live[r] ? vr[r][x] : 0u;
-    }
-  }
 #pragma unroll
   for (int m = 0; m < VPL; ++m) {
     const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
@@ -297,6 +314,17 @@ __device__ __forceinline__ void chunk_softmax_pv(const float (&z)[4],
     const uint32_t b1 = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
     acc[m] = mfma_k16<OPV>(pa0, pa1, b0, b1, acc[m]);
   }
+}
+
+// v_operand followed by softmax_pv (one column tile per chunk).
+template <Ty KV, Ty QT, int D>
+__device__ __forceinline__ void chunk_softmax_pv(const float (&z)[4],
+                                                 const uint32_t (&vr)[4][D / 16 * TyInfo<KV>::bytes / 4],
+                                                 const bool (&live)[4], f32x4_t (&acc)[D / 16],
+                                                 float& m_ref, float& l_sum, int lane) {
+  uint32_t vw[4][D / 32];
+  v_operand<KV, QT, D>(vr, live, vw);
+  softmax_pv<KV, QT, D>(z, vw, acc, m_ref, l_sum, lane);
 }
 
 }  // namespace pa

@@ -10,14 +10,17 @@
 // sequence by sequence (query_start_loc); the n_s rows of sequence s are its
 // positions ctx_s - n_s .. ctx_s - 1.
 //
-// One wave owns one (sequence, KV head, tile): the tile's 16 columns are 16/G
-// consecutive query positions x the G query heads of the KV head, so each
-// 16-key chunk of K and V is read once for the whole group. Per chunk the
-// score tile S[16 keys][16 columns] and P.V run on the matrix cores exactly as
-// in decode (pa_mfma.h), with the causal mask key <= position(column). A
-// three-stage pipeline keeps the block ids of chunk j+2 and the K/V of chunk
-// j+1 in flight while chunk j is processed; every step issues the same loads.
-// Tiles are launched last-first, so the longest causal ranges start first.
+// A column tile is 16/G consecutive query positions x the G query heads of a
+// KV head; one wave owns 2 consecutive tiles of one (sequence, KV head), so
+// each 16-key chunk of K and V it loads serves 32 columns, and the 4 waves of
+// a workgroup own consecutive tiles of the same (sequence, KV head), so they
+// stream the same key chunks at about the same time and share them in the
+// caches. Per chunk the score tiles S[16 keys][16 columns] and P.V run on the
+// matrix cores as in decode (pa_mfma.h), with the causal mask key <=
+// position(column). A three-stage pipeline keeps the block ids of chunk j+2
+// and the K/V of chunk j+1 in flight while chunk j is processed; every step
+// issues the same loads. Workgroups launch last-first, so the longest causal
+// ranges start first.
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
@@ -29,7 +32,10 @@ constexpr int PW = 4;           // waves per workgroup
 constexpr int PCH = 16;         // keys per chunk
 
 template <Ty KV, int D>
-constexpr int pf_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
+constexpr int pf_waves_per_simd() { return D == 64 ? 3 : 2; }
+
+// Column tiles per wave: each loaded key chunk serves NT x 16 columns.
+constexpr int PNT = 2;
 
 template <Ty KV, Ty QT, int D, int G>
 __global__ void __launch_bounds__(PW * 64)
@@ -44,48 +50,53 @@ prefill_kernel(const PrefillParams a) {
   constexpr int KW = KL::KW;
   constexpr int VPL = D / 16;
   constexpr int VDW = VPL * EB / 4;
-  constexpr int QTOK = 16 / G;              // query positions per tile
+  constexpr int NT = PNT;
+  constexpr int QTOK = 16 / G;              // query positions per column tile
+  constexpr int WTOK = NT * QTOK;           // query positions per wave
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int n = lane & 15;                  // column: position n / G, head n % G
   const int H = a.num_kv_heads;
-  const int64_t w = (int64_t)blockIdx.x * PW + wave;
-  if (w >= (int64_t)a.num_seqs * H) return;
-  const int s = (int)(w / H);
-  const int kvh = (int)(w - (int64_t)s * H);
-  const int tile = (int)(gridDim.y - 1 - blockIdx.y);
+  const int s = (int)(blockIdx.x / H);
+  const int kvh = (int)(blockIdx.x - (unsigned)s * H);
+  // the workgroup's waves take consecutive position groups of one (sequence,
+  // KV head): they stream the same key chunks at about the same time
+  const int t0 = ((int)(gridDim.y - 1 - blockIdx.y) * PW + wave) * WTOK;
   const int r0 = a.query_start_loc[s];
   const int nq = a.query_start_loc[s + 1] - r0;
-  const int t0 = tile * QTOK;
   // rows outside the packed query array are never touched
   if (nq <= 0 || t0 >= nq || r0 < 0 || (int64_t)r0 + nq > a.num_q_tokens) return;
-  const int rows = min(QTOK, nq - t0);      // query positions of this tile
+  const int rows = min(WTOK, nq - t0);      // query positions of this wave
   const int ctx = a.context_lens[s];
   const int lg = a.log2_block_size;
   const bool ctx_ok = ctx >= nq && ctx <= a.max_context_len &&
                       (((int64_t)ctx + a.block_size - 1) >> lg) <= a.max_blocks_per_seq;
 
-  // output rows of this tile: column c = 4g + r of the accumulators
-  auto store_rows = [&](const f32x4_t (&acc)[VPL], const float (&norm)[4]) __attribute__((always_inline)) {
+  f32x4_t acc[NT][VPL];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) acc[t][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  // output rows of tile t: column c = 4g + r of its accumulators
+  auto store_rows = [&](int t, const float (&norm)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = 4 * g + r;
-      if (c / G < rows) {
-        const int64_t o = (((int64_t)r0 + t0 + c / G) * a.num_q_heads + (int64_t)kvh * G + c % G) * D +
+      const int tok = t * QTOK + c / G;
+      if (tok < rows) {
+        const int64_t o = (((int64_t)r0 + t0 + tok) * a.num_q_heads + (int64_t)kvh * G + c % G) * D +
                           VPL * n;
 #pragma unroll
-        for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm[r]);
+        for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[t][m][r] * norm[r]);
       }
     }
   };
-  f32x4_t acc[VPL];
-#pragma unroll
-  for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   if (!ctx_ok) {                            // invalid context or query count: NaN rows
     const float nan4[4] = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    store_rows(acc, nan4);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) store_rows(t, nan4);
     return;
   }
 
@@ -95,20 +106,21 @@ prefill_kernel(const PrefillParams a) {
   const int bmask = a.block_size - 1;
   const bool big_blocks = a.block_size >= PCH;
   const float qk_scale = a.qk_scale_log2;
-  const int pos0 = ctx - nq + t0;           // position of the tile's first row
+  const int pos0 = ctx - nq + t0;           // position of the wave's first row
   const int p_last = pos0 + rows - 1;
-  const int nch = p_last / PCH + 1;         // key chunks the tile needs
+  const int nch = p_last / PCH + 1;         // key chunks the wave needs
   const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int64_t head_off = a.layer_offset + (int64_t)kvh * a.block_size * D;
 
-  // the tile's q as the B operand: lane l holds column l%16 (rows past the
-  // tile repeat its last row; their scores are masked)
-  uint32_t qr[KS][4];
-  {
-    const int64_t row = (((int64_t)r0 + t0 + min(n / G, rows - 1)) * a.num_q_heads +
+  // q of each tile as the B operand: lane l holds column l%16 (rows past the
+  // wave's last repeat it; their scores are masked)
+  uint32_t qr[NT][KS][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int64_t row = (((int64_t)r0 + t0 + min(t * QTOK + n / G, rows - 1)) * a.num_q_heads +
                          (int64_t)kvh * G + n % G) * D;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim_t<D, EB>(k, g)) >> 1), qr[k]);
+    for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim_t<D, EB>(k, g)) >> 1), qr[t][k]);
   }
 
   // block ids of chunk j (clamped to the last chunk): lane i holds the id of
@@ -167,25 +179,38 @@ prefill_kernel(const PrefillParams a) {
     for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
   };
 
-  float m_ref = -__builtin_inff();          // reference max of column n (log2 units)
-  float l_sum = 0.f;
-  const bool col_ok = n / G < rows;
-  const int pcol = pos0 + n / G;            // position of column n
+  float m_ref[NT], l_sum[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m_ref[t] = -__builtin_inff();           // reference max of the column (log2 units)
+    l_sum[t] = 0.f;
+  }
   auto process = [&](int j, const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW])
       __attribute__((always_inline)) {
     const int cb = j * PCH;
-    const f32x4_t sc = chunk_scores<KV, QT, D>(kr, [&](int k) {
-      return make_uint4(qr[k][0], qr[k][1], qr[k][2], qr[k][3]);
-    }, lane);
-    float z[4];
+    uint32_t kraw[KS][KL::KDW];
+    k_operand<D, EB>(kr, kraw, lane);
     bool live[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = cb + 4 * g + r;
-      z[r] = (col_ok && t <= pcol) ? sc[r] * qk_scale : -__builtin_inff();
-      live[r] = t < ctx;
+    for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
+    uint32_t vw[4][D / 32];
+    v_operand<KV, QT, D>(vr, live, vw);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int tok = t * QTOK + n / G;
+      const int pcol = pos0 + tok;          // position of this column
+      if (t * QTOK >= rows) break;          // tile past the wave's rows (uniform)
+      const f32x4_t sc = chunk_scores_raw<KV, QT, D>(kraw, [&](int k) {
+        return make_uint4(qr[t][k][0], qr[t][k][1], qr[t][k][2], qr[t][k][3]);
+      });
+      float z[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tk = cb + 4 * g + r;
+        z[r] = (tok < rows && tk <= pcol) ? sc[r] * qk_scale : -__builtin_inff();
+      }
+      softmax_pv<KV, QT, D>(z, vw, acc[t], m_ref[t], l_sum[t], lane);
     }
-    chunk_softmax_pv<KV, QT, D>(z, vr, live, acc, m_ref, l_sum, lane);
   };
 
   uint32_t kA[KR][KW], vA[4][VDW], kB[KR][KW], vB[4][VDW];
@@ -202,15 +227,18 @@ prefill_kernel(const PrefillParams a) {
     process(j + 1, kB, vB);
   }
 
-  float lt = l_sum + __shfl_xor(l_sum, 16);
-  lt += __shfl_xor(lt, 32);
-  float norm[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float lh = __shfl(lt, 4 * g + r);
-    norm[r] = bad ? __builtin_nanf("") : a.v_scale / lh;
+  for (int t = 0; t < NT; ++t) {
+    float lt = l_sum[t] + __shfl_xor(l_sum[t], 16);
+    lt += __shfl_xor(lt, 32);
+    float norm[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lh = __shfl(lt, 4 * g + r);
+      norm[r] = bad ? __builtin_nanf("") : a.v_scale / lh;
+    }
+    store_rows(t, norm);
   }
-  store_rows(acc, norm);
 }
 
 template <Ty KV, Ty QT, int D>
@@ -243,15 +271,15 @@ bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g) {
          (g == 1 || g == 2 || g == 4 || g == 8 || g == 16);
 }
 
+// Workgroups along the query rows: each covers PW * PNT * (16 / g) positions.
 int prefill_tiles(int g, int max_query_len) {
-  const int qtok = 16 / g;
-  return (max_query_len + qtok - 1) / qtok;
+  const int per = PW * PNT * (16 / g);
+  return (max_query_len + per - 1) / per;
 }
 
 hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
                           hipStream_t st) {
-  const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
-  const dim3 grid((unsigned)((waves + PW - 1) / PW), (unsigned)prefill_tiles(g, max_query_len));
+  const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads), (unsigned)prefill_tiles(g, max_query_len));
   const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
   if (kv == Ty::BF16 && q == Ty::BF16) return launch_d<Ty::BF16, Ty::BF16>(a, g, grid, st);
   if (kv == Ty::F16 && q == Ty::F16) return launch_d<Ty::F16, Ty::F16>(a, g, grid, st);
