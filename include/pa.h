@@ -82,7 +82,9 @@ typedef enum {
   PA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad dtype combination   */
   PA_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. head_dim)  */
   PA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required  */
-  PA_ERR_HIP = 4          /* a HIP launch or copy call failed                 */
+  PA_ERR_HIP = 4,         /* a HIP launch or copy call failed                 */
+  PA_ERR_NO_SPACE = 5     /* block manager: not enough free blocks (nothing    */
+                          /* was changed)                                      */
 } pa_status;
 
 typedef enum {

@@ -6,14 +6,19 @@ import os
 
 from .build import LIB_PATH
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_SPACE = range(6)
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = range(4)
 PA_COPY_D2D, PA_COPY_H2D, PA_COPY_D2H = range(3)
 
 #: every function the header declares
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_attend", "pa_decode_merge",
             "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_prefill",
-            "pa_copy_blocks", "pa_status_string", "pa_version")
+            "pa_copy_blocks", "pa_status_string", "pa_version",
+            # pa_blocks.h
+            "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_add", "pa_bm_fork",
+            "pa_bm_append", "pa_bm_blocks_needed", "pa_bm_copy_last_block", "pa_bm_release",
+            "pa_bm_table", "pa_bm_newest_running", "pa_bm_swap_out", "pa_bm_swap_out_done",
+            "pa_bm_swap_in")
 
 
 class PaKvCache(ctypes.Structure):
@@ -57,6 +62,28 @@ def load_library(path: str = LIB_PATH):
     lib.pa_prefill.argtypes = [P, i32, vp, ctypes.c_int, vp, vp, i32, vp, i32, vp, i32, i32, i32,
                                i32, f32, vp]
     lib.pa_prefill.restype = ctypes.c_int
+    # host block manager (pa_blocks.h)
+    vpp = ctypes.POINTER(ctypes.c_void_p)
+    pi32, pi64 = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    sig = {
+        "pa_bm_create": ([i32, i32, vp, i32, vpp], ctypes.c_int),
+        "pa_bm_destroy": ([vp], None),
+        "pa_bm_num_free": ([vp, i32], i32),
+        "pa_bm_add": ([vp, i64], ctypes.c_int),
+        "pa_bm_fork": ([vp, i64, i64], ctypes.c_int),
+        "pa_bm_append": ([vp, i64, i32, vp, vp, pi32], ctypes.c_int),
+        "pa_bm_blocks_needed": ([vp, i64, i32], i32),
+        "pa_bm_copy_last_block": ([vp, i64, vp], ctypes.c_int),
+        "pa_bm_release": ([vp, i64], ctypes.c_int),
+        "pa_bm_table": ([vp, i64, vp, i32, pi32, pi32], ctypes.c_int),
+        "pa_bm_newest_running": ([vp, pi64], ctypes.c_int),
+        "pa_bm_swap_out": ([vp, i64, vp, i32, pi32], ctypes.c_int),
+        "pa_bm_swap_out_done": ([vp, i64], ctypes.c_int),
+        "pa_bm_swap_in": ([vp, i64, vp, i32, pi32], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = res
     lib.pa_decode_partition_tokens.argtypes = [P, i32, i32, i32]
     lib.pa_decode_partition_tokens.restype = i32
     lib.pa_decode_workspace_size.argtypes = [P, i32, i32, i32]

@@ -505,6 +505,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported size, dtype or alignment";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch or copy failed";
+    case PA_ERR_NO_SPACE: return "PA_ERR_NO_SPACE: not enough free blocks";
   }
   return "unknown pa_status";
 }
