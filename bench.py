@@ -70,6 +70,10 @@ def parse():
                     help="time the long FP8 workload's swap-victim block moves between pinned "
                          "host memory and the device (1 layer and a 64-layer stack); one JSON "
                          "line per case")
+    ap.add_argument("--swap-sweep", action="store_true",
+                    help="swap moves of a 1,500-token FP8 victim for block sizes 8..128, one "
+                         "layer and 64 layers, block-major and layer-major pools; then the "
+                         "swap pipeline (copy stream beside decode); one JSON line per case")
     ap.add_argument("--prefill", action="store_true",
                     help="time paged prefill: the GQA bf16 workload's contexts prefilled whole, "
                          "and the long FP8 workload's 1,500-token victim recomputed; one JSON "
@@ -212,6 +216,193 @@ def swap_bench(reps: int = 20):
         del host, dev
 
 
+def _time_ms(fn, reps: int, stream=None) -> float:
+    """Median milliseconds of fn() between two events on ``stream``."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def _swap_pools(dtype, nvb, ndev, L, H, B, D, layout):
+    """A pinned host pool of nvb packed blocks and a device pool of ndev
+    blocks: block-major (a block's layers back to back) or layer-major (one
+    packed array of blocks per layer)."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    host = pa.KVCache.empty(dtype, nvb, L, H, B, D, pin_memory=True)
+    slab = H * B * D
+    if layout == "block_major":
+        dev = pa.KVCache.empty(dtype, ndev, L, H, B, D)
+    else:
+        td = pa.TORCH_DTYPE[dtype]
+        dev = pa.KVCache(torch.empty(ndev * L * slab, dtype=td, device="cuda"),
+                         torch.empty(ndev * L * slab, dtype=td, device="cuda"), dtype, ndev, L, H,
+                         B, D, block_stride=slab, layer_stride=ndev * slab)
+    for t, c in ((host.k, 1), (host.v, 2), (dev.k, 3), (dev.v, 4)):
+        t.view(torch.uint8).fill_(c)
+    return host, dev
+
+
+def swap_sweep(reps: int = 8):
+    """Block-size sweep of swap moves ("41 · Preemption, Recomputation & KV
+    Pressure", section 3; "Efficient Memory Management for Large Language
+    Model Serving with PagedAttention", block-size paragraph): the long FP8
+    workload's 1,500-token victim (8 KV heads, head dim 128) for B = 8 .. 128,
+    one layer and a 64-layer stack, the device blocks scattered at random and
+    the host blocks packed. Block-major pools move a whole block (every layer)
+    per DMA transfer; layer-major pools, one layer of one block. Each move is
+    timed by the DMA engines, by the copy kernel (one launch for every block
+    and layer) and staged (a gather / scatter kernel beside a few large DMA
+    transfers). One JSON line per case."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+    wl = workloads.config5()
+    H, D, dt = wl.num_kv_heads, wl.head_dim, wl.pool_dtype
+    eb = workloads.ELEM_BYTES[dt]
+    tokens = 1500
+    rng = np.random.default_rng(77)
+    for L in (1, 64):
+        for B in (8, 16, 32, 64, 128):
+            nvb = -(-tokens // B)
+            ndev = 4 * nvb
+            for layout in (("block_major",) if L == 1 else ("block_major", "layer_major")):
+                host, dev = _swap_pools(dt, nvb, ndev, L, H, B, D, layout)
+                dev_ids = rng.permutation(ndev)[:nvb].astype(np.int64)
+                host_ids = np.arange(nvb, dtype=np.int64)
+                p_in = torch.from_numpy(np.stack([host_ids, dev_ids], 1).copy())
+                p_out = torch.from_numpy(np.stack([dev_ids, host_ids], 1).copy())
+                nbytes = nvb * 2 * L * H * B * D * eb
+                transfers = 2 * nvb * (1 if layout == "block_major" else L)
+                staging = torch.empty(pa.copy_staging_size(dev, nvb), dtype=torch.uint8,
+                                      device="cuda")
+                res = {}
+                for name, dst, src, pairs in (("d2h", host, dev, p_out), ("h2d", dev, host, p_in)):
+                    res[name] = {}
+                    for method in ("dma", "kernel", "staged"):
+                        def move():
+                            if method == "staged":
+                                pa.copy_blocks_staged(dst, src, pairs, name, staging)
+                            else:
+                                pa.copy_blocks(dst, src, pairs,
+                                               name + ("_kernel" if method == "kernel" else ""))
+                        for _ in range(2):
+                            move()
+                        torch.cuda.synchronize()
+                        ms = _time_ms(move, reps)
+                        res[name][method] = {"ms": round(ms, 4),
+                                             "GBps": round(nbytes / (ms * 1e-3) / 1e9, 2)}
+                print(json.dumps({"metric": "swap block moves, GB/s over PCIe",
+                                  "workload": "1,500-token FP8 victim", "layers": L,
+                                  "block_size": B, "blocks": nvb, "layout": layout,
+                                  "bytes_each_way": int(nbytes),
+                                  "host_pool_mapped": pa.host_pool_mapped(host),
+                                  "dma_transfers": transfers,
+                                  "bytes_per_dma_transfer": int(nbytes // transfers),
+                                  "d2h": res["d2h"], "h2d": res["h2d"]}),
+                      flush=True)
+                del host, dev, staging
+                torch.cuda.empty_cache()
+
+
+def swap_overlap(steps: int = 40):
+    """The swap pipeline: the 64-layer victim's blocks move out and back on a
+    copy stream while decode steps of the long FP8 workload run on the
+    compute stream; the copy stream waits on an event the compute stream
+    records after the victim's last use, and the compute stream waits on the
+    swap-in's completion event before the next step that reads the victim
+    ("When KV Capacity Runs Out", section "Restore KV stored outside the
+    GPU": blocks must not be reused before their copy has finished). Reports
+    each side alone and both together, for the DMA engines, the copy kernel
+    and the staged copy (gather kernel + large DMA transfers)."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+    wl = workloads.config5()
+    dev = torch.device("cuda:0")
+    pool = wl.empty_pool()
+    cache = pa.KVCache(codes_tensor(pool, wl.pool_dtype, dev), codes_tensor(pool, wl.pool_dtype, dev),
+                       wl.pool_dtype, wl.num_blocks, wl.num_layers, wl.num_kv_heads,
+                       wl.block_size, wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    for op in workloads.fill_plan(wl):
+        if op[0] == "write":
+            pa.write_kv(cache, wl.layer, codes_tensor(op[1], wl.src_dtype, dev),
+                        codes_tensor(op[2], wl.src_dtype, dev), torch.from_numpy(op[3]).to(dev))
+        else:
+            pa.copy_blocks(cache, cache, torch.from_numpy(op[1]).to(dev), "d2d")
+    q = codes_tensor(wl.q, wl.q_dtype, dev)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    S, Hq, mc = wl.num_seqs, wl.num_q_heads, wl.max_context_len
+    ws = torch.empty(max(1, pa.decode_workspace_size(cache, S, Hq, mc)), dtype=torch.uint8, device=dev)
+
+    H, B, D, L = wl.num_kv_heads, wl.block_size, wl.head_dim, 64
+    nvb = -(-1500 // B)
+    host, sp = _swap_pools(wl.pool_dtype, nvb, 4 * nvb, L, H, B, D, "block_major")
+    rng = np.random.default_rng(78)
+    ids = rng.permutation(4 * nvb)[:2 * nvb].astype(np.int64)
+    hid = np.arange(nvb, dtype=np.int64)
+    p_out = torch.from_numpy(np.stack([ids[:nvb], hid], 1).copy())
+    p_in = torch.from_numpy(np.stack([hid, ids[nvb:]], 1).copy())
+    nbytes = nvb * 2 * L * H * B * D * workloads.ELEM_BYTES[wl.pool_dtype]
+    copy_stream = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+
+    def decode_steps():
+        for _ in range(steps):
+            pa.decode(cache, wl.layer, q, tables, ctx, mc, wl.scale, out=out, workspace=ws)
+
+    decode_steps()
+    torch.cuda.synchronize()
+    dec_ms = _time_ms(decode_steps, 5, compute)
+    res = {}
+    staging = torch.empty(pa.copy_staging_size(sp, nvb), dtype=torch.uint8, device=dev)
+    for method in ("dma", "kernel", "staged"):
+        def swap_round_trip():
+            if method == "staged":
+                pa.copy_blocks_staged(host, sp, p_out, "d2h", staging, stream=copy_stream)
+                pa.copy_blocks_staged(sp, host, p_in, "h2d", staging, stream=copy_stream)
+            else:
+                sfx = "_kernel" if method == "kernel" else ""
+                pa.copy_blocks(host, sp, p_out, "d2h" + sfx, stream=copy_stream)
+                pa.copy_blocks(sp, host, p_in, "h2d" + sfx, stream=copy_stream)
+
+        swap_round_trip()
+        torch.cuda.synchronize()
+        swp_ms = _time_ms(swap_round_trip, 5, copy_stream)
+        both = []
+        for _ in range(5):
+            a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            a.record(compute)
+            copy_stream.wait_event(a)        # the victim's last use precedes its copy
+            swap_round_trip()
+            c.record(copy_stream)
+            decode_steps()
+            b.record(compute)
+            compute.wait_event(c)            # a step reading the victim waits for its swap-in
+            d.record(compute)
+            torch.cuda.synchronize()
+            both.append((a.elapsed_time(b), a.elapsed_time(c), a.elapsed_time(d)))
+        both = np.median(np.array(both), axis=0)
+        res[method] = {"swap_ms_alone": round(swp_ms, 3),
+                       "swap_GBps_alone": round(2 * nbytes / (swp_ms * 1e-3) / 1e9, 2),
+                       "decode_ms_during_swap": round(float(both[0]), 3),
+                       "swap_ms_during_decode": round(float(both[1]), 3),
+                       "both_ms": round(float(both[2]), 3),
+                       "serial_ms": round(dec_ms + swp_ms, 3)}
+    print(json.dumps({"metric": "swap pipeline overlap", "workload": "long_fp8 decode + 64-layer "
+                      "1,500-token victim out and back", "decode_steps": steps,
+                      "decode_ms_alone": round(dec_ms, 3), **res}), flush=True)
+
+
 MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 / f16 matrix-core peak
 
 
@@ -348,6 +539,10 @@ def main():
         return
     if args.swap:
         swap_bench()
+        return
+    if args.swap_sweep:
+        swap_sweep()
+        swap_overlap()
         return
     if args.prefill:
         prefill_bench(args.steps if args.steps != 50 else 20, args.warmup if args.warmup != 10 else 3)

@@ -60,6 +60,9 @@
  *   so all layers of one block are one contiguous range, which makes a swap
  *   of a block a single transfer ("KV Cache Preemption in vLLM", section
  *   "Swap versus recompute", notes that a block's data spans every layer).
+ *   A layer-major layout (one array of blocks per layer: block_stride = the
+ *   slab, layer_stride >= num_blocks * slab) is accepted too. Either way no
+ *   two (block, layer) slabs may overlap, else PA_ERR_INVALID_ARG.
  *   Positions are 0-based: token t of a sequence lives in logical block
  *   t / block_size at slot t % block_size ("When KV Capacity Runs Out",
  *   section "Running out of KV space during generation": positions count
@@ -281,8 +284,19 @@ pa_status pa_prefill(const pa_kv_cache* cache, int32_t layer, const void* q,
 /*               ("When KV Capacity Runs Out", section "Restore KV stored    */
 /*               outside the GPU").                                          */
 /*               For D2H / H2D `pairs` is in host memory and is validated    */
-/*               (ids in range, destination ids distinct) before any copy;   */
-/*               runs of consecutive ids become one transfer each.           */
+/*               (ids in range, destination ids distinct) before any copy.   */
+/*               The DMA engines copy, one transfer per run of consecutive   */
+/*               ids (per layer unless a block's layers are contiguous on    */
+/*               both sides); kernels on other streams run on undisturbed,   */
+/*               so a swap on a copy stream overlaps decode.                 */
+/*  PA_COPY_D2H_KERNEL, PA_COPY_H2D_KERNEL  the same moves by one kernel     */
+/*               that reads and writes the host pool directly: the host link */
+/*               runs at full speed whatever the block size ("41 ·           */
+/*               Preemption, Recomputation & KV Pressure", section 3: many   */
+/*               small transfers underuse it), but memory-bound kernels on   */
+/*               other streams stall while it runs. The host pool must be    */
+/*               pinned and device-mapped (pa_host_pool_mapped), else        */
+/*               PA_ERR_UNSUPPORTED before any copy.                         */
 /*  pairs        int64 [num_pairs][2] = {src_block, dst_block}.              */
 /*  Both pools must have the same dtype, layers, heads, block size and head  */
 /*  dim (strides may differ). Destination ids must be distinct and, for D2D  */
@@ -290,11 +304,53 @@ pa_status pa_prefill(const pa_kv_cache* cache, int32_t layer, const void* q,
 /*  call (undefined result otherwise). The copied bytes are identical.       */
 /*  num_pairs == 0 is a no-op.                                               */
 /* ------------------------------------------------------------------------ */
-typedef enum { PA_COPY_D2D = 0, PA_COPY_H2D = 1, PA_COPY_D2H = 2 } pa_copy_dir;
+typedef enum {
+  PA_COPY_D2D = 0,
+  PA_COPY_H2D = 1,
+  PA_COPY_D2H = 2,
+  PA_COPY_H2D_KERNEL = 3,
+  PA_COPY_D2H_KERNEL = 4
+} pa_copy_dir;
 
 pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src,
                          const int64_t* pairs, int32_t num_pairs,
                          pa_copy_dir dir, hipStream_t stream);
+
+/* pa_copy_blocks_staged — swap through a device staging buffer.            */
+/*                                                                           */
+/*  The moves of PA_COPY_D2H / PA_COPY_H2D, with the DMA engines moving a    */
+/*  few large ranges: for D2H a kernel first gathers the scattered device    */
+/*  blocks into `staging` (device memory the caller owns, 16-byte aligned),  */
+/*  then one DMA transfer per run of consecutive host ids moves K and V;     */
+/*  for H2D the transfers land in `staging` and a kernel scatters them into  */
+/*  the device blocks. The DMA engines carry the host-link traffic, so a     */
+/*  swap on a copy stream overlaps decode ("When KV Capacity Runs Out",      */
+/*  section "Restore KV stored outside the GPU"), and large transfers keep   */
+/*  the link busy whatever the block size or device layout ("41 ·           */
+/*  Preemption, Recomputation & KV Pressure", section 3).                    */
+/*  dir          PA_COPY_D2H or PA_COPY_H2D.                                 */
+/*  staging      holds at least one block: 2 * num_layers * num_kv_heads *   */
+/*               block_size * head_dim * element bytes; larger lists go in  */
+/*               chunks of as many blocks as fit (pa_copy_staging_size gives */
+/*               the size that moves a list in one chunk), else              */
+/*               PA_ERR_WORKSPACE. Its contents afterwards are unspecified.  */
+/*  The host pool's layers must be contiguous within a block (num_layers ==  */
+/*  1 or layer_stride == num_kv_heads * block_size * head_dim), else        */
+/*  PA_ERR_UNSUPPORTED; the device pool may have any valid layout. Pairs are */
+/*  host memory, checked as for pa_copy_blocks before any device work.       */
+/* ------------------------------------------------------------------------ */
+pa_status pa_copy_blocks_staged(const pa_kv_cache* dst, const pa_kv_cache* src,
+                                const int64_t* pairs, int32_t num_pairs, pa_copy_dir dir,
+                                void* staging, size_t staging_bytes, hipStream_t stream);
+
+/* Staging bytes that let pa_copy_blocks_staged move num_pairs blocks of     */
+/* this pool's geometry in one chunk (0 for an invalid pool or count).       */
+size_t pa_copy_staging_size(const pa_kv_cache* pool, int32_t num_pairs);
+
+/* 1 when the pool's K and V arrays are pinned host memory that the current  */
+/* device addresses directly (what PA_COPY_*_KERNEL needs), 0 otherwise,    */
+/* including for an invalid pool. Leaves no pending HIP error behind.        */
+int32_t pa_host_pool_mapped(const pa_kv_cache* pool);
 
 /* Static, human-readable name of a status code. */
 const char* pa_status_string(pa_status s);

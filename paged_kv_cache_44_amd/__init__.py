@@ -246,22 +246,25 @@ def prefill(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Ten
     return out
 
 
-_DIRS = {"d2d": B.PA_COPY_D2D, "h2d": B.PA_COPY_H2D, "d2h": B.PA_COPY_D2H}
+_DIRS = {"d2d": B.PA_COPY_D2D, "h2d": B.PA_COPY_H2D, "d2h": B.PA_COPY_D2H,
+         "h2d_kernel": B.PA_COPY_H2D_KERNEL, "d2h_kernel": B.PA_COPY_D2H_KERNEL}
 
 
 def copy_blocks(dst: KVCache, src: KVCache, pairs: torch.Tensor, direction: str = "d2d",
                 stream=None) -> None:
     """Copy whole blocks: pairs int64 [N][2] = (src_block, dst_block); device
-    memory for "d2d", host memory for "h2d" / "d2h"."""
+    memory for "d2d", host memory for "h2d" / "d2h" (the DMA engines) and
+    "h2d_kernel" / "d2h_kernel" (one copy kernel; the host pool must be
+    pinned and device-mapped)."""
     _need(pairs.dtype == torch.int64 and pairs.is_contiguous() and
           (pairs.numel() == 0 or (pairs.dim() == 2 and pairs.shape[1] == 2)),
           "pairs must be contiguous int64 [N][2]")
     if direction == "d2d":
         _need(dst.is_device and src.is_device and pairs.is_cuda, "d2d needs device pools and pairs")
-    elif direction == "h2d":
+    elif direction in ("h2d", "h2d_kernel"):
         _need(dst.is_device and not src.is_device and not pairs.is_cuda,
               "h2d copies a host pool into a device pool with host pairs")
-    elif direction == "d2h":
+    elif direction in ("d2h", "d2h_kernel"):
         _need(src.is_device and not dst.is_device and not pairs.is_cuda,
               "d2h copies a device pool into a host pool with host pairs")
     else:
@@ -271,6 +274,39 @@ def copy_blocks(dst: KVCache, src: KVCache, pairs: torch.Tensor, direction: str 
     st = _lib().pa_copy_blocks(ctypes.byref(d), ctypes.byref(s), _ptr(pairs), n,
                                _DIRS[direction], _stream(stream))
     B.check(st, "pa_copy_blocks")
+
+
+def copy_staging_size(pool: KVCache, num_pairs: int) -> int:
+    """Bytes of staging that let :func:`copy_blocks_staged` move num_pairs
+    blocks in one chunk."""
+    c = pool.struct()
+    return int(_lib().pa_copy_staging_size(ctypes.byref(c), int(num_pairs)))
+
+
+def copy_blocks_staged(dst: KVCache, src: KVCache, pairs: torch.Tensor, direction: str,
+                       staging: torch.Tensor, stream=None) -> None:
+    """Swap through a device staging buffer (pa_copy_blocks_staged): "d2h"
+    gathers the device blocks into ``staging`` and moves runs of host blocks
+    by DMA; "h2d" the reverse. pairs int64 [N][2] in host memory."""
+    _need(pairs.dtype == torch.int64 and pairs.is_contiguous() and not pairs.is_cuda and
+          (pairs.numel() == 0 or (pairs.dim() == 2 and pairs.shape[1] == 2)),
+          "pairs must be contiguous host int64 [N][2]")
+    _need(direction in ("h2d", "d2h"), "direction must be 'h2d' or 'd2h'")
+    dev_pool, host_pool = (dst, src) if direction == "h2d" else (src, dst)
+    _need(dev_pool.is_device and not host_pool.is_device, f"{direction} pools on the wrong sides")
+    _on_device(staging)
+    d, s = dst.struct(), src.struct()
+    n = int(pairs.shape[0]) if pairs.dim() == 2 else 0
+    st = _lib().pa_copy_blocks_staged(ctypes.byref(d), ctypes.byref(s), _ptr(pairs), n,
+                                      _DIRS[direction], _ptr(staging),
+                                      staging.numel() * staging.element_size(), _stream(stream))
+    B.check(st, "pa_copy_blocks_staged")
+
+
+def host_pool_mapped(pool: KVCache) -> bool:
+    """Whether the copy kernel can move blocks to and from this host pool."""
+    c = pool.struct()
+    return bool(_lib().pa_host_pool_mapped(ctypes.byref(c)))
 
 
 def version() -> str:

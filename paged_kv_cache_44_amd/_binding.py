@@ -8,12 +8,13 @@ from .build import LIB_PATH
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_SPACE = range(6)
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = range(4)
-PA_COPY_D2D, PA_COPY_H2D, PA_COPY_D2H = range(3)
+PA_COPY_D2D, PA_COPY_H2D, PA_COPY_D2H, PA_COPY_H2D_KERNEL, PA_COPY_D2H_KERNEL = range(5)
 
 #: every function the header declares
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_attend", "pa_decode_merge",
             "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_prefill",
-            "pa_copy_blocks", "pa_status_string", "pa_version",
+            "pa_copy_blocks", "pa_copy_blocks_staged", "pa_copy_staging_size",
+            "pa_host_pool_mapped", "pa_status_string", "pa_version",
             # pa_blocks.h
             "pa_bm_create", "pa_bm_destroy", "pa_bm_num_free", "pa_bm_add", "pa_bm_fork",
             "pa_bm_append", "pa_bm_blocks_needed", "pa_bm_copy_last_block", "pa_bm_release",
@@ -90,6 +91,12 @@ def load_library(path: str = LIB_PATH):
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_copy_blocks.argtypes = [P, P, vp, i32, ctypes.c_int, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_copy_blocks_staged.argtypes = [P, P, vp, i32, ctypes.c_int, vp, sz, vp]
+    lib.pa_copy_blocks_staged.restype = ctypes.c_int
+    lib.pa_copy_staging_size.argtypes = [P, i32]
+    lib.pa_copy_staging_size.restype = sz
+    lib.pa_host_pool_mapped.argtypes = [P]
+    lib.pa_host_pool_mapped.restype = ctypes.c_int32
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []

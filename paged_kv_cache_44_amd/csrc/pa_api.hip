@@ -45,11 +45,18 @@ pa_status check_cache(const pa_kv_cache* c, bool need_ptrs) {
     return PA_ERR_INVALID_ARG;
   if (!is_pow2(c->block_size) || c->block_size > 256) return PA_ERR_INVALID_ARG;
   const int64_t slab = (int64_t)c->num_kv_heads * c->block_size * c->head_dim;
-  if (c->layer_stride < slab && c->num_layers > 1) return PA_ERR_INVALID_ARG;
-  if (c->layer_stride < 0) return PA_ERR_INVALID_ARG;
-  const int64_t span = (int64_t)(c->num_layers - 1) * c->layer_stride + slab;
-  if (c->block_stride < span && c->num_blocks > 1) return PA_ERR_INVALID_ARG;
-  if (c->block_stride < 0) return PA_ERR_INVALID_ARG;
+  if (c->layer_stride < 0 || c->block_stride < 0) return PA_ERR_INVALID_ARG;
+  // no two (block, layer) slabs may overlap: block-major (a block's layers
+  // nested inside its stride) or layer-major (a layer's blocks nested inside
+  // the layer stride)
+  const bool one_l = c->num_layers == 1, one_b = c->num_blocks == 1;
+  const bool block_major =
+      (one_l || c->layer_stride >= slab) &&
+      (one_b || c->block_stride >= (int64_t)(c->num_layers - 1) * c->layer_stride + slab);
+  const bool layer_major =
+      (one_b || c->block_stride >= slab) &&
+      (one_l || c->layer_stride >= (int64_t)(c->num_blocks - 1) * c->block_stride + slab);
+  if (!block_major && !layer_major) return PA_ERR_INVALID_ARG;
   const int eb = elem_bytes(c->dtype);
   if ((c->block_stride * eb) % 16 || (c->layer_stride * eb) % 16) return PA_ERR_UNSUPPORTED;
   if ((c->head_dim * eb) % 16) return PA_ERR_UNSUPPORTED;
@@ -304,6 +311,86 @@ pa_status prefill_impl(const pa_kv_cache* cache, int32_t layer, const void* q, p
   return PA_OK;
 }
 
+// True when K and V of a pool sit in pinned host memory that the current
+// device reaches at the same addresses (hipHostMalloc memory under ROCm's
+// unified addressing), so a kernel can read and write it directly.
+bool host_pool_mapped(const pa_kv_cache* c) {
+  void* p[2] = {c->k, c->v};
+  for (void* q : p) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, q) != hipSuccess) {
+      (void)hipGetLastError();   // pageable memory: not an error of this call
+      return false;
+    }
+    if (at.type != hipMemoryTypeHost || at.devicePointer != q) return false;
+  }
+  return true;
+}
+
+// Launches of arg_copy_kernel over a host-side pair list, kArgCopyPairs at a
+// time. Each side is described by its K and V bases and byte strides.
+struct CopySide {
+  char* k;
+  char* v;
+  int64_t block_bytes;
+  int64_t layer_bytes;
+};
+
+CopySide side_of(const pa_kv_cache* c) {
+  const int eb = elem_bytes(c->dtype);
+  return {reinterpret_cast<char*>(c->k), reinterpret_cast<char*>(c->v), c->block_stride * eb,
+          c->layer_stride * eb};
+}
+
+// pair i of the list is (src_of(i), dst_of(i))
+template <typename SrcOf, typename DstOf>
+pa_status launch_list_copy(const CopySide& dst, const CopySide& src, int64_t slab_bytes,
+                           int32_t num_layers, int32_t n, SrcOf src_of, DstOf dst_of, int max_wgs,
+                           hipStream_t stream) {
+  pa::ArgCopyParams a;
+  memset(&a, 0, sizeof(a));
+  a.dst_k = dst.k;
+  a.dst_v = dst.v;
+  a.src_k = src.k;
+  a.src_v = src.v;
+  a.dst_block_bytes = dst.block_bytes;
+  a.dst_layer_bytes = dst.layer_bytes;
+  a.src_block_bytes = src.block_bytes;
+  a.src_layer_bytes = src.layer_bytes;
+  a.slab_bytes = slab_bytes;
+  a.num_layers = num_layers;
+  a.max_wgs = max_wgs;
+  for (int32_t i = 0; i < n; i += pa::kArgCopyPairs) {
+    const int32_t m = std::min<int32_t>(pa::kArgCopyPairs, n - i);
+    a.num_pairs = m;
+    for (int32_t j = 0; j < m; ++j) {
+      a.pairs[2 * j] = src_of(i + j);
+      a.pairs[2 * j + 1] = dst_of(i + j);
+    }
+    if (pa::launch_arg_copy(a, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+// grid caps: a few dozen workgroups saturate the host link; staging copies
+// stay inside HBM and want the whole chip
+constexpr int kHostLinkWgs = 64;
+constexpr int kStagingWgs = 1024;
+
+// Host pair list checks shared by the host-side copies: ids in range and
+// destination ids distinct.
+bool host_pairs_valid(const pa_kv_cache* dst, const pa_kv_cache* src, const int64_t* pairs,
+                      int32_t num_pairs) {
+  std::vector<int64_t> dsts(num_pairs);
+  for (int i = 0; i < num_pairs; ++i) {
+    const int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= src->num_blocks || d < 0 || d >= dst->num_blocks) return false;
+    dsts[i] = d;
+  }
+  std::sort(dsts.begin(), dsts.end());
+  return std::adjacent_find(dsts.begin(), dsts.end()) == dsts.end();
+}
+
 bool same_shape(const pa_kv_cache* a, const pa_kv_cache* b) {
   return a->dtype == b->dtype && a->num_layers == b->num_layers &&
          a->num_kv_heads == b->num_kv_heads && a->block_size == b->block_size &&
@@ -422,7 +509,9 @@ pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src, const i
   if (st != PA_OK) return st;
   if (!same_shape(dst, src)) return PA_ERR_INVALID_ARG;
   if (num_pairs < 0) return PA_ERR_INVALID_ARG;
-  if (!(dir == PA_COPY_D2D || dir == PA_COPY_H2D || dir == PA_COPY_D2H)) return PA_ERR_INVALID_ARG;
+  if (!(dir == PA_COPY_D2D || dir == PA_COPY_H2D || dir == PA_COPY_D2H ||
+        dir == PA_COPY_H2D_KERNEL || dir == PA_COPY_D2H_KERNEL))
+    return PA_ERR_INVALID_ARG;
   if (num_pairs == 0) return PA_OK;
   if (!pairs) return PA_ERR_INVALID_ARG;
   const int eb = elem_bytes(dst->dtype);
@@ -451,16 +540,18 @@ pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src, const i
   }
 
   // host pairs: validate everything before the first copy
-  std::vector<int64_t> dsts(num_pairs);
-  for (int i = 0; i < num_pairs; ++i) {
-    const int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
-    if (s < 0 || s >= src->num_blocks || d < 0 || d >= dst->num_blocks) return PA_ERR_INVALID_ARG;
-    dsts[i] = d;
-  }
-  std::sort(dsts.begin(), dsts.end());
-  if (std::adjacent_find(dsts.begin(), dsts.end()) != dsts.end()) return PA_ERR_INVALID_ARG;
+  if (!host_pairs_valid(dst, src, pairs, num_pairs)) return PA_ERR_INVALID_ARG;
 
-  const hipMemcpyKind kind = dir == PA_COPY_H2D ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+  const bool to_dev = dir == PA_COPY_H2D || dir == PA_COPY_H2D_KERNEL;
+  if (dir == PA_COPY_H2D_KERNEL || dir == PA_COPY_D2H_KERNEL) {
+    if (dst->num_layers > 32767 || !host_pool_mapped(to_dev ? src : dst)) return PA_ERR_UNSUPPORTED;
+    return launch_list_copy(
+        side_of(dst), side_of(src), slab, dst->num_layers, num_pairs,
+        [&](int32_t i) { return pairs[2 * i]; }, [&](int32_t i) { return pairs[2 * i + 1]; },
+        kHostLinkWgs, stream);
+  }
+
+  const hipMemcpyKind kind = to_dev ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
   const int L = dst->num_layers;
   const int64_t block_bytes = slab * L;
   // a block is one contiguous range when its layers sit back to back; runs of
@@ -496,6 +587,80 @@ pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src, const i
     i += run;
   }
   return PA_OK;
+}
+
+pa_status pa_copy_blocks_staged(const pa_kv_cache* dst, const pa_kv_cache* src,
+                                const int64_t* pairs, int32_t num_pairs, pa_copy_dir dir,
+                                void* staging, size_t staging_bytes, hipStream_t stream) {
+  pa_status st = check_cache(dst, true);
+  if (st != PA_OK) return st;
+  st = check_cache(src, true);
+  if (st != PA_OK) return st;
+  if (!same_shape(dst, src)) return PA_ERR_INVALID_ARG;
+  if (num_pairs < 0 || !(dir == PA_COPY_H2D || dir == PA_COPY_D2H)) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs || !staging) return PA_ERR_INVALID_ARG;
+  if (!aligned(staging, 16)) return PA_ERR_UNSUPPORTED;
+  const bool to_dev = dir == PA_COPY_H2D;
+  const pa_kv_cache* host = to_dev ? src : dst;
+  const int eb = elem_bytes(dst->dtype);
+  const int L = dst->num_layers;
+  const int64_t slab = (int64_t)dst->num_kv_heads * dst->block_size * dst->head_dim * eb;
+  const int64_t blk = slab * L;                       // one block's K (or V), every layer
+  if (L > 1 && host->layer_stride * eb != slab) return PA_ERR_UNSUPPORTED;
+  if (L > 32767) return PA_ERR_UNSUPPORTED;
+  const int64_t cap64 = (int64_t)(staging_bytes / (size_t)(2 * blk));
+  if (cap64 < 1) return PA_ERR_WORKSPACE;
+  if (!host_pairs_valid(dst, src, pairs, num_pairs)) return PA_ERR_INVALID_ARG;
+
+  const int32_t cap = (int32_t)std::min<int64_t>(cap64, num_pairs);
+  char* sk = static_cast<char*>(staging);
+  const CopySide stage = {sk, sk + (int64_t)cap * blk, blk, slab};
+  const CopySide hs = side_of(host);
+  const bool packed = host->num_blocks == 1 || hs.block_bytes == blk;
+  const hipMemcpyKind kind = to_dev ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+  for (int32_t c = 0; c < num_pairs; c += cap) {
+    const int32_t m = std::min<int32_t>(cap, num_pairs - c);
+    const int64_t* pc = pairs + 2 * (int64_t)c;
+    if (!to_dev) {   // gather the device blocks into staging slots 0..m-1
+      st = launch_list_copy(
+          stage, side_of(src), slab, L, m, [&](int32_t i) { return pc[2 * i]; },
+          [&](int32_t i) { return (int64_t)i; }, kStagingWgs, stream);
+      if (st != PA_OK) return st;
+    }
+    // one DMA transfer per run of consecutive host ids, for K and for V
+    for (int32_t i = 0; i < m;) {
+      const int64_t h0 = pc[2 * i + (to_dev ? 0 : 1)];
+      int32_t run = 1;
+      while (packed && i + run < m && pc[2 * (i + run) + (to_dev ? 0 : 1)] == h0 + run) ++run;
+      for (int kv = 0; kv < 2; ++kv) {
+        char* hp = (kv ? hs.v : hs.k) + h0 * hs.block_bytes;
+        char* sp = (kv ? stage.v : stage.k) + (int64_t)i * blk;
+        if (hipMemcpyAsync(to_dev ? sp : hp, to_dev ? hp : sp, (size_t)run * (size_t)blk, kind,
+                           stream) != hipSuccess)
+          return PA_ERR_HIP;
+      }
+      i += run;
+    }
+    if (to_dev) {    // scatter staging slots 0..m-1 into the device blocks
+      st = launch_list_copy(
+          side_of(dst), stage, slab, L, m, [&](int32_t i) { return (int64_t)i; },
+          [&](int32_t i) { return pc[2 * i + 1]; }, kStagingWgs, stream);
+      if (st != PA_OK) return st;
+    }
+  }
+  return PA_OK;
+}
+
+size_t pa_copy_staging_size(const pa_kv_cache* pool, int32_t num_pairs) {
+  if (check_cache(pool, false) != PA_OK || num_pairs <= 0) return 0;
+  return (size_t)num_pairs * 2 * (size_t)pool->num_layers * (size_t)pool->num_kv_heads *
+         (size_t)pool->block_size * (size_t)pool->head_dim * (size_t)elem_bytes(pool->dtype);
+}
+
+int32_t pa_host_pool_mapped(const pa_kv_cache* pool) {
+  if (check_cache(pool, true) != PA_OK) return 0;
+  return host_pool_mapped(pool) ? 1 : 0;
 }
 
 const char* pa_status_string(pa_status s) {

@@ -101,6 +101,26 @@ struct CopyParams {
   int32_t num_pairs;
 };
 
+// Block copies whose pairs travel in the kernel arguments (kArgCopyPairs
+// per launch): between device memory and pinned, device-mapped host memory,
+// and between device pools and a staging buffer. max_wgs caps the grid.
+constexpr int kArgCopyPairs = 64;
+struct ArgCopyParams {
+  char* dst_k;
+  char* dst_v;
+  const char* src_k;
+  const char* src_v;
+  int64_t dst_block_bytes;
+  int64_t dst_layer_bytes;
+  int64_t src_block_bytes;
+  int64_t src_layer_bytes;
+  int64_t slab_bytes;
+  int32_t num_layers;
+  int32_t num_pairs;         // <= kArgCopyPairs
+  int32_t max_wgs;
+  int64_t pairs[2 * kArgCopyPairs];
+};
+
 hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipStream_t st);
 hipError_t launch_merge(const DecodeParams& a, int q_ty, hipStream_t st);
 bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
@@ -116,5 +136,6 @@ hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, in
                           hipStream_t st);
 hipError_t launch_write(const WriteParams& a, int src_ty, int dst_ty, hipStream_t st);
 hipError_t launch_copy(const CopyParams& a, hipStream_t st);
+hipError_t launch_arg_copy(const ArgCopyParams& a, hipStream_t st);
 
 }  // namespace pa

@@ -117,3 +117,55 @@ def test_host_copy_pairs_validated_before_any_copy(pa_lib):
     other = _cache(blocks=4, bs=8)
     assert run([(0, 1)], src=other) == B.PA_ERR_INVALID_ARG  # geometry differs
     assert run([], direction=B.PA_COPY_D2D) == B.PA_OK
+
+
+def test_pool_layouts_block_major_and_layer_major(pa_lib):
+    heads, bs, dim, nb, L = 8, 16, 128, 10, 4
+    slab = heads * bs * dim
+
+    def status(block_stride, layer_stride, blocks=nb, layers=L):
+        c = B.PaKvCache(FAKE, FAKE, B.PA_BF16, blocks, layers, heads, bs, dim, block_stride,
+                        layer_stride, 1.0, 1.0)
+        return pa_lib.pa_copy_blocks(ctypes.byref(c), ctypes.byref(c), None, 0, B.PA_COPY_D2D, None)
+    assert status(L * slab, slab) == B.PA_OK                       # block-major, packed
+    assert status(L * (slab + 32) + 64, slab + 32) == B.PA_OK       # block-major, padded
+    assert status(slab, nb * slab) == B.PA_OK                       # layer-major
+    assert status(slab + 64, nb * (slab + 64)) == B.PA_OK           # layer-major, padded
+    assert status(slab, slab) == B.PA_ERR_INVALID_ARG               # layers and blocks collide
+    assert status(L * slab - 8, slab) == B.PA_ERR_INVALID_ARG       # blocks overlap
+    assert status(slab, (nb - 1) * slab) == B.PA_ERR_INVALID_ARG    # layers overlap
+    assert status(slab - 8, 0, layers=1) == B.PA_ERR_INVALID_ARG    # blocks overlap
+    assert status(0, slab - 8, blocks=1) == B.PA_ERR_INVALID_ARG    # layers overlap
+    assert status(0, 0, blocks=1, layers=1) == B.PA_OK
+
+
+def test_host_pool_mapped_rejects_invalid_pool_without_device_calls(pa_lib):
+    assert pa_lib.pa_host_pool_mapped(ctypes.byref(_cache(bs=0))) == 0
+    assert pa_lib.pa_host_pool_mapped(None) == 0
+
+
+def test_staged_copy_arguments_checked_before_device_work(pa_lib):
+    heads, bs, dim, L = 8, 16, 128, 4
+    slab = heads * bs * dim
+    dev = B.PaKvCache(FAKE, FAKE, B.PA_BF16, 10, L, heads, bs, dim, slab, 10 * slab, 1.0, 1.0)
+    host = B.PaKvCache(FAKE, FAKE, B.PA_BF16, 6, L, heads, bs, dim, L * slab, slab, 1.0, 1.0)
+    one = 2 * L * slab * 2                              # bytes of one block, K and V
+    assert pa_lib.pa_copy_staging_size(ctypes.byref(dev), 3) == 3 * one
+    assert pa_lib.pa_copy_staging_size(ctypes.byref(dev), 0) == 0
+
+    def run(pairs, direction=B.PA_COPY_D2H, dst=host, src=dev, staging=FAKE, nbytes=one):
+        arr = (ctypes.c_int64 * (2 * len(pairs)))(*[x for p in pairs for x in p])
+        return pa_lib.pa_copy_blocks_staged(ctypes.byref(dst), ctypes.byref(src), arr, len(pairs),
+                                            direction, staging, nbytes, None)
+    assert run([]) == B.PA_OK
+    assert run([(0, 1)], direction=B.PA_COPY_D2D) == B.PA_ERR_INVALID_ARG
+    assert run([(0, 1)], direction=B.PA_COPY_D2H_KERNEL) == B.PA_ERR_INVALID_ARG
+    assert run([(0, 1)], staging=None) == B.PA_ERR_INVALID_ARG
+    assert run([(0, 1)], staging=FAKE + 8) == B.PA_ERR_UNSUPPORTED
+    assert run([(0, 1)], nbytes=one - 16) == B.PA_ERR_WORKSPACE
+    assert run([(0, 6)]) == B.PA_ERR_INVALID_ARG             # host id out of range
+    assert run([(0, 1), (2, 1)]) == B.PA_ERR_INVALID_ARG     # duplicate destination
+    # the host pool's layers must be contiguous within a block
+    assert run([(0, 1)], dst=dev, src=dev) == B.PA_ERR_UNSUPPORTED
+    assert run([(1, 0)], direction=B.PA_COPY_H2D, dst=dev, src=host, nbytes=0) == \
+        B.PA_ERR_WORKSPACE

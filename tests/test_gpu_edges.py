@@ -256,11 +256,16 @@ def test_write_skips_padding_and_foreign_slots_multilayer():
     assert same
 
 
-def _pool_pair(dtype, nblk, L, H, B, D, bpad=0, lpad=0, pin=False, seed=0):
+def _pool_pair(dtype, nblk, L, H, B, D, bpad=0, lpad=0, pin=False, seed=0, layer_major=False):
     """A KVCache with optional stride padding, filled with random codes,
-    plus its oracle geometry and host code copies."""
-    ls = H * B * D + lpad
-    bs = L * ls + bpad
+    plus its oracle geometry and host code copies. Block-major by default;
+    layer-major puts each layer's blocks in one array."""
+    if layer_major:
+        bs = H * B * D + bpad
+        ls = nblk * bs + lpad
+    else:
+        ls = H * B * D + lpad
+        bs = L * ls + bpad
     n = (nblk - 1) * bs + (L - 1) * ls + H * B * D
     rng = np.random.default_rng(seed)
     ct = workloads.CODE_TYPE[dtype]
@@ -288,24 +293,88 @@ def test_copy_d2d_bit_exact(bpad, lpad):
     assert np.array_equal(tensor_codes(cache.v), ev)
 
 
-@pytest.mark.parametrize("layout", ["packed", "padded"])
-def test_swap_out_and_in_bit_exact(layout):
-    bpad = 0 if layout == "packed" else 48
-    dev, dgeom, dk, dv = _pool_pair("bf16", 30, 2, 2, 16, 64, bpad, 0, seed=1)
-    host, hgeom, hk, hv = _pool_pair("bf16", 12, 2, 2, 16, 64, 0, 0, pin=True, seed=2)
-    # runs of consecutive ids (coalesced) and scattered ones
-    out_pairs = np.array([[3, 0], [4, 1], [5, 2], [17, 7], [9, 3], [10, 4]], dtype=np.int64)
-    pa.copy_blocks(host, dev, torch.from_numpy(out_pairs), "d2h")
+@pytest.mark.parametrize("method", ["kernel", "dma", "staged"])
+@pytest.mark.parametrize("layout", ["packed", "padded", "layer_major"])
+def test_swap_out_and_in_bit_exact(layout, method):
+    """Swap out to pinned host blocks and back into other device blocks, by
+    the DMA engines, by the copy kernel (pinned host memory is
+    device-mapped) and through a staging buffer that holds 20 blocks (so the
+    list goes in four chunks): runs of consecutive ids, scattered ids, and
+    more pairs than one kernel launch carries."""
+    nd, nh = 160, 100
+    dev, dgeom, dk, dv = _pool_pair("bf16", nd, 2, 2, 16, 64, 0 if layout == "packed" else 48,
+                                    16 if layout == "layer_major" else 0, seed=1,
+                                    layer_major=layout == "layer_major")
+    host, hgeom, hk, hv = _pool_pair("bf16", nh, 2, 2, 16, 64, 0, 0, pin=True, seed=2)
+    assert pa.host_pool_mapped(host)
+    assert not pa.host_pool_mapped(dev)
+    sfx = "_kernel" if method == "kernel" else ""
+    staging = torch.empty(pa.copy_staging_size(dev, 20), dtype=torch.uint8, device="cuda")
+
+    def move(dst, src, pairs, direction):
+        if method == "staged":
+            pa.copy_blocks_staged(dst, src, torch.from_numpy(pairs), direction, staging)
+        else:
+            pa.copy_blocks(dst, src, torch.from_numpy(pairs), direction + sfx)
+    rng = np.random.default_rng(5)
+    scattered = rng.permutation(np.arange(30, nd))[:70]
+    out_pairs = np.concatenate([np.array([[3, 0], [4, 1], [5, 2], [17, 7], [9, 3], [10, 4]]),
+                                np.stack([scattered, 10 + np.arange(70)], 1)]).astype(np.int64)
+    move(host, dev, out_pairs, "d2h")
     torch.cuda.synchronize()
     ehk, ehv = paged.copy_blocks(hk, hv, hgeom, dk, dv, dgeom, out_pairs)
     assert np.array_equal(tensor_codes(host.k), ehk)
     assert np.array_equal(tensor_codes(host.v), ehv)
-    in_pairs = np.array([[0, 20], [1, 21], [2, 22], [7, 11], [3, 29], [4, 0]], dtype=np.int64)
-    pa.copy_blocks(dev, host, torch.from_numpy(in_pairs), "h2d")
+    back = rng.permutation(nd)[:76]
+    in_pairs = np.stack([out_pairs[:, 1], back], 1).astype(np.int64)
+    move(dev, host, in_pairs, "h2d")
     torch.cuda.synchronize()
     edk, edv = paged.copy_blocks(dk, dv, dgeom, ehk, ehv, hgeom, in_pairs)
     assert np.array_equal(tensor_codes(dev.k), edk)
     assert np.array_equal(tensor_codes(dev.v), edv)
+
+
+def test_layer_major_pool_write_decode_prefill():
+    """A layer-major pool (each layer's blocks in one padded array): writes
+    into three layers, then decode and prefill of every layer against the
+    oracle on the same strides."""
+    dt, L, H, G, B, D, nblk = "f16", 3, 2, 4, 16, 128, 24
+    cache, geom, _, _ = _pool_pair(dt, nblk, L, H, B, D, 64, 256, seed=7, layer_major=True)
+    ok, ov = tensor_codes(cache.k), tensor_codes(cache.v)
+    rng = np.random.default_rng(8)
+    ctx = np.array([37, 16, 70], np.int32)
+    perm = rng.permutation(nblk)
+    nbs = -(-ctx // B)
+    tables = np.zeros((3, nbs.max()), np.int32)
+    pos = 0
+    for i, n in enumerate(nbs):
+        tables[i, :n] = perm[pos:pos + n]
+        pos += n
+    slots = np.concatenate([tables[i, np.arange(n) // B].astype(np.int64) * B + np.arange(n) % B
+                            for i, n in enumerate(ctx)])
+    for layer in range(L):
+        k = workloads.normal_codes(rng, (len(slots), H, D), dt)
+        v = workloads.normal_codes(rng, (len(slots), H, D), dt)
+        pa.write_kv(cache, layer, codes_to_tensor(k, dt), codes_to_tensor(v, dt),
+                    torch.from_numpy(slots).cuda())
+        ok, ov = paged.write_kv(ok, ov, geom, dt, layer, k, v, dt, slots)
+    q = workloads.normal_codes(rng, (3, H * G, D), dt)
+    nq = np.array([5, 16, 20])
+    qsl = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    qp = workloads.normal_codes(rng, (int(qsl[-1]), H * G, D), dt)
+    tt, ct = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    for layer in range(L):
+        out = pa.decode(cache, layer, codes_to_tensor(q, dt), tt, ct, int(ctx.max()), 0.1)
+        outp = pa.prefill(cache, layer, codes_to_tensor(qp, dt), tt, ct, int(ctx.max()),
+                          torch.from_numpy(qsl).cuda(), int(nq.max()), 0.1)
+        torch.cuda.synchronize()
+        ref = paged.decode(q, dt, ok, ov, geom, dt, layer, tables, ctx, 0.1)
+        refp = paged.prefill(qp, dt, ok, ov, geom, dt, layer, tables, ctx, qsl, 0.1)
+        e1 = max_err_stored(codecs.decode(tensor_codes(out), dt), ref, dt)
+        e2 = max_err_stored(codecs.decode(tensor_codes(outp), dt), refp, dt)
+        say(f"layer {layer}: decode {e1:.3e}, prefill {e2:.3e} beyond output rounding")
+        assert e1 <= TOL[dt] and e2 <= TOL[dt]
+    assert np.array_equal(tensor_codes(cache.k), ok) and np.array_equal(tensor_codes(cache.v), ov)
 
 
 def test_argument_errors_raise():

@@ -1,0 +1,101 @@
+"""Swap on a copy stream beside the compute stream, ordered by events ("When
+KV Capacity Runs Out", section "Restore KV stored outside the GPU": a block
+must not be handed to another sequence before its copy out has finished, and
+restored blocks may land elsewhere): a four-layer victim is written on the
+compute stream, copied out on the copy stream after an event, its blocks are
+reused on the compute stream only after the copy's completion event, and it
+is copied back into other blocks and decoded once the compute stream has
+waited for the copy in. Pools, host copy and decode outputs against the
+oracle mirror of the same steps."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_44_amd as pa
+import workloads
+from oracle import codecs, paged
+from tests.gpu_helpers import TOL, codes_to_tensor, max_err_stored, say, tensor_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request, gpu):
+    say(f"\n[gpu] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dt", ["f16", "fp8_e4m3"])
+def test_copy_stream_swap_ordered_by_events(dt):
+    rng = np.random.default_rng(91)
+    L, H, B, D, NB, NH, G = 4, 2, 16, 128, 32, 8, 4
+    src_dt = "f16"
+    ks, vs = (1.0, 1.0) if dt != "fp8_e4m3" else (0.05, 0.04)
+    geom, hgeom = paged.Geometry(NB, L, H, B, D), paged.Geometry(NH, L, H, B, D)
+    nan = workloads.NAN_CODE[dt]
+    ok = np.full(geom.pool_elements(), nan, workloads.CODE_TYPE[dt])
+    ov = ok.copy()
+    hk = np.full(hgeom.pool_elements(), nan, workloads.CODE_TYPE[dt])
+    hv = hk.copy()
+    dev = pa.KVCache(codes_to_tensor(ok, dt), codes_to_tensor(ov, dt), dt, NB, L, H, B, D,
+                     k_scale=ks, v_scale=vs)
+    host = pa.KVCache.empty(dt, NH, L, H, B, D, pin_memory=True, k_scale=ks, v_scale=vs)
+    host.k.view(torch.uint8).fill_(0xFF)
+    host.v.view(torch.uint8).fill_(0xFF)
+    hk[:] = tensor_codes(host.k)
+    hv[:] = tensor_codes(host.v)
+
+    compute, copy_stream = torch.cuda.current_stream(), torch.cuda.Stream()
+    n = 41                                           # 3 blocks, the last partly used
+    victim = np.array([21, 5, 13], np.int64)
+    slots = (victim[np.arange(n) // B] * B + np.arange(n) % B).astype(np.int64)
+
+    def write(layer, k, v, sl):
+        nonlocal ok, ov
+        pa.write_kv(dev, layer, codes_to_tensor(k, src_dt), codes_to_tensor(v, src_dt),
+                    torch.from_numpy(sl).cuda())
+        ok, ov = paged.write_kv(ok, ov, geom, dt, layer, k, v, src_dt, sl, ks, vs)
+
+    for layer in range(L):
+        write(layer, workloads.normal_codes(rng, (n, H, D), src_dt),
+              workloads.normal_codes(rng, (n, H, D), src_dt), slots)
+    ready = torch.cuda.Event()
+    ready.record(compute)
+    copy_stream.wait_event(ready)                    # after the victim's last write
+    out_pairs = np.stack([victim, np.array([2, 3, 4])], 1)
+    pa.copy_blocks(host, dev, torch.from_numpy(out_pairs.copy()), "d2h", stream=copy_stream)
+    hk, hv = paged.copy_blocks(hk, hv, hgeom, ok, ov, geom, out_pairs)
+    copied = torch.cuda.Event()
+    copied.record(copy_stream)
+    compute.wait_event(copied)                       # only now may the blocks be reused
+    for layer in range(L):
+        write(layer, workloads.normal_codes(rng, (n, H, D), src_dt),
+              workloads.normal_codes(rng, (n, H, D), src_dt), slots)
+    reused = torch.cuda.Event()
+    reused.record(compute)
+    copy_stream.wait_event(reused)
+    restore = np.array([30, 0, 17], np.int64)
+    in_pairs = np.stack([np.array([2, 3, 4]), restore], 1)
+    pa.copy_blocks(dev, host, torch.from_numpy(in_pairs.copy()), "h2d", stream=copy_stream)
+    ok, ov = paged.copy_blocks(ok, ov, geom, hk, hv, hgeom, in_pairs)
+    restored = torch.cuda.Event()
+    restored.record(copy_stream)
+    compute.wait_event(restored)                     # decode reads the restored blocks
+    q = workloads.normal_codes(rng, (2, H * G, D), "f16")
+    tables = np.stack([restore, victim]).astype(np.int32)
+    ctx = np.array([n, n], np.int32)
+    outs = []
+    for layer in range(L):
+        outs.append(pa.decode(dev, layer, codes_to_tensor(q, "f16"), torch.from_numpy(tables).cuda(),
+                              torch.from_numpy(ctx).cuda(), n, 0.088))
+    torch.cuda.synchronize()
+    assert np.array_equal(tensor_codes(host.k), hk) and np.array_equal(tensor_codes(host.v), hv)
+    assert np.array_equal(tensor_codes(dev.k), ok) and np.array_equal(tensor_codes(dev.v), ov)
+    for layer in range(L):
+        got = codecs.decode(tensor_codes(outs[layer]), "f16")
+        ref = paged.decode(q, "f16", ok, ov, geom, dt, layer, tables, ctx, 0.088, ks, vs)
+        ex = max_err_stored(got, ref, "f16")
+        say(f"{dt} layer {layer}: decode error beyond output rounding {ex:.3e}")
+        assert np.all(np.isfinite(got)) and ex <= TOL[dt if dt == "fp8_e4m3" else "f16"]
