@@ -70,6 +70,9 @@ def parse():
                     help="time the long FP8 workload's swap-victim block moves between pinned "
                          "host memory and the device (1 layer and a 64-layer stack); one JSON "
                          "line per case")
+    ap.add_argument("--shared", action="store_true",
+                    help="decode with pa_decode_shared (prefixes shared by runs of consecutive "
+                         "sequences read once per group; sharing planned every step)")
     ap.add_argument("--swap-sweep", action="store_true",
                     help="swap moves of a 1,500-token FP8 victim for block sizes 8..128, one "
                          "layer and 64 layers, block-major and layer-major pools; then the "
@@ -576,8 +579,9 @@ def main():
     ctx = torch.from_numpy(wl.context_lens).to(dev)
     max_ctx = wl.max_context_len
     S, Hq = wl.num_seqs, wl.num_q_heads
-    ws = torch.empty(max(1, pa.decode_workspace_size(cache, S, Hq, max_ctx)), dtype=torch.uint8,
-                     device=dev)
+    ws_n = (pa.decode_shared_workspace_size(cache, S, Hq) if args.shared
+            else pa.decode_workspace_size(cache, S, Hq, max_ctx))
+    ws = torch.empty(max(1, ws_n), dtype=torch.uint8, device=dev)
     part = pa.decode_partition_tokens(cache, S, Hq, max_ctx)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; partition {part} tokens",
@@ -590,6 +594,12 @@ def main():
         pa.write_kv(cache, wl.layer, step_k, step_v, step_slots)
         if i is not None:
             ev[i][0].record()
+        if args.shared:     # planning, prefix pass, suffix pass and merges: all timed
+            pa.decode_shared(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out=out,
+                             workspace=ws)
+            if i is not None:
+                ev[i][1].record()
+            return
         pa.decode_attend(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
         if i is not None:
             ev[i][1].record()
@@ -610,7 +620,7 @@ def main():
     # the Infinity Cache before each call (untimed)
     scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     fl = []
-    for _ in range(args.flush_iters):
+    for _ in range(0 if args.shared else args.flush_iters):
         scratch.fill_(1.0)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -625,9 +635,15 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     uniq = unique_decode_bytes(wl)
     ab = attend_bytes(wl)
-    achieved = ab / (attend_ms * 1e-3) / 1e9
     kname = attend_kernel_name(wl)
     traffic = load_traffic(kname, wl.name)
+    if args.shared:
+        # the whole shared decode against the bytes it must read at the least:
+        # every physical slot in use once
+        ab = uniq - (workloads.decode_bytes(wl) - attend_bytes(wl))
+        kname = "decode_shared (plan, prefix and suffix passes, merges)"
+        traffic = None
+    achieved = ab / (attend_ms * 1e-3) / 1e9
     rec = {
         "metric": "paged-decode KV GB/s and % of MI355X HBM peak; sequences/s at 1 GPU",
         "value": round(value, 2),

@@ -229,6 +229,51 @@ size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t max_context_len);
 
 /* ------------------------------------------------------------------------ */
+/* pa_decode_shared — pa_decode that reads a prefix shared by several        */
+/* sequences once per group of up to 16 / g of them.                         */
+/*                                                                           */
+/* Same arguments and same result as pa_decode. Parallel samples of one      */
+/* prompt share the prompt's blocks ("Efficient Memory Management ... with   */
+/* PagedAttention", sampling paragraph; "Continuous Batching and             */
+/* PagedAttention", section "Sharing, the part that goes beyond fixing what  */
+/* broke"); pa_decode reads such a block once per sequence. Here sharing is  */
+/* found in the block tables: a run of consecutive sequences, each naming    */
+/* the same leading blocks as the one before for at least 16 tokens, shares */
+/* the common prefix of all its members (rounded down to a multiple of 16   */
+/* tokens and capped by every member's context). Up to 16 / g members at a   */
+/* time attend to that prefix together, their queries side by side in one   */
+/* matrix-core tile, so each prefix block is read once per group; each      */
+/* member then attends to the rest of its context, starting from the        */
+/* prefix's partial result. Put the samples of one prompt next to each      */
+/* other in the batch; sequences that share nothing cost one extra pass     */
+/* over the batch's descriptors.                                             */
+/*                                                                           */
+/*  reuse_plan   0: find the sharing from block_tables / context_lens and    */
+/*               store it in the workspace (two small launches). 1: use the  */
+/*               plan the previous call left in this workspace (another      */
+/*               layer of the same step: same tables, lengths, num_seqs and  */
+/*               pool geometry; anything else gives undefined results).      */
+/*  workspace    >= pa_decode_shared_workspace_size(...) bytes, 256-byte     */
+/*               aligned.                                                    */
+/* Supported: the matrix-core configurations of pa_decode (PA_F16 / PA_BF16 */
+/* pools with the same q_dtype, PA_FP8_E4M3 pools with PA_F16 / PA_BF16     */
+/* queries; head_dim 64 or 128; g in {1, 2, 4, 8}; num_seqs <= 8192); others */
+/* return PA_ERR_UNSUPPORTED (use pa_decode).                                */
+/* ------------------------------------------------------------------------ */
+pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* q,
+                           pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t num_seqs,
+                           int32_t num_q_heads, float scale, int32_t reuse_plan,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes pa_decode_shared needs for these sizes (0 if the          */
+/* configuration is unsupported or invalid). Depends on the current         */
+/* device's compute-unit count; query it with that device current.          */
+size_t pa_decode_shared_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
+                                       int32_t num_q_heads);
+
+/* ------------------------------------------------------------------------ */
 /* pa_prefill — paged prefill: causal attention of each sequence's newest    */
 /* positions (a whole prompt, a later chunk of one, or the prompt plus the   */
 /* generated tokens of a recomputed request, which "When KV Capacity Runs    */

@@ -201,6 +201,47 @@ def decode(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Tens
                         max_context_len, scale, out, workspace, stream)[0]
 
 
+def decode_shared_workspace_size(cache: KVCache, num_seqs: int, num_q_heads: int) -> int:
+    c = cache.struct()
+    return int(_lib().pa_decode_shared_workspace_size(ctypes.byref(c), num_seqs, num_q_heads))
+
+
+def decode_shared(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, max_context_len: int, scale: float,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  reuse_plan: bool = False, stream=None) -> torch.Tensor:
+    """pa_decode_shared: the result of :func:`decode`, reading the prefix that
+    runs of consecutive sequences share (same leading blocks in their tables)
+    once per group of up to 16 / G of them. ``reuse_plan`` keeps the sharing
+    found by the previous call with this workspace (same tables and lengths)."""
+    _need(cache.is_device, "decode needs a device pool")
+    _need(q.dim() == 3 and q.shape[2] == cache.head_dim, "q must be [S][H_q][head_dim]")
+    S, Hq, D = q.shape
+    _on_device(q, block_tables, context_lens)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _on_device(out)
+        _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    if workspace is None:
+        n = decode_shared_workspace_size(cache, S, Hq)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _on_device(workspace)
+    c = cache.struct()
+    st = _lib().pa_decode_shared(
+        ctypes.byref(c), layer, _ptr(q), DTYPES[dtype_name(q)], _ptr(out), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), S, Hq,
+        float(scale), 1 if reuse_plan else 0, _ptr(workspace), int(workspace.numel()),
+        _stream(stream))
+    B.check(st, "pa_decode_shared")
+    return out
+
+
 def decode_attend(cache, layer, q, block_tables, context_lens, max_context_len, scale,
                   out, workspace, stream=None):
     """Phase 1 of :func:`decode` (partition attention)."""

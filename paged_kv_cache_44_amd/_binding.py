@@ -12,7 +12,8 @@ PA_COPY_D2D, PA_COPY_H2D, PA_COPY_D2H, PA_COPY_H2D_KERNEL, PA_COPY_D2H_KERNEL = 
 
 #: every function the header declares
 EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_attend", "pa_decode_merge",
-            "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_prefill",
+            "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode_shared",
+            "pa_decode_shared_workspace_size", "pa_prefill",
             "pa_copy_blocks", "pa_copy_blocks_staged", "pa_copy_staging_size",
             "pa_host_pool_mapped", "pa_status_string", "pa_version",
             # pa_blocks.h
@@ -60,6 +61,10 @@ def load_library(path: str = LIB_PATH):
     for name in ("pa_decode", "pa_decode_attend", "pa_decode_merge"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = ctypes.c_int
+    lib.pa_decode_shared.argtypes = dec[:12] + [i32] + dec[12:]
+    lib.pa_decode_shared.restype = ctypes.c_int
+    lib.pa_decode_shared_workspace_size.argtypes = [P, i32, i32]
+    lib.pa_decode_shared_workspace_size.restype = sz
     lib.pa_prefill.argtypes = [P, i32, vp, ctypes.c_int, vp, vp, i32, vp, i32, vp, i32, i32, i32,
                                i32, f32, vp]
     lib.pa_prefill.restype = ctypes.c_int

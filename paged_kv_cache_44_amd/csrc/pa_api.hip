@@ -175,6 +175,74 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
 
 enum Phase { PHASE_ATTEND = 1, PHASE_MERGE = 2, PHASE_BOTH = 3 };
 
+// Launch parameters common to every decode kernel.
+DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* q, void* out,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t max_context_len,
+                           int32_t num_seqs, int32_t num_q_heads, float scale) {
+  DecodeParams a;
+  memset(&a, 0, sizeof(a));
+  a.k_pool = cache->k;
+  a.v_pool = cache->v;
+  a.block_stride = cache->block_stride;
+  a.layer_offset = (int64_t)layer * cache->layer_stride;
+  a.num_blocks = cache->num_blocks;
+  a.block_size = cache->block_size;
+  a.log2_block_size = ilog2(cache->block_size);
+  a.head_dim = cache->head_dim;
+  const bool fp8 = cache->dtype == PA_FP8_E4M3;
+  a.v_scale = fp8 ? cache->v_scale : 1.0f;
+  const double log2e = 1.4426950408889634;
+  a.qk_scale_log2 = (float)((double)scale * log2e * (fp8 ? (double)cache->k_scale : 1.0));
+  a.q = q;
+  a.out = out;
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  return a;
+}
+
+// Shared-prefix decode: the piece region sized for 16-column prefix slots,
+// then the plan (shared lengths, starts, slot descriptors) and the prefix
+// partials.
+struct SharedLayout {
+  WsLayout w;
+  size_t lcp, start, desc, pm, pl, po, total;
+  int blocks_pre, blocks_suf, g;
+};
+
+pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dtype q_dtype,
+                        SharedLayout* L) {
+  pa_status st = check_cache(c, false);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0) return PA_ERR_INVALID_ARG;
+  if (c->num_kv_heads > 65535 || num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
+  int g = 0;
+  st = decode_supported(c, num_q_heads, q_dtype, &g);
+  if (st != PA_OK) return st;
+  if (!pa::mfma_supported((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs) || g > 8)
+    return PA_ERR_UNSUPPORTED;
+  L->g = g;
+  L->blocks_pre = pa::sk_blocks_shared((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs, 1);
+  L->blocks_suf = pa::sk_blocks_shared((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs, 2);
+  const int bmax = std::max(L->blocks_pre, L->blocks_suf);
+  const size_t rows = pa::sk_slots(bmax, num_seqs, c->num_kv_heads) * 16;
+  L->w = ws_layout(rows, c->head_dim, (size_t)bmax * 4);
+  const size_t S = (size_t)num_seqs, R = S * (size_t)num_q_heads;
+  L->lcp = L->w.total;
+  L->start = L->lcp + align256(S * 4);
+  L->desc = L->start + align256(S * 4);
+  L->pm = L->desc + align256(S * 16);
+  L->pl = L->pm + align256(R * 4);
+  L->po = L->pl + align256(R * 4);
+  L->total = L->po + align256(R * (size_t)c->head_dim * 4);
+  return PA_OK;
+}
+
 pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const void* q,
                       pa_dtype q_dtype, void* out, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens,
@@ -201,29 +269,8 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
       return PA_ERR_WORKSPACE;
   }
 
-  DecodeParams a;
-  memset(&a, 0, sizeof(a));
-  a.k_pool = cache->k;
-  a.v_pool = cache->v;
-  a.block_stride = cache->block_stride;
-  a.layer_offset = (int64_t)layer * cache->layer_stride;
-  a.num_blocks = cache->num_blocks;
-  a.block_size = cache->block_size;
-  a.log2_block_size = ilog2(cache->block_size);
-  a.head_dim = cache->head_dim;
-  const bool fp8 = cache->dtype == PA_FP8_E4M3;
-  a.v_scale = fp8 ? cache->v_scale : 1.0f;
-  const double log2e = 1.4426950408889634;
-  a.qk_scale_log2 = (float)((double)scale * log2e * (fp8 ? (double)cache->k_scale : 1.0));
-  a.q = q;
-  a.out = out;
-  a.block_tables = block_tables;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.context_lens = context_lens;
-  a.max_context_len = max_context_len;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = cache->num_kv_heads;
+  DecodeParams a = decode_params(cache, layer, q, out, block_tables, max_blocks_per_seq,
+                                 context_lens, max_context_len, num_seqs, num_q_heads, scale);
   a.part_tokens = plan.part_tokens;
   a.num_parts = plan.num_parts;
   a.team = plan.mfma ? pa::sk_team(cache->num_kv_heads) : 1;
@@ -477,6 +524,65 @@ pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q, pa_d
   return decode_impl(PHASE_BOTH, cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
                      context_lens, max_context_len, num_seqs, num_q_heads, scale, workspace,
                      workspace_bytes, stream);
+}
+
+pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* q,
+                           pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                           float scale, int32_t reuse_plan, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  pa_status st = check_cache(cache, true);
+  if (st != PA_OK) return st;
+  if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || (reuse_plan != 0 && reuse_plan != 1)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !out || !context_lens || (!block_tables && max_blocks_per_seq > 0))
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * cache->block_size < 0) return PA_ERR_INVALID_ARG;
+  SharedLayout L;
+  st = shared_layout(cache, num_seqs, num_q_heads, q_dtype, &L);
+  if (st != PA_OK) return st;
+  if (!aligned(q, 16) || !aligned(out, 4)) return PA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < L.total || !aligned(workspace, 256)) return PA_ERR_WORKSPACE;
+
+  DecodeParams a = decode_params(cache, layer, q, out, block_tables, max_blocks_per_seq,
+                                 context_lens, max_context_len, num_seqs, num_q_heads, scale);
+  a.part_tokens = 16;
+  a.num_parts = 1;
+  a.team = pa::sk_team(cache->num_kv_heads);
+  char* w = reinterpret_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(w + L.w.o);
+  a.ws_m = reinterpret_cast<float*>(w + L.w.m);
+  a.ws_l = reinterpret_cast<float*>(w + L.w.l);
+  a.ws_team = reinterpret_cast<int32_t*>(w + L.w.team);
+  a.share_lcp = reinterpret_cast<int32_t*>(w + L.lcp);
+  a.share_start = reinterpret_cast<int32_t*>(w + L.start);
+  a.share_desc = reinterpret_cast<int32_t*>(w + L.desc);
+  a.pre_m = reinterpret_cast<float*>(w + L.pm);
+  a.pre_l = reinterpret_cast<float*>(w + L.pl);
+  a.pre_o = reinterpret_cast<float*>(w + L.po);
+  const int kv = (int)cache->dtype, qt = (int)q_dtype;
+  if (!reuse_plan && pa::launch_share_plan(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_pre, 1, stream) != hipSuccess ||
+      pa::launch_merge_shared(a, qt, L.g, L.blocks_pre, 1, stream) != hipSuccess ||
+      pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess ||
+      pa::launch_merge_shared(a, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
+size_t pa_decode_shared_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
+                                       int32_t num_q_heads) {
+  if (!cache) return 0;
+  size_t best = 0;
+  const pa_dtype qs[2] = {PA_F16, PA_BF16};
+  for (pa_dtype qd : qs) {
+    SharedLayout L;
+    if (shared_layout(cache, num_seqs, num_q_heads, qd, &L) == PA_OK) best = std::max(best, L.total);
+  }
+  return best;
 }
 
 pa_status pa_decode_attend(const pa_kv_cache* cache, int32_t layer, const void* q,

@@ -1,0 +1,805 @@
+// pa_decode_sk.h — paged decode attention with the grouped-query tile on
+// the gfx950 matrix cores, work split evenly over the resident waves.
+//
+// Same result as the VALU kernel ("Efficient Memory Management for Large
+// Language Model Serving with PagedAttention", kernel paragraph: fetch each
+// block through the block table, score the query group against it, combine
+// with its values; identical to ordinary attention). With G query heads per
+// KV head both products of a 16-token chunk are small dense contractions:
+//   S[16 tokens][G heads] = K[16][D] . Q^T[D][G]   (v_mfma_f32_16x16x32)
+//   O[G heads][D]        += P[G][16] . V[16][D]    (v_mfma_f32_16x16x16)
+// G <= 16 fills the 16 columns of the tile.
+//
+// Work split ("stream-K"): the W resident waves form teams of T waves (T =
+// the largest power of two up to 8 dividing the KV head count). Segments are
+// (sequence, head group of T KV heads), sequence-major, each a run of
+// ceil(context / 16) column chunks; team t takes columns [t*Cc/Wt,
+// (t+1)*Cc/Wt) of the Cc total, wave i of the team the i-th KV head of each
+// group. So every team gets the same amount of work whatever the length mix,
+// and the T waves of a team read the T head slices of the same KV block (one
+// contiguous stretch of the pool) at about the same time, which the memory
+// system serves markedly faster than the same number of scattered slices. A
+// segment cut by range boundaries leaves one partial (running max m, sum l,
+// unnormalised o) per piece and head, stored at slot ((team + segment) * T +
+// i); merge_sk_kernel combines them in team order.
+//
+// Layout facts used (CDNA 16x16xK MFMA, checked on gfx950): lane l holds
+// A[row l%16][k in (l/16)*KL ..], B[k in (l/16)*KL ..][col l%16] and
+// C[rows 4*(l/16) .. +3][col l%16].
+//  * K: lane l loads token l%16, dims 32c + 8(l/16) .. +8 of step c: the A
+//    operand of the score MFMA straight from memory.
+//  * The score tile comes out as lane l = (tokens 4(l/16)..+3, head l%16),
+//    exactly the A-operand layout of the P.V MFMA: probabilities never leave
+//    their lane.
+//  * V: lane (g, n) loads the slice [VPL*n, +VPL) of tokens 4g..4g+3 (whole
+//    256-byte rows per load instruction); P.V MFMA m uses output column n for
+//    dim VPL*n + m and takes element m of the four vectors (two byte permutes).
+//  * Online softmax with a lazily moved reference maximum per head: it moves
+//    (exact cross-lane max, rescale) only when a score exceeds it by more than
+//    2^TAU, so probabilities stay <= 2^8 and most chunks need no cross-lane
+//    traffic.
+//  * Block ids come from a 64-entry window of the block table held in one
+//    register (lane i = entry i), read with readlane / a lane shuffle.
+//  * Workgroups are dealt to the 8 XCDs round-robin; team ranges are assigned
+//    so that each XCD works through one contiguous stretch of sequences.
+//  * Each loaded chunk travels with a descriptor (segment, chunk, piece
+//    boundaries), so pieces of any length, down to one chunk, are handled
+//    while the next chunk is already in flight.
+//
+// Shared prefixes ("Efficient Memory Management for Large Language Model
+// Serving with PagedAttention", sampling paragraph: parallel samples share
+// the prompt's blocks; "Continuous Batching and PagedAttention", section
+// "Sharing, the part that goes beyond fixing what broke") are read once per
+// up to 16/G sequences instead of once per sequence, in two passes of the
+// same kernel:
+//  * M_PREFIX: a segment is a slot of up to 16/G consecutive sequences
+//    whose tables share the prefix blocks; their queries fill the 16 tile
+//    columns side by side (column c: sequence first + c/G, head c%G), so
+//    each K/V chunk of the prefix is loaded once for all of them. The result
+//    is an unnormalised partial (m, l, o) per sequence and head.
+//  * M_SUFFIX: each sequence's segment starts after its shared prefix, and
+//    the piece holding its first chunk continues from the prefix's partial,
+//    so the usual finish / merge produce the full result.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_mfma.h"
+
+namespace pa {
+namespace {
+
+constexpr int NWM = 4;          // waves per workgroup
+constexpr int CH = 16;          // tokens per chunk
+constexpr int NXCD = 8;         // XCDs of an MI355X
+
+// Chunks of a sequence: 0 when its context is empty or invalid (those rows
+// are written by the merge kernel).
+__device__ __forceinline__ int seq_chunks(const DecodeParams& a, int ctx) {
+  if (ctx <= 0 || ctx > a.max_context_len) return 0;
+  const int64_t nb = ((int64_t)ctx + a.block_size - 1) >> a.log2_block_size;
+  if (nb > a.max_blocks_per_seq) return 0;
+  return (ctx + CH - 1) / CH;
+}
+
+// Team ranges. The W resident waves form Wt = W / T teams of T consecutive
+// (XCD-contiguous) waves, one KV head of the group per wave; team t takes
+// columns [t*Cc/Wt, (t+1)*Cc/Wt) of the Cc total.
+__device__ __forceinline__ int64_t team_begin(int64_t t, int64_t Cc, int64_t Wt) {
+  return t * Cc / Wt;
+}
+
+// Team whose range holds column c (the last team starting at or before c).
+__device__ __forceinline__ int64_t team_of(int64_t c, int64_t Cc, int64_t Wt) {
+  return ((c + 1) * Wt - 1) / Cc;
+}
+
+// Dynamic LDS of the attention kernel: prefix sums, the shared-prefix modes'
+// per-segment word, and last-chunk lengths.
+inline size_t sk_lds_bytes(int num_seqs, int mode) {
+  return (size_t)(num_seqs + 1) * sizeof(int) + (mode ? (size_t)num_seqs * sizeof(uint32_t) : 0) +
+         (((size_t)num_seqs + 3) & ~(size_t)3);
+}
+
+}  // namespace
+
+// Decode modes (see the head of this file): whole contexts, shared prefixes
+// of several sequences side by side, the rest of each context after its
+// shared prefix.
+constexpr int M_PLAIN = 0, M_PREFIX = 1, M_SUFFIX = 2;
+
+// Occupancy: FP8 pools and D = 64 fit 3 waves per SIMD without spilling;
+// 16-bit pools at D = 128 run at 2.
+template <Ty KV, int D, int G>
+constexpr int sk_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
+
+template <Ty KV, Ty QT, int D, int G, int MODE>
+__global__ void __launch_bounds__(NWM * 64)
+__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G>())))
+attend_sk_kernel(const DecodeParams a) {
+  static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
+  static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
+  static_assert(MODE == M_PLAIN || MODE == M_PREFIX || MODE == M_SUFFIX, "mode");
+  constexpr int GC = MODE == M_PREFIX ? 16 : G;   // tile columns holding queries
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int EB = TyInfo<KV>::bytes;
+  constexpr int KS = D / 32;              // score MFMA steps
+  constexpr int VPL = D / 16;             // value elements per lane per token = P.V MFMAs
+  constexpr int KDW = 8 * EB / 4;         // raw K dwords per lane per step
+  constexpr int VDW = VPL * EB / 4;       // raw V dwords per lane per token
+  // K loads: whole 128-byte lines where rows have them (see KLayout)
+  constexpr bool KFULL = KLayout<D, EB>::FULL;
+  constexpr int KR = KLayout<D, EB>::KR;           // K loads per chunk
+  constexpr int KW = KLayout<D, EB>::KW;           // dwords per lane per K load
+  auto kdim = [](int k, int a) { return kdim_t<D, EB>(k, a); };
+
+  // [num_seqs + 1] chunk prefix sums; in the shared-prefix modes [num_seqs]
+  // words (M_PREFIX: first sequence | sequences << 16 of the slot; M_SUFFIX:
+  // the first chunk after the shared prefix); then [num_seqs] bytes: tokens
+  // in each segment's last chunk (1..16), so a segment spans 16 (chunks - 1)
+  // + tail tokens
+  extern __shared__ int s_cum[];
+  // per wave: the q B-operand of the piece being processed, [step][lane]
+  __shared__ uint4 s_q[NWM][KS][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;                // row group
+  const int n = lane & 15;                // column: head (scores) / dim slice (values)
+  const int S = a.num_seqs;
+  const int T = a.team;                   // waves per team = KV heads per head group
+  const int HG = a.num_kv_heads / T;      // head groups
+  uint32_t* const s_aux = reinterpret_cast<uint32_t*>(s_cum + S + 1);
+  uint8_t* const s_tail = reinterpret_cast<uint8_t*>(s_cum + S + 1 + (MODE != M_PLAIN ? S : 0));
+
+  // ---- chunk prefix sums over sequences (every workgroup, in LDS) ---------
+  {
+    int carry = 0;
+    for (int base = 0; base < S; base += NWM * 64) {
+      const int s = base + tid;
+      int v = 0;
+      if (s < S) {
+        if constexpr (MODE == M_PREFIX) {
+          // slot s: its sequences and the prefix they share (a multiple of
+          // 16); a descriptor that does not fit the batch and table is idle
+          const int4 sd = reinterpret_cast<const int4*>(a.share_desc)[s];
+          const bool fits = sd.y >= 1 && sd.y <= 16 / G && sd.x >= 0 && sd.x + sd.y <= S &&
+                            sd.z > 0 && seq_chunks(a, sd.z) > 0 && (sd.z & (CH - 1)) == 0;
+          v = fits ? sd.z / CH : 0;
+          s_aux[s] = fits ? (uint32_t)sd.x | ((uint32_t)sd.y << 16) : 0u;
+          s_tail[s] = (uint8_t)(v ? CH : 0);
+        } else {
+          const int ctx = a.context_lens[s];
+          const bool ok = seq_chunks(a, ctx) > 0;
+          int st0 = 0;                              // tokens already covered by a prefix
+          if constexpr (MODE == M_SUFFIX) {
+            st0 = ok ? a.share_start[s] : 0;
+            if (st0 < 0 || st0 > ctx || (st0 & (CH - 1))) st0 = 0;
+            s_aux[s] = (uint32_t)(st0 / CH);
+          }
+          v = ok ? (ctx - st0 + CH - 1) / CH : 0;
+          s_tail[s] = (uint8_t)(v ? ctx - st0 - CH * (v - 1) : 0);
+        }
+      }
+      // inclusive scan inside the workgroup: wave scan, then across waves
+      int x = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      __shared__ int s_wsum[NWM];
+      if (lane == 63) s_wsum[wave] = x;
+      __syncthreads();
+      int before = carry;
+      for (int w = 0; w < wave; ++w) before += s_wsum[w];
+      if (s < S) s_cum[s] = before + x - v;                   // exclusive
+      int tot = 0;
+      for (int w = 0; w < NWM; ++w) tot += s_wsum[w];
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) s_cum[S] = carry;
+    __syncthreads();
+  }
+  // rows of sequences with nothing to attend to: zeros for an empty context,
+  // NaN for an invalid one (negative, beyond max_context_len or the table);
+  // in M_SUFFIX a context that is all shared prefix takes the prefix's
+  // partial, normalised
+  if constexpr (MODE != M_PREFIX) {
+    for (int s = blockIdx.x; s < S; s += gridDim.x) {
+      if (s_cum[s + 1] == s_cum[s]) {
+        const int64_t base = (int64_t)s * a.num_q_heads * D;
+        if (MODE == M_SUFFIX && s_aux[s] > 0) {
+          for (int e = tid; e < a.num_q_heads * D; e += NWM * 64)
+            store_out<QT>(a.out, base + e,
+                          a.pre_o[base + e] * (a.v_scale / a.pre_l[(int64_t)s * a.num_q_heads + e / D]));
+        } else {
+          const float fill = a.context_lens[s] == 0 ? 0.f : __builtin_nanf("");
+          for (int e = tid; e < a.num_q_heads * D; e += NWM * 64) store_out<QT>(a.out, base + e, fill);
+        }
+      }
+    }
+  }
+  const int64_t CS = __builtin_amdgcn_readfirstlane(s_cum[S]);   // chunks per KV head
+  const int64_t Cc = CS * HG;                                   // column chunks
+  // (Cc == 0: every team's range is empty; each still records "nothing to
+  // merge" below, so the merge never reads a stale descriptor)
+  // XCD-contiguous wave numbering: workgroup b runs on XCD b % 8; give each
+  // XCD one contiguous stretch of the column stream (gridDim.x is a multiple
+  // of 8, and T divides the 8 waves of a workgroup pair)
+  const int per_xcd = gridDim.x / NXCD;
+  const int vb = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  const int64_t w = (int64_t)vb * NWM + wave;
+  const int64_t Wt = (int64_t)gridDim.x * NWM / T;              // teams
+  const int64_t team = w / T;
+  const int ti = (int)(w - team * T);                           // KV head within the group
+
+  const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
+  const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
+  const int lg = a.log2_block_size;
+  const int bmask = a.block_size - 1;
+  const bool big_blocks = a.block_size >= CH;                   // one block per chunk
+  const float qk_scale = a.qk_scale_log2;
+
+  // ---- three-stage pipeline over this wave's ranges: the index stage walks
+  // the column stream and fetches the block ids of chunk i+2, the load stage
+  // issues the K/V loads of chunk i+1, the compute stage processes chunk i.
+  // Segment = (sequence, head group), sequence-major; this wave's KV head in
+  // it is hg * T + ti.
+  struct Seg {
+    int seq, hg, nc, ctx;           // ctx: the segment's end, as a token position
+    int x;                          // M_PREFIX: slot word; M_SUFFIX: first chunk; else 0
+  };
+  // flags of a chunk in flight
+  constexpr int F_VALID = 1;        // a real chunk (else a placeholder past the wave's last)
+  constexpr int F_FIRST = 2;        // first chunk of a piece
+  constexpr int F_LAST = 4;         // last chunk of a piece
+  constexpr int F_BAD = 8;          // a bad block id was seen in the piece (set at its last chunk)
+  struct Desc {
+    int seq, hg, nc, ctx, j;        // segment and chunk (j: position / 16)
+    int x;                          // Seg::x
+    int f;                          // F_* flags
+  };
+  auto first_chunk = [](int x) { return MODE == M_SUFFIX ? x : 0; };
+  auto seg_at = [&](int64_t cg, int& j) __attribute__((always_inline)) -> Seg {     // segment holding column chunk cg
+    int lo = 0, hi = S - 1;                          // last s with s_cum[s] * HG <= cg
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)__builtin_amdgcn_readfirstlane(s_cum[mid]) * HG <= cg) lo = mid; else hi = mid - 1;
+    }
+    Seg sg;
+    sg.seq = lo;
+    sg.nc = __builtin_amdgcn_readfirstlane(s_cum[lo + 1] - s_cum[lo]);
+    const int64_t rel = cg - (int64_t)__builtin_amdgcn_readfirstlane(s_cum[lo]) * HG;
+    sg.hg = (int)(rel / sg.nc);
+    j = (int)(rel - (int64_t)sg.hg * sg.nc);
+    sg.x = MODE != M_PLAIN ? (int)__builtin_amdgcn_readfirstlane(s_aux[lo]) : 0;
+    sg.ctx = CH * (first_chunk(sg.x) + sg.nc - 1) + __builtin_amdgcn_readfirstlane(s_tail[lo]);
+    return sg;
+  };
+
+  // -- index stage state: next column ic of the team's range [.., ie)
+  int64_t ic = team_begin(team, Cc, Wt);
+  const int64_t ie = team_begin(team + 1, Cc, Wt);
+  bool iact = ic < ie;                               // the index stage has chunks left
+  if (ti == 0) {
+    // merge descriptor of the team: the segment its range ends in, when that
+    // segment starts in this range and continues past it: {last team it
+    // reaches, sequence, head group, Cc when some team ranges are empty (Cc <
+    // Wt) else 0}; else {-1}
+    int4 md = make_int4(-1, 0, 0, 0);
+    if (iact) {
+      int j;
+      const Seg sg = seg_at(ie - 1, j);
+      const int64_t s0 = ie - 1 - j;                 // the segment's first column
+      if (s0 >= ic && s0 + sg.nc > ie)
+        md = make_int4((int)team_of(s0 + sg.nc - 1, Cc, Wt), sg.seq, sg.hg, Cc < Wt ? (int)Cc : 0);
+    }
+    if (lane == 0) reinterpret_cast<int4*>(a.ws_team)[team] = md;
+  }
+  if (!iact) return;
+  int ij = 0;
+  Seg is = seg_at(ic, ij);
+  bool ifirst = true;                                // next indexed chunk starts a piece
+
+  // Descriptor and block ids of the index stage's chunk; then advance. Lane
+  // i fetches the id of the chunk's i-th block (lanes past its last block
+  // repeat the last one); out-of-context entries are never read. Once the
+  // wave's chunks are exhausted it yields placeholders and repeats its last
+  // (in-bounds) id fetch, so every pipeline step issues the same loads.
+  const int32_t* irow = a.block_tables;              // table row of the last indexed chunk
+  int ifb = 0, ilb = 0;                              // its first and last block
+  auto index_chunk = [&](Desc& d, int& idr) __attribute__((always_inline)) {
+    d.f = 0;
+    d.x = 0;
+    if (iact) {
+      const int cb = (first_chunk(is.x) + ij) * CH;
+      ifb = cb >> lg;
+      ilb = (min(cb + CH, is.ctx) - 1) >> lg;
+      // M_PREFIX: the slot's first sequence's table (its sequences share the
+      // prefix blocks)
+      const int trow = MODE == M_PREFIX ? (is.x & 0xffff) : is.seq;
+      irow = a.block_tables + (int64_t)trow * a.max_blocks_per_seq;
+      d.seq = is.seq;
+      d.hg = is.hg;
+      d.nc = is.nc;
+      d.ctx = is.ctx;
+      d.j = first_chunk(is.x) + ij;
+      d.x = is.x;
+      ++ic;
+      ++ij;
+      const bool seg_end = ij == is.nc;
+      const bool rng_end = ic == ie;
+      d.f = F_VALID | (ifirst ? F_FIRST : 0) | ((seg_end || rng_end) ? F_LAST : 0);
+      ifirst = seg_end || rng_end;
+      if (rng_end) {
+        iact = false;
+      } else if (seg_end) {
+        if (is.hg + 1 < HG) {
+          ++is.hg;
+        } else {
+          is = seg_at(ic, ij);
+        }
+        ij = 0;
+      }
+    }
+    idr = irow[min(ifb + lane, ilb)];
+  };
+
+  // q of this wave's KV head in chunk d's segment as the B operand (lane l:
+  // head l%16, dims 32k + 8(l/16) .. +8), fetched into qn with a piece's
+  // first chunk and put into LDS at the start of the next pipeline step,
+  // after the piece before it has been processed. Columns past the G heads
+  // repeat a real head's row: their scores are masked out. M_PREFIX: column
+  // l%16 is head (l%16)%G of the slot's sequence (l%16)/G.
+  uint32_t qn[KS][4];
+  bool qpend = false;
+  auto load_q = [&](const Desc& d) __attribute__((always_inline)) {
+    if ((d.f & (F_VALID | F_FIRST)) == (F_VALID | F_FIRST)) {
+      int qseq = d.seq;
+      if constexpr (MODE == M_PREFIX) qseq = (d.x & 0xffff) + min(n / G, (d.x >> 16) - 1);
+      const int64_t row = ((int64_t)qseq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G + (n % G)) * D;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim(k, g)) >> 1), qn[k]);
+      qpend = true;
+    }
+  };
+  auto flush_q = [&]() __attribute__((always_inline)) {
+    if (qpend) {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) s_q[wave][k][lane] = make_uint4(qn[k][0], qn[k][1], qn[k][2], qn[k][3]);
+      qpend = false;
+    }
+  };
+
+  // -- load stage: issue the K/V loads of chunk d (a placeholder reloads
+  // the start of the pool)
+  bool lbad = false;                                 // bad block id seen in the load piece
+  auto load_chunk = [&](Desc& d, int idr, uint32_t (&kr)[KR][KW],
+                        uint32_t (&vr)[4][VDW]) __attribute__((always_inline)) {
+    const bool ok = d.f & F_VALID;
+    const int ctx = ok ? d.ctx : 1;
+    const int cb = ok ? d.j * CH : 0;
+    const int fb = cb >> lg;
+    const bool badl = idr < 0 || idr >= a.num_blocks;
+    const bool bad = __any(badl);
+    const int idv = (badl || !ok) ? 0 : idr;
+    const int64_t head_off = ok ? a.layer_offset + (int64_t)(d.hg * T + ti) * a.block_size * D : 0;
+    auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {          // element of token t (< ctx), dim 0
+      t = min(t, ctx - 1);
+      const int id = big_blocks ? __builtin_amdgcn_readfirstlane(idv) : __shfl(idv, (t >> lg) - fb);
+      return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
+    };
+    int64_t ek[KFULL ? 2 : 1], ev[4];
+    if (big_blocks) {
+      const int64_t base = elem_of(cb);                      // one block per chunk
+      if constexpr (KFULL) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          ek[hf] = base + (int64_t)min(k_load_row<D, EB>(hf, lane), ctx - 1 - cb) * D + k_load_col<D, EB>(0, lane);
+      } else {
+        ek[0] = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
+    } else {
+      if constexpr (KFULL) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) ek[hf] = elem_of(cb + k_load_row<D, EB>(hf, lane)) + k_load_col<D, EB>(0, lane);
+      } else {
+        ek[0] = elem_of(cb + n) + 8 * g;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
+    }
+    if constexpr (KFULL) {
+#pragma unroll
+      for (int u = 0; u < KR; ++u) ld<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+    if (ok) {
+      lbad = lbad || bad;
+      if (lbad && (d.f & F_LAST)) d.f |= F_BAD;
+      if (d.f & F_LAST) lbad = false;
+    }
+  };
+
+  // ---- compute stage state of the current piece
+  int pj0 = 0;                                       // first chunk of the piece
+  f32x4_t acc[VPL];
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m_ref = -__builtin_inff();                   // reference max of head n (log2 units)
+  float l_sum = 0.f;                                 // this lane's probability sum (head n)
+
+  // Write the piece that ends with chunk d (final rows or a partial) and
+  // reset the state.
+  auto finish_piece = [&](const Desc& d) __attribute__((always_inline)) {
+    const bool bad = d.f & F_BAD;
+    float lt = l_sum + __shfl_xor(l_sum, 16);
+    lt += __shfl_xor(lt, 32);
+    const int j0 = first_chunk(d.x);
+    const bool whole = (pj0 == j0) && (d.j + 1 == j0 + d.nc);
+    const int kvh = d.hg * T + ti;
+    const int64_t out_row0 = ((int64_t)d.seq * a.num_q_heads + (int64_t)kvh * G) * D;
+    const int64_t cseg = (int64_t)d.seq * HG + d.hg;
+    const int ncol = MODE == M_PREFIX ? G * (d.x >> 16) : G;   // columns holding queries
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * g + r;                      // accumulator row = column (head)
+      const float lh = __shfl(lt, h);
+      const float mh = __shfl(m_ref, h);
+      if (h < ncol) {
+        if (MODE == M_PREFIX && whole) {
+          // the prefix's partial of sequence first + h/G, head kvh*G + h%G
+          const int64_t pr = (int64_t)((d.x & 0xffff) + h / G) * a.num_q_heads + (int64_t)kvh * G + h % G;
+          float* po = a.pre_o + pr * D + VPL * n;
+#pragma unroll
+          for (int m = 0; m < VPL; ++m) po[m] = bad ? __builtin_nanf("") : acc[m][r];
+          if (n == 0) {
+            a.pre_m[pr] = bad ? 0.f : mh;
+            a.pre_l[pr] = bad ? __builtin_nanf("") : lh;
+          }
+        } else if (whole) {
+          const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
+          const int64_t o = out_row0 + (int64_t)h * D + VPL * n;
+#pragma unroll
+          for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm);
+        } else {
+          const int64_t slot = ((team + cseg) * T + ti) * GC + h;
+          float* wo = a.ws_o + slot * D + VPL * n;
+#pragma unroll
+          for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[m][r];
+          if (n == 0) {
+            a.ws_m[slot] = bad ? 0.f : mh;
+            a.ws_l[slot] = bad ? __builtin_nanf("") : lh;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    m_ref = -__builtin_inff();
+    l_sum = 0.f;
+  };
+
+  auto process_chunk = [&](const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW],
+                           const Desc& d) __attribute__((always_inline)) {
+    if (d.f & F_FIRST) pj0 = d.j;
+    if constexpr (MODE == M_SUFFIX) {
+      if ((d.f & F_FIRST) && d.x > 0 && d.j == d.x) {
+        // the piece opening the sequence's own tokens continues from the
+        // shared prefix's partial (state layout of softmax_pv)
+        const int64_t r0 = (int64_t)d.seq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G;
+        m_ref = n < G ? a.pre_m[r0 + n] : -__builtin_inff();
+        l_sum = (n < G && g == 0) ? a.pre_l[r0 + n] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (4 * g + r < G) {
+            const float* po = a.pre_o + (r0 + 4 * g + r) * D + VPL * n;
+#pragma unroll
+            for (int m = 0; m < VPL; ++m) acc[m][r] = po[m];
+          }
+        }
+      }
+    }
+    const int ctx = d.ctx;
+    const int cb = d.j * CH;
+    const f32x4_t s = chunk_scores<KV, QT, D>(kr, [&](int k) { return s_q[wave][k][lane]; }, lane);
+    const bool tail = cb + CH > ctx;
+    float z[4];
+    bool live[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = (n < (MODE == M_PREFIX ? G * (d.x >> 16) : G)) && (cb + 4 * g + r < ctx);
+      z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
+      live[r] = !tail || cb + 4 * g + r < ctx;
+    }
+    chunk_softmax_pv<KV, QT, D>(z, vr, live, acc, m_ref, l_sum, lane);
+    if (d.f & F_LAST) finish_piece(d);
+  };
+
+  // ---- the pipeline. Chunks alternate between buffers A and B; a chunk's
+  // block ids live in the id register of its buffer from indexing to
+  // loading. Each step: q of the previous step's new piece goes to LDS; q of
+  // chunk i+1 is fetched if it starts a piece (the only conditional load,
+  // issued first so that it cannot shorten the waits that follow); the ids
+  // of chunk i+2 and the K/V of chunk i+1 are fetched; chunk i is processed.
+  // The waits before processing leave every load of the step in flight.
+  uint32_t kA[KR][KW], vA[4][VDW], kB[KR][KW], vB[4][VDW];
+  Desc dA, dB;                                       // chunk in (or bound for) each buffer
+  int iA = 0, iB = 0;
+  index_chunk(dA, iA);
+  load_q(dA);
+  index_chunk(dB, iB);
+  load_chunk(dA, iA, kA, vA);
+  while (true) {
+    Desc dn;
+    flush_q();
+    load_q(dB);
+    index_chunk(dn, iA);
+    load_chunk(dB, iB, kB, vB);
+    process_chunk(kA, vA, dA);
+    if (!(dB.f & F_VALID)) break;
+    dA = dn;
+    flush_q();
+    load_q(dA);
+    index_chunk(dn, iB);
+    load_chunk(dA, iA, kA, vA);
+    process_chunk(kB, vB, dB);
+    if (!(dA.f & F_VALID)) break;
+    dB = dn;
+  }
+}
+
+// Merge of segments cut by team range boundaries: M = max_p m_p,
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p. Workgroup (t, i)
+// merges KV head i of the group of the segment recorded by team t (if any),
+// over its pieces from teams t .. r1. Threads form PG groups, each covering
+// all GC x D outputs (DPT dims per thread) over every PG-th piece with a
+// running (online) combination; the groups are combined in LDS. M_PREFIX
+// writes the combined partial (M, L, O) of each of the slot's sequences
+// instead of the normalised output.
+template <Ty QT, int D, int G, int MODE>
+__global__ void __launch_bounds__(256)
+merge_sk_kernel(const DecodeParams a, int64_t W) {
+  constexpr int GC = MODE == M_PREFIX ? 16 : G;        // tile columns holding queries
+  constexpr int GD = GC * D;
+  constexpr int DPT = GD >= 1024 ? 16 : (GD >= 512 ? 8 : 4);   // dims per thread
+  constexpr int NV4 = DPT / 4;
+  constexpr int TPG = GD / DPT;                        // threads per group
+  static_assert(TPG <= 256 && 256 % TPG == 0, "group size");
+  constexpr int PG = 256 / TPG;                        // piece groups
+  __shared__ float s_m[PG][GC], s_l[PG][GC];
+  __shared__ float s_o[PG > 1 ? PG : 1][GD];
+
+  const int64_t t0 = blockIdx.x;
+  const int ti = blockIdx.y;
+  const int4 md = reinterpret_cast<const int4*>(a.ws_team)[t0];
+  const int64_t t1 = md.x;
+  if (t1 <= t0) return;                                // no segment to merge here
+  const int T = a.team;
+  const int HG = a.num_kv_heads / T;
+  const int64_t Wt = W / T;
+  const int seq = md.y, hg = md.z;
+  const int kvh = hg * T + ti;
+  const int tid = threadIdx.x;
+  const int grp = tid / TPG;
+  const int t = tid - grp * TPG;
+  const int h = t / (D / DPT);
+  const int d0 = (t - h * (D / DPT)) * DPT;
+  const int64_t orow = ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h) * D + d0;
+  const int64_t cseg = (int64_t)seq * HG + hg;
+  const int64_t Cs = md.w;                             // nonzero: some team ranges are empty
+
+  float M = -__builtin_inff(), L = 0.f, O[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) O[e] = 0.f;
+  auto combine = [&](float m, float l, const float4* o) {
+    const float mn = fmaxf(M, m);
+    if (mn == -__builtin_inff()) return;
+    const float f1 = __builtin_amdgcn_exp2f(M - mn);   // 0 when M = -inf
+    const float f2 = __builtin_amdgcn_exp2f(m - mn);
+    L = L * f1 + l * f2;
+#pragma unroll
+    for (int v = 0; v < NV4; ++v) {
+      O[4 * v + 0] = O[4 * v + 0] * f1 + o[v].x * f2;
+      O[4 * v + 1] = O[4 * v + 1] * f1 + o[v].y * f2;
+      O[4 * v + 2] = O[4 * v + 2] * f1 + o[v].z * f2;
+      O[4 * v + 3] = O[4 * v + 3] * f1 + o[v].w * f2;
+    }
+    M = mn;
+  };
+  // pieces of teams t0 + grp, t0 + grp + PG, ...; U loads in flight per group
+  // (every nonempty team in t0 .. t1 holds a piece: the segment covers it)
+  constexpr int U = 4;
+  for (int64_t tb = t0 + grp; tb <= t1; tb += (int64_t)PG * U) {
+    float mv[U], lv[U];
+    float4 ov[U][NV4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tm = tb + (int64_t)u * PG;
+      const bool ok = tm <= t1 && (Cs == 0 || team_begin(tm, Cs, Wt) != team_begin(tm + 1, Cs, Wt));
+      const int64_t slot = ((tm + cseg) * T + ti) * GC + h;
+      mv[u] = ok ? a.ws_m[slot] : -__builtin_inff();
+      lv[u] = ok ? a.ws_l[slot] : 0.f;
+#pragma unroll
+      for (int v = 0; v < NV4; ++v)
+        ov[u][v] = ok ? reinterpret_cast<const float4*>(a.ws_o + slot * D + d0)[v]
+                      : make_float4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) combine(mv[u], lv[u], ov[u]);
+  }
+  if constexpr (PG > 1) {
+    if (d0 == 0) { s_m[grp][h] = M; s_l[grp][h] = L; }
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) s_o[grp][h * D + d0 + e] = O[e];
+    __syncthreads();
+    if (grp != 0) return;
+    M = -__builtin_inff(); L = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) O[e] = 0.f;
+#pragma unroll
+    for (int q = 0; q < PG; ++q)
+      combine(s_m[q][h], s_l[q][h], reinterpret_cast<const float4*>(&s_o[q][h * D + d0]));
+  }
+  if constexpr (MODE == M_PREFIX) {
+    const int4 sd = reinterpret_cast<const int4*>(a.share_desc)[seq];
+    if (h >= G * sd.y) return;                         // column without a query
+    const int64_t pr = (int64_t)(sd.x + h / G) * a.num_q_heads + (int64_t)kvh * G + h % G;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) a.pre_o[pr * D + d0 + e] = O[e];
+    if (d0 == 0) {
+      a.pre_m[pr] = M;
+      a.pre_l[pr] = L;
+    }
+  } else {
+    const float norm = a.v_scale / L;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, O[e] * norm);
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Launch side, templated on the mode. The shared-prefix modes exist for the
+// group sizes the C ABI takes (1, 2, 4, 8).
+template <Ty KV, Ty QT, int D, int G, int MODE>
+static hipError_t sk_launch_t(const DecodeParams& a, int blocks, hipStream_t st) {
+  const size_t lds = sk_lds_bytes(a.num_seqs, MODE);
+  hipLaunchKernelGGL((attend_sk_kernel<KV, QT, D, G, MODE>), dim3(blocks), dim3(NWM * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <Ty KV, Ty QT, int D, int MODE>
+static hipError_t sk_launch_g(const DecodeParams& a, int g, int blocks, hipStream_t st) {
+  switch (g) {
+    case 1: return sk_launch_t<KV, QT, D, 1, MODE>(a, blocks, st);
+    case 2: return sk_launch_t<KV, QT, D, 2, MODE>(a, blocks, st);
+    case 4: return sk_launch_t<KV, QT, D, 4, MODE>(a, blocks, st);
+    case 8: return sk_launch_t<KV, QT, D, 8, MODE>(a, blocks, st);
+    case 16:
+      if constexpr (MODE == M_PLAIN) return sk_launch_t<KV, QT, D, 16, MODE>(a, blocks, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <Ty KV, Ty QT, int MODE>
+static hipError_t sk_launch_d(const DecodeParams& a, int g, int blocks, hipStream_t st) {
+  if (a.head_dim == 64) return sk_launch_g<KV, QT, 64, MODE>(a, g, blocks, st);
+  if (a.head_dim == 128) return sk_launch_g<KV, QT, 128, MODE>(a, g, blocks, st);
+  return hipErrorInvalidValue;
+}
+
+template <int MODE>
+static hipError_t sk_launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
+                                   hipStream_t st) {
+  const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
+  if (kv == Ty::BF16 && q == Ty::BF16) return sk_launch_d<Ty::BF16, Ty::BF16, MODE>(a, g, blocks, st);
+  if (kv == Ty::F16 && q == Ty::F16) return sk_launch_d<Ty::F16, Ty::F16, MODE>(a, g, blocks, st);
+  if (kv == Ty::FP8 && q == Ty::BF16) return sk_launch_d<Ty::FP8, Ty::BF16, MODE>(a, g, blocks, st);
+  if (kv == Ty::FP8 && q == Ty::F16) return sk_launch_d<Ty::FP8, Ty::F16, MODE>(a, g, blocks, st);
+  return hipErrorInvalidValue;
+}
+
+// Workgroups to launch: exactly the number that are resident at once (every
+// wave's range is processed concurrently), a multiple of the XCD count.
+template <Ty KV, Ty QT, int D, int G, int MODE>
+static int sk_blocks_t(int num_seqs) {
+  int dev = 0, cus = 256, per_cu = 0;
+  const size_t lds = sk_lds_bytes(num_seqs, MODE);
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&attend_sk_kernel<KV, QT, D, G, MODE>), NWM * 64,
+            lds) != hipSuccess)
+      per_cu = 0;
+  }
+  // More resident workgroups than the compiled target adds no bandwidth (the
+  // slab reads already keep the memory system full at that occupancy) and
+  // only shortens each wave's range, raising the merge's share of the work.
+  const int target = sk_waves_per_simd<KV, D, G>();
+  if (per_cu <= 0 || per_cu > target) per_cu = target;
+  const int b = cus * per_cu;
+  return b >= NXCD ? b / NXCD * NXCD : NXCD;
+}
+
+template <Ty KV, Ty QT, int D, int MODE>
+static int sk_blocks_g(int g, int num_seqs) {
+  switch (g) {
+    case 1: return sk_blocks_t<KV, QT, D, 1, MODE>(num_seqs);
+    case 2: return sk_blocks_t<KV, QT, D, 2, MODE>(num_seqs);
+    case 4: return sk_blocks_t<KV, QT, D, 4, MODE>(num_seqs);
+    case 8: return sk_blocks_t<KV, QT, D, 8, MODE>(num_seqs);
+    default:
+      if constexpr (MODE == M_PLAIN) return sk_blocks_t<KV, QT, D, 16, MODE>(num_seqs);
+      return 0;
+  }
+}
+
+template <int MODE>
+static int sk_blocks_mode(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {
+  const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
+  auto by_d = [&](auto kvt, auto qt) {
+    constexpr Ty K = decltype(kvt)::value, Q = decltype(qt)::value;
+    return head_dim == 64 ? sk_blocks_g<K, Q, 64, MODE>(g, num_seqs)
+                          : sk_blocks_g<K, Q, 128, MODE>(g, num_seqs);
+  };
+  using BF = std::integral_constant<Ty, Ty::BF16>;
+  using HF = std::integral_constant<Ty, Ty::F16>;
+  using F8 = std::integral_constant<Ty, Ty::FP8>;
+  if (kv == Ty::BF16) return by_d(BF{}, BF{});
+  if (kv == Ty::F16) return by_d(HF{}, HF{});
+  if (q == Ty::F16) return by_d(F8{}, HF{});
+  return by_d(F8{}, BF{});
+}
+
+template <Ty QT, int D, int MODE>
+static hipError_t sk_launch_merge_d(const DecodeParams& a, int64_t W, int g, hipStream_t st) {
+  dim3 grid((unsigned)(W / a.team), (unsigned)a.team);
+  switch (g) {
+    case 1: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 1, MODE>), grid, dim3(256), 0, st, a, W); break;
+    case 2: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 2, MODE>), grid, dim3(256), 0, st, a, W); break;
+    case 4: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 4, MODE>), grid, dim3(256), 0, st, a, W); break;
+    case 8: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 8, MODE>), grid, dim3(256), 0, st, a, W); break;
+    case 16:
+      if constexpr (MODE == M_PLAIN) {
+        hipLaunchKernelGGL((merge_sk_kernel<QT, D, 16, MODE>), grid, dim3(256), 0, st, a, W);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t sk_launch_merge(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st) {
+  const int64_t W = (int64_t)blocks * NWM;
+  auto by_d = [&](auto qt) {
+    constexpr Ty Q = decltype(qt)::value;
+    if (a.head_dim == 64) return sk_launch_merge_d<Q, 64, MODE>(a, W, g, st);
+    if (a.head_dim == 128) return sk_launch_merge_d<Q, 128, MODE>(a, W, g, st);
+    return hipErrorInvalidValue;
+  };
+  switch ((Ty)q_ty) {
+    case Ty::BF16: return by_d(std::integral_constant<Ty, Ty::BF16>{});
+    case Ty::F16: return by_d(std::integral_constant<Ty, Ty::F16>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

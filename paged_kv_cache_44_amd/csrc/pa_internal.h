@@ -40,6 +40,13 @@ struct DecodeParams {
   float* ws_l;               // [num_seqs][num_q_heads][num_parts]
   int32_t team;              // matrix-core path: waves per team (KV heads per head group)
   int32_t* ws_team;          // matrix-core path: merge descriptors, int4 per team
+  // shared-prefix decode (matrix-core path only)
+  int32_t* share_lcp;        // [num_seqs] tokens sequence s shares with s - 1 (from the tables)
+  int32_t* share_start;      // [num_seqs] tokens of the shared prefix each sequence starts after
+  int32_t* share_desc;       // [num_seqs] int4 {first member, members, prefix tokens, 0} per slot
+  float* pre_m;              // [num_seqs][num_q_heads] prefix partials: running max (log2)
+  float* pre_l;              // [num_seqs][num_q_heads] sum of weights
+  float* pre_o;              // [num_seqs][num_q_heads][head_dim] unnormalised output
 };
 
 struct PrefillParams {
@@ -130,6 +137,14 @@ int sk_team(int num_kv_heads);
 hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
                               hipStream_t st);
 hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st);
+// shared-prefix decode: planning (fills share_lcp, share_start, share_desc),
+// then attend / merge in the prefix (mode 1) and suffix (mode 2) passes
+hipError_t launch_share_plan(const DecodeParams& a, int g, hipStream_t st);
+int sk_blocks_shared(int kv_ty, int q_ty, int head_dim, int g, int num_seqs, int mode);
+hipError_t launch_attend_shared(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
+                                int mode, hipStream_t st);
+hipError_t launch_merge_shared(const DecodeParams& a, int q_ty, int g, int blocks, int mode,
+                               hipStream_t st);
 bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g);
 int prefill_tiles(int g, int max_query_len);
 hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,

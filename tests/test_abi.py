@@ -169,3 +169,23 @@ def test_staged_copy_arguments_checked_before_device_work(pa_lib):
     assert run([(0, 1)], dst=dev, src=dev) == B.PA_ERR_UNSUPPORTED
     assert run([(1, 0)], direction=B.PA_COPY_H2D, dst=dev, src=host, nbytes=0) == \
         B.PA_ERR_WORKSPACE
+
+
+def test_shared_decode_arguments(pa_lib):
+    c = _cache()
+    n = pa_lib.pa_decode_shared_workspace_size(ctypes.byref(c), 256, 32)
+    assert n > pa_lib.pa_decode_workspace_size(ctypes.byref(c), 256, 32, 4000)
+    f32 = _cache(dtype=B.PA_F32, dim=64, heads=4)
+    assert pa_lib.pa_decode_shared_workspace_size(ctypes.byref(f32), 8, 4) == 0
+
+    def run(cache=c, q_dtype=B.PA_BF16, reuse=0, ws=FAKE, nbytes=n, hq=32, S=256):
+        return pa_lib.pa_decode_shared(ctypes.byref(cache), 0, FAKE, q_dtype, FAKE, FAKE, 8, FAKE,
+                                       128, S, hq, ctypes.c_float(0.1), reuse, ws, nbytes, None)
+    assert run(S=0) == B.PA_OK
+    assert run(reuse=2) == B.PA_ERR_INVALID_ARG
+    assert run(cache=f32, q_dtype=B.PA_F32, hq=4) == B.PA_ERR_UNSUPPORTED
+    assert run(q_dtype=B.PA_F16) == B.PA_ERR_UNSUPPORTED      # bf16 pool, f16 queries
+    assert run(hq=30) == B.PA_ERR_INVALID_ARG                 # not a multiple of the KV heads
+    assert run(nbytes=n - 256) == B.PA_ERR_WORKSPACE
+    assert run(ws=None) == B.PA_ERR_WORKSPACE
+    assert run(ws=FAKE + 64) == B.PA_ERR_WORKSPACE

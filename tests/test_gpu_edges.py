@@ -467,3 +467,23 @@ def test_worked_example_swap_round_trip_on_device():
     got, _ = _decode_one(st, Bq, q)
     dense = paged.attention(codecs.decode(q, "f32")[0], k, k, wl.scale)
     assert np.max(np.abs(got[0] - dense)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("fill", ["empty", "invalid"])
+def test_batch_with_nothing_to_attend_over_stale_workspace(fill):
+    """Every context empty (zero rows) or invalid (NaN rows): the attention
+    kernel has no chunk to process, yet every team still records that it
+    has nothing to merge, so a workspace holding stale bytes is harmless."""
+    wl = workloads.custom(21, [30, 40, 17], pool_dtype="bf16", q_dtype="bf16", num_q_heads=8,
+                          num_kv_heads=2, head_dim=128, block_size=16)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    ctx = np.zeros(3, np.int32) if fill == "empty" else np.full(3, 5000, np.int32)
+    n = pa.decode_workspace_size(st.cache, 3, 8, 64)
+    ws = torch.full((n,), 0x7f, dtype=torch.uint8, device="cuda")   # descriptors would read "merge"
+    q = codes_to_tensor(wl.q, "bf16")
+    out = pa.decode(st.cache, 0, q, torch.from_numpy(wl.block_tables).cuda(),
+                    torch.from_numpy(ctx).cuda(), 64, 0.1, workspace=ws)
+    torch.cuda.synchronize()
+    got = codecs.decode(tensor_codes(out), "bf16")
+    assert np.all(got == 0) if fill == "empty" else np.all(np.isnan(got))

@@ -400,6 +400,77 @@ def custom(seed: int, ctx, *, pool_dtype: str, q_dtype: str, num_q_heads: int,
     return wl
 
 
+def shared_prefix(seed: int, groups, *, pool_dtype: str, q_dtype: str, num_q_heads: int,
+                  num_kv_heads: int, head_dim: int, block_size: int,
+                  src_dtype: str = None) -> Workload:
+    """Parallel samples of several prompts (the layout of the shared-prefix
+    workload, any geometry). ``groups`` lists (prompt tokens, [private
+    tokens of each sample]); a group's samples are consecutive sequences
+    whose tables name the prompt's blocks. A sample that appends to a
+    partly filled last prompt block first copies it (copy-on-write), so its
+    table names the copy there. Writes run in three phases like
+    :func:`fill_plan` expects: prompts, copies, private tokens."""
+    rng = np.random.default_rng(seed)
+    B = block_size
+    src = src_dtype or (BF16 if pool_dtype == FP8 else pool_dtype)
+    needed = 0
+    for P, priv in groups:
+        nbp = -(-P // B)
+        needed += nbp
+        for n in priv:
+            cow = 1 if (P % B and n > 0) else 0
+            room = (B - P % B) % B if not cow else (B - P % B)
+            needed += cow + -(-max(0, n - room) // B)
+    nblk = _pool_size(needed) + 1
+    perm = rng.permutation(nblk)
+    pos = 0
+
+    def take(n):
+        nonlocal pos
+        out = [int(x) for x in perm[pos:pos + n]]
+        pos += n
+        return out
+
+    placements, ctx, cow_pairs, prompt_slots, priv_slots = [], [], [], [], []
+    for P, priv in groups:
+        pb = take(-(-P // B))
+        prompt_slots.append(_slots_of(pb, P, B))
+        for n in priv:
+            tbl = list(pb)
+            if P % B and n > 0:
+                nb_new = take(1)[0]
+                cow_pairs.append((pb[-1], nb_new))
+                tbl[-1] = nb_new
+            extra = -(-max(0, P + n - len(tbl) * B) // B)
+            tbl += take(extra)
+            placements.append(tbl)
+            ctx.append(P + n)
+            t = np.arange(P, P + n, dtype=np.int64)
+            priv_slots.append(np.asarray(tbl, dtype=np.int64)[t // B] * B + t % B)
+    spare = int(perm[pos]) if pos < nblk else int(perm[0])
+    tables = _tables_from_placement(placements, spare)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    S = len(ctx)
+    q = normal_codes(rng, (S, num_q_heads, head_dim), q_dtype)
+    n0 = sum(P for P, _ in groups)
+    npriv = int(sum(sum(p) for _, p in groups))
+    k = normal_codes(rng, (n0 + npriv, num_kv_heads, head_dim), src)
+    v = normal_codes(rng, (n0 + npriv, num_kv_heads, head_dim), src)
+    slots = np.concatenate(prompt_slots + priv_slots) if n0 + npriv else np.zeros(0, np.int64)
+    wl = Workload(name=f"shared_{seed}", seed=seed, pool_dtype=pool_dtype, src_dtype=src,
+                  q_dtype=q_dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                  head_dim=head_dim, block_size=B, num_blocks=nblk, num_layers=1, layer=0,
+                  scale=float(np.float32(1.0) / np.sqrt(np.float32(head_dim))),
+                  context_lens=ctx, block_tables=tables, q=q, write_k=k, write_v=v,
+                  write_slots=slots, spare_block=spare)
+    wl.extra.update(cow_pairs=np.asarray(cow_pairs, dtype=np.int64).reshape(-1, 2),
+                    num_prefix_tokens_written=n0)
+    if pool_dtype == FP8 and k.shape[0]:
+        wl.k_scale = fp8_scale(k, src)
+        wl.v_scale = fp8_scale(v, src)
+    return wl
+
+
 def make(config: int, **kw) -> Workload:
     return {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}[config](**kw)
 
