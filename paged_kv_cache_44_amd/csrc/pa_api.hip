@@ -206,12 +206,13 @@ DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* 
   return a;
 }
 
-// Shared-prefix decode: the piece region sized for 16-column prefix slots,
-// then the plan (shared lengths, starts, slot descriptors) and the prefix
-// partials.
+// Shared-prefix decode: the suffix pass's pieces and merge descriptors (the
+// usual decode workspace), the prefix pass's pieces (16 columns per slot),
+// the plan (shared lengths, starts, slot records) and the team range of
+// each prefix segment.
 struct SharedLayout {
-  WsLayout w;
-  size_t lcp, start, desc, pm, pl, po, total;
+  WsLayout suf, pre;
+  size_t pre_base, lcp, start, desc, seg, pm, pl, po, total;
   int blocks_pre, blocks_suf, g;
 };
 
@@ -229,14 +230,19 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
   L->g = g;
   L->blocks_pre = pa::sk_blocks_shared((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs, 1);
   L->blocks_suf = pa::sk_blocks_shared((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs, 2);
-  const int bmax = std::max(L->blocks_pre, L->blocks_suf);
-  const size_t rows = pa::sk_slots(bmax, num_seqs, c->num_kv_heads) * 16;
-  L->w = ws_layout(rows, c->head_dim, (size_t)bmax * 4);
-  const size_t S = (size_t)num_seqs, R = S * (size_t)num_q_heads;
-  L->lcp = L->w.total;
+  const int H = c->num_kv_heads;
+  L->suf = ws_layout(pa::sk_slots(L->blocks_suf, num_seqs, H) * g, c->head_dim,
+                     (size_t)L->blocks_suf * 4);
+  L->pre_base = L->suf.total;
+  L->pre = ws_layout(pa::sk_slots(L->blocks_pre, num_seqs, H) * 16, c->head_dim,
+                     (size_t)L->blocks_pre * 4);
+  const size_t S = (size_t)num_seqs;
+  L->lcp = L->pre_base + L->pre.total;
   L->start = L->lcp + align256(S * 4);
   L->desc = L->start + align256(S * 4);
-  L->pm = L->desc + align256(S * 16);
+  L->seg = L->desc + align256(S * 16);
+  const size_t R = S * (size_t)num_q_heads;
+  L->pm = L->seg + align256(S * (size_t)H * 16);
   L->pl = L->pm + align256(R * 4);
   L->po = L->pl + align256(R * 4);
   L->total = L->po + align256(R * (size_t)c->head_dim * 4);
@@ -553,21 +559,35 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   a.num_parts = 1;
   a.team = pa::sk_team(cache->num_kv_heads);
   char* w = reinterpret_cast<char*>(workspace);
-  a.ws_o = reinterpret_cast<float*>(w + L.w.o);
-  a.ws_m = reinterpret_cast<float*>(w + L.w.m);
-  a.ws_l = reinterpret_cast<float*>(w + L.w.l);
-  a.ws_team = reinterpret_cast<int32_t*>(w + L.w.team);
   a.share_lcp = reinterpret_cast<int32_t*>(w + L.lcp);
   a.share_start = reinterpret_cast<int32_t*>(w + L.start);
   a.share_desc = reinterpret_cast<int32_t*>(w + L.desc);
+  a.share_seg = reinterpret_cast<int32_t*>(w + L.seg);
   a.pre_m = reinterpret_cast<float*>(w + L.pm);
   a.pre_l = reinterpret_cast<float*>(w + L.pl);
   a.pre_o = reinterpret_cast<float*>(w + L.po);
+  a.pre_teams = L.blocks_pre * 4 / a.team;
   const int kv = (int)cache->dtype, qt = (int)q_dtype;
   if (!reuse_plan && pa::launch_share_plan(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
-  if (pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_pre, 1, stream) != hipSuccess ||
-      pa::launch_merge_shared(a, qt, L.g, L.blocks_pre, 1, stream) != hipSuccess ||
-      pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess ||
+  // prefix pass: pieces into its own region
+  char* wp = w + L.pre_base;
+  a.ws_o = reinterpret_cast<float*>(wp + L.pre.o);
+  a.ws_m = reinterpret_cast<float*>(wp + L.pre.m);
+  a.ws_l = reinterpret_cast<float*>(wp + L.pre.l);
+  a.ws_team = reinterpret_cast<int32_t*>(wp + L.pre.team);
+  if (pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_pre, 1, stream) != hipSuccess)
+    return PA_ERR_HIP;
+  // the prefix pieces, combined per sequence and head
+  a.pre_ws_o = a.ws_o;
+  a.pre_ws_m = a.ws_m;
+  a.pre_ws_l = a.ws_l;
+  if (pa::launch_prefix_combine(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
+  // suffix pass: continues from the combined partials, merges its own pieces
+  a.ws_o = reinterpret_cast<float*>(w + L.suf.o);
+  a.ws_m = reinterpret_cast<float*>(w + L.suf.m);
+  a.ws_l = reinterpret_cast<float*>(w + L.suf.l);
+  a.ws_team = reinterpret_cast<int32_t*>(w + L.suf.team);
+  if (pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess ||
       pa::launch_merge_shared(a, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;

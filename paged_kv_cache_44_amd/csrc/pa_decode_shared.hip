@@ -16,9 +16,10 @@
 //     minimum of those lengths (the common prefix of all its members),
 //     rounded down to a multiple of 16. Each member starts its own pass
 //     after it (share_start), and each group of up to 16/G consecutive
-//     members is one prefix slot, kept at its first member's index
-//     (share_desc).
-// Then the matrix-core kernel's prefix pass and suffix pass (pa_decode_sk.h).
+//     members is one prefix slot, kept at its first member's index; every
+//     member records its slot (share_desc).
+// Then the matrix-core kernel's prefix pass, prefix_combine_kernel, and the
+// suffix pass (pa_decode_sk.h).
 #include "pa_decode_sk.h"
 
 namespace pa {
@@ -63,26 +64,33 @@ __global__ void __launch_bounds__(256) share_lcp_kernel(const DecodeParams a) {
 constexpr int PT = 1024;                         // planning threads
 constexpr int NOPEN = 0x7fffffff;
 
-// Inclusive scans of one value per thread across the workgroup, through
-// LDS: forward max (over threads 0..t) and backward min (over t..PT-1).
-__device__ __forceinline__ int scan_max_fwd(int v, int* s_buf) {
-  const int t = threadIdx.x;
-  for (int o = 1; o < PT; o <<= 1) {
-    s_buf[t] = v;
-    __syncthreads();
-    if (t >= o) v = max(v, s_buf[t - o]);
-    __syncthreads();
+// Inclusive scans of one value per thread across the workgroup: forward max
+// (over threads 0..t) and backward min (over t..PT-1). Each wave scans with
+// lane shuffles; the waves' totals meet in LDS once.
+__device__ __forceinline__ int scan_max_fwd(int v, int* s_wave) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v = max(v, y);
   }
+  if (lane == 63) s_wave[wv] = v;
+  __syncthreads();
+  for (int u = 0; u < wv; ++u) v = max(v, s_wave[u]);
+  __syncthreads();
   return v;
 }
-__device__ __forceinline__ int scan_min_bwd(int v, int* s_buf) {
-  const int t = threadIdx.x;
-  for (int o = 1; o < PT; o <<= 1) {
-    s_buf[t] = v;
-    __syncthreads();
-    if (t + o < PT) v = min(v, s_buf[t + o]);
-    __syncthreads();
+__device__ __forceinline__ int scan_min_bwd(int v, int* s_wave) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(v, o);
+    if (lane + o < 64) v = min(v, y);
   }
+  if (lane == 0) s_wave[wv] = v;
+  __syncthreads();
+  for (int u = wv + 1; u < PT / 64; ++u) v = min(v, s_wave[u]);
+  __syncthreads();
   return v;
 }
 
@@ -92,6 +100,7 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
   constexpr int E = (PA_SK_MAX_SEQS + PT - 1) / PT;   // sequences per thread at most
   extern __shared__ int s_min[];                 // [num_seqs]: run minimum, at its first member
   __shared__ int s_buf[PT];
+  __shared__ int s_wave[PT / 64];
   const int S = a.num_seqs;
   const int t = threadIdx.x;
   const int per = (S + PT - 1) / PT;             // <= E
@@ -112,8 +121,8 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
     }
   }
   // last opening before this thread's range, first one after it
-  const int upto = scan_max_fwd(last_open, s_buf);
-  const int from = scan_min_bwd(first_open, s_buf);
+  const int upto = scan_max_fwd(last_open, s_wave);
+  const int from = scan_min_bwd(first_open, s_wave);
   s_buf[t] = upto;
   __syncthreads();
   const int open_before = t > 0 ? s_buf[t - 1] : -1;
@@ -150,13 +159,105 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
     const int m = s_min[L];
     const int pre = (end[i] - L >= 2 && m >= 16 && m != NOPEN) ? (m & ~15) : 0;
     a.share_start[s] = pre;
-    int4 d = make_int4(s, 0, 0, 0);
-    if (pre > 0 && (s - L) % NS == 0) d = make_int4(s, min(NS, end[i] - s), pre, 0);
+    // the slot of s: the group of NS members it belongs to, kept at the
+    // group's first member
+    const int slot = pre > 0 ? L + (s - L) / NS * NS : s;
+    int4 d = make_int4(slot, 0, 0, 0);
+    if (pre > 0 && slot == s) d = make_int4(s, min(NS, end[i] - s), pre, 0);
     reinterpret_cast<int4*>(a.share_desc)[s] = d;
   }
 }
 
+// Each sequence's prefix pieces, combined into one partial (M, L, O) per
+// query head for the suffix pass: one wave per (sequence, KV head), 64 / G
+// lanes per head, every piece's loads of a batch of eight in flight before
+// they are combined (M = max m_p, L = sum 2^(m_p - M) l_p, O likewise).
+template <int G, int D>
+__global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams a) {
+  constexpr int LPH = 64 / G;                    // lanes per head
+  constexpr int DPL = D / LPH;                   // dims per lane
+  constexpr int NB = 8;                          // pieces per batch
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int H = a.num_kv_heads, T = a.team, HG = H / T;
+  if (w >= (int64_t)a.num_seqs * H) return;
+  const int s = (int)(w / H), kvh = (int)(w - (int64_t)s * H);
+  if (a.share_start[s] <= 0) return;
+  const int hh = lane / LPH, d0 = (lane % LPH) * DPL;
+  const int64_t pr = (int64_t)s * a.num_q_heads + (int64_t)kvh * G + hh;
+  int64_t cs = 0, ccp = 0;
+  int col0 = 0, t0 = 0, t1 = -1;
+  float M = -__builtin_inff(), L = 0.f, O[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
+  if (!prefix_segment(a, s, kvh / T, HG, 16 / G, G, cs, col0, t0, t1, ccp)) L = __builtin_nanf("");
+  for (int tb = t0; tb <= t1; tb += NB) {
+    float mv[NB], lv[NB], ov[NB][DPL];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int tm = tb + u;
+      const bool ok = tm <= t1 && team_begin(tm, ccp, a.pre_teams) != team_begin(tm + 1, ccp, a.pre_teams);
+      const int64_t sl = ((tm + cs) * T + kvh % T) * 16 + col0 + hh;
+      mv[u] = ok ? a.pre_ws_m[ok ? sl : 0] : -__builtin_inff();
+      lv[u] = ok ? a.pre_ws_l[ok ? sl : 0] : 0.f;
+      const float* po = a.pre_ws_o + (ok ? sl : 0) * D + d0;
+      if constexpr (DPL % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < DPL; i += 4) {
+          const float4 x = ok ? *reinterpret_cast<const float4*>(po + i) : make_float4(0, 0, 0, 0);
+          ov[u][i] = x.x; ov[u][i + 1] = x.y; ov[u][i + 2] = x.z; ov[u][i + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) ov[u][i] = ok ? po[i] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float mn = fmaxf(M, mv[u]);
+      if (mn == -__builtin_inff()) continue;
+      const float f1 = __builtin_amdgcn_exp2f(M - mn), f2 = __builtin_amdgcn_exp2f(mv[u] - mn);
+      L = L * f1 + lv[u] * f2;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) O[i] = O[i] * f1 + ov[u][i] * f2;
+      M = mn;
+    }
+  }
+  float* o = a.pre_o + pr * D + d0;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = O[i];
+  if (lane % LPH == 0) {
+    a.pre_m[pr] = M;
+    a.pre_l[pr] = L;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_prefix_combine(const DecodeParams& a, int g, hipStream_t st) {
+  const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  };
+  if (a.head_dim == 128) {
+    switch (g) {
+      case 1: return go(prefix_combine_kernel<1, 128>);
+      case 2: return go(prefix_combine_kernel<2, 128>);
+      case 4: return go(prefix_combine_kernel<4, 128>);
+      case 8: return go(prefix_combine_kernel<8, 128>);
+    }
+  } else if (a.head_dim == 64) {
+    switch (g) {
+      case 1: return go(prefix_combine_kernel<1, 64>);
+      case 2: return go(prefix_combine_kernel<2, 64>);
+      case 4: return go(prefix_combine_kernel<4, 64>);
+      case 8: return go(prefix_combine_kernel<8, 64>);
+    }
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_share_plan(const DecodeParams& a, int g, hipStream_t st) {
   if (a.num_seqs <= 0) return hipSuccess;
@@ -185,8 +286,8 @@ hipError_t launch_attend_shared(const DecodeParams& a, int kv_ty, int q_ty, int 
 
 hipError_t launch_merge_shared(const DecodeParams& a, int q_ty, int g, int blocks, int mode,
                                hipStream_t st) {
-  return mode == M_PREFIX ? sk_launch_merge<M_PREFIX>(a, q_ty, g, blocks, st)
-                          : sk_launch_merge<M_SUFFIX>(a, q_ty, g, blocks, st);
+  if (mode != M_SUFFIX) return hipErrorInvalidValue;   // prefix pieces merge in the suffix pass
+  return sk_launch_merge<M_SUFFIX>(a, q_ty, g, blocks, st);
 }
 
 }  // namespace pa

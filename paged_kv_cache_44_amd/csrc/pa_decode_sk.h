@@ -55,8 +55,11 @@
 //  * M_PREFIX: a segment is a slot of up to 16/G consecutive sequences
 //    whose tables share the prefix blocks; their queries fill the 16 tile
 //    columns side by side (column c: sequence first + c/G, head c%G), so
-//    each K/V chunk of the prefix is loaded once for all of them. The result
-//    is an unnormalised partial (m, l, o) per sequence and head.
+//    each K/V chunk of the prefix is loaded once for all of them. Every
+//    piece is left as a partial (m, l, o) per column, and the team range of
+//    each prefix segment is recorded.
+//  * prefix_combine_kernel (pa_decode_shared.hip) combines each sequence's
+//    prefix pieces into one partial per head.
 //  * M_SUFFIX: each sequence's segment starts after its shared prefix, and
 //    the piece holding its first chunk continues from the prefix's partial,
 //    so the usual finish / merge produce the full result.
@@ -82,6 +85,28 @@ __device__ __forceinline__ int seq_chunks(const DecodeParams& a, int ctx) {
   const int64_t nb = ((int64_t)ctx + a.block_size - 1) >> a.log2_block_size;
   if (nb > a.max_blocks_per_seq) return 0;
   return (ctx + CH - 1) / CH;
+}
+
+// The prefix-pass segment holding sequence s's prefix for head group hg:
+// its index cs, the sequence's first tile column col0, and the teams t0 ..
+// t1 (and the column count Ccp) of the prefix pass whose ranges hold its
+// pieces. False when s has no prefix slot or the records do not fit the
+// batch (they then are not read).
+__device__ __forceinline__ bool prefix_segment(const DecodeParams& a, int s, int hg, int hgs,
+                                               int ns, int g, int64_t& cs, int& col0, int& t0,
+                                               int& t1, int64_t& ccp) {
+  const int4 sd = reinterpret_cast<const int4*>(a.share_desc)[s];
+  const int p = sd.x;
+  if (p < 0 || p > s || s - p >= ns) return false;
+  cs = (int64_t)p * hgs + hg;
+  const int4 sg = reinterpret_cast<const int4*>(a.share_seg)[cs];
+  if (!(sg.x >= 0 && sg.x <= sg.y && sg.y < a.pre_teams && sg.z > 0 && sg.w == a.pre_teams))
+    return false;
+  t0 = sg.x;
+  t1 = sg.y;
+  ccp = sg.z;
+  col0 = (s - p) * g;
+  return true;
 }
 
 // Team ranges. The W resident waves form Wt = W / T teams of T consecutive
@@ -112,12 +137,16 @@ constexpr int M_PLAIN = 0, M_PREFIX = 1, M_SUFFIX = 2;
 
 // Occupancy: FP8 pools and D = 64 fit 3 waves per SIMD without spilling;
 // 16-bit pools at D = 128 run at 2.
-template <Ty KV, int D, int G>
-constexpr int sk_waves_per_simd() { return (KV == Ty::FP8 || D == 64) ? 3 : 2; }
+// The prefix pass (16 query columns of several sequences) needs more
+// registers and runs at 2 everywhere.
+template <Ty KV, int D, int G, int MODE>
+constexpr int sk_waves_per_simd() {
+  return MODE == M_PREFIX ? 2 : ((KV == Ty::FP8 || D == 64) ? 3 : 2);
+}
 
 template <Ty KV, Ty QT, int D, int G, int MODE>
 __global__ void __launch_bounds__(NWM * 64)
-__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G>())))
+__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G, MODE>())))
 attend_sk_kernel(const DecodeParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
@@ -214,6 +243,7 @@ attend_sk_kernel(const DecodeParams a) {
       if (s_cum[s + 1] == s_cum[s]) {
         const int64_t base = (int64_t)s * a.num_q_heads * D;
         if (MODE == M_SUFFIX && s_aux[s] > 0) {
+          // the whole context is shared prefix: its partial, normalised
           for (int e = tid; e < a.num_q_heads * D; e += NWM * 64)
             store_out<QT>(a.out, base + e,
                           a.pre_o[base + e] * (a.v_scale / a.pre_l[(int64_t)s * a.num_q_heads + e / D]));
@@ -331,6 +361,11 @@ attend_sk_kernel(const DecodeParams a) {
       d.ctx = is.ctx;
       d.j = first_chunk(is.x) + ij;
       d.x = is.x;
+      if constexpr (MODE == M_PREFIX) {
+        if (ij == 0 && ti == 0 && lane == 0)
+          reinterpret_cast<int4*>(a.share_seg)[(int64_t)is.seq * HG + is.hg] =
+              make_int4((int)team, (int)team_of(ic + is.nc - 1, Cc, Wt), (int)Cc, (int)Wt);
+      }
       ++ic;
       ++ij;
       const bool seg_end = ij == is.nc;
@@ -459,17 +494,7 @@ attend_sk_kernel(const DecodeParams a) {
       const float lh = __shfl(lt, h);
       const float mh = __shfl(m_ref, h);
       if (h < ncol) {
-        if (MODE == M_PREFIX && whole) {
-          // the prefix's partial of sequence first + h/G, head kvh*G + h%G
-          const int64_t pr = (int64_t)((d.x & 0xffff) + h / G) * a.num_q_heads + (int64_t)kvh * G + h % G;
-          float* po = a.pre_o + pr * D + VPL * n;
-#pragma unroll
-          for (int m = 0; m < VPL; ++m) po[m] = bad ? __builtin_nanf("") : acc[m][r];
-          if (n == 0) {
-            a.pre_m[pr] = bad ? 0.f : mh;
-            a.pre_l[pr] = bad ? __builtin_nanf("") : lh;
-          }
-        } else if (whole) {
+        if (whole && MODE != M_PREFIX) {
           const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
           const int64_t o = out_row0 + (int64_t)h * D + VPL * n;
 #pragma unroll
@@ -498,7 +523,8 @@ attend_sk_kernel(const DecodeParams a) {
     if constexpr (MODE == M_SUFFIX) {
       if ((d.f & F_FIRST) && d.x > 0 && d.j == d.x) {
         // the piece opening the sequence's own tokens continues from the
-        // shared prefix's partial (state layout of softmax_pv)
+        // shared prefix's partial (state layout of softmax_pv: column n =
+        // head n's max and sum, accumulator rows 4g + r = heads)
         const int64_t r0 = (int64_t)d.seq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G;
         m_ref = n < G ? a.pre_m[r0 + n] : -__builtin_inff();
         l_sum = (n < G && g == 0) ? a.pre_l[r0 + n] : 0.f;
@@ -566,13 +592,14 @@ attend_sk_kernel(const DecodeParams a) {
 // merges KV head i of the group of the segment recorded by team t (if any),
 // over its pieces from teams t .. r1. Threads form PG groups, each covering
 // all GC x D outputs (DPT dims per thread) over every PG-th piece with a
-// running (online) combination; the groups are combined in LDS. M_PREFIX
-// writes the combined partial (M, L, O) of each of the slot's sequences
-// instead of the normalised output.
+// running (online) combination; the groups are combined in LDS. (The prefix
+// pass of the shared-prefix decode has no merge: the suffix pass combines
+// its pieces.)
 template <Ty QT, int D, int G, int MODE>
 __global__ void __launch_bounds__(256)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
-  constexpr int GC = MODE == M_PREFIX ? 16 : G;        // tile columns holding queries
+  static_assert(MODE != M_PREFIX, "prefix pieces are combined by the suffix pass");
+  constexpr int GC = G;
   constexpr int GD = GC * D;
   constexpr int DPT = GD >= 1024 ? 16 : (GD >= 512 ? 8 : 4);   // dims per thread
   constexpr int NV4 = DPT / 4;
@@ -653,23 +680,10 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     for (int q = 0; q < PG; ++q)
       combine(s_m[q][h], s_l[q][h], reinterpret_cast<const float4*>(&s_o[q][h * D + d0]));
   }
-  if constexpr (MODE == M_PREFIX) {
-    const int4 sd = reinterpret_cast<const int4*>(a.share_desc)[seq];
-    if (h >= G * sd.y) return;                         // column without a query
-    const int64_t pr = (int64_t)(sd.x + h / G) * a.num_q_heads + (int64_t)kvh * G + h % G;
+  const float norm = a.v_scale / L;
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) a.pre_o[pr * D + d0 + e] = O[e];
-    if (d0 == 0) {
-      a.pre_m[pr] = M;
-      a.pre_l[pr] = L;
-    }
-  } else {
-    const float norm = a.v_scale / L;
-#pragma unroll
-    for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, O[e] * norm);
-  }
+  for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, O[e] * norm);
 }
-
 
 // ---------------------------------------------------------------------------
 // Launch side, templated on the mode. The shared-prefix modes exist for the
@@ -731,7 +745,7 @@ static int sk_blocks_t(int num_seqs) {
   // More resident workgroups than the compiled target adds no bandwidth (the
   // slab reads already keep the memory system full at that occupancy) and
   // only shortens each wave's range, raising the merge's share of the work.
-  const int target = sk_waves_per_simd<KV, D, G>();
+  const int target = sk_waves_per_simd<KV, D, G, MODE>();
   if (per_cu <= 0 || per_cu > target) per_cu = target;
   const int b = cus * per_cu;
   return b >= NXCD ? b / NXCD * NXCD : NXCD;

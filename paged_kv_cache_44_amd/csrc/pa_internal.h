@@ -43,7 +43,14 @@ struct DecodeParams {
   // shared-prefix decode (matrix-core path only)
   int32_t* share_lcp;        // [num_seqs] tokens sequence s shares with s - 1 (from the tables)
   int32_t* share_start;      // [num_seqs] tokens of the shared prefix each sequence starts after
-  int32_t* share_desc;       // [num_seqs] int4 {first member, members, prefix tokens, 0} per slot
+  int32_t* share_desc;       // [num_seqs] int4 {slot, members, prefix tokens, 0}: members and
+                             // prefix are nonzero only at a slot's own index
+  int32_t* share_seg;        // [num_seqs * head groups] int4 {first team, last team, Cc, teams}
+                             // of each prefix segment, written by the prefix pass
+  const float* pre_ws_o;     // the prefix pass's pieces (its ws_o, ws_m, ws_l), combined
+  const float* pre_ws_m;     // per sequence and head into pre_m, pre_l, pre_o
+  const float* pre_ws_l;
+  int32_t pre_teams;         // teams of the prefix pass
   float* pre_m;              // [num_seqs][num_q_heads] prefix partials: running max (log2)
   float* pre_l;              // [num_seqs][num_q_heads] sum of weights
   float* pre_o;              // [num_seqs][num_q_heads][head_dim] unnormalised output
@@ -145,6 +152,7 @@ hipError_t launch_attend_shared(const DecodeParams& a, int kv_ty, int q_ty, int 
                                 int mode, hipStream_t st);
 hipError_t launch_merge_shared(const DecodeParams& a, int q_ty, int g, int blocks, int mode,
                                hipStream_t st);
+hipError_t launch_prefix_combine(const DecodeParams& a, int g, hipStream_t st);
 bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g);
 int prefill_tiles(int g, int max_query_len);
 hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
