@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_44_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_mfma.h", "pa_device.h", "pa_internal.h")]
+                  for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_decode_sk.h", "pa_mfma.h", "pa_device.h",
+                            "pa_internal.h")]
 
 
 def attend_kernel_name(wl) -> str:

@@ -316,6 +316,58 @@ __device__ __forceinline__ void softmax_pv(const float (&z)[4], const uint32_t (
   }
 }
 
+// The B operands of the P.V products of one chunk (element m of the four
+// token vectors, two byte permutes per m), for kernels that apply the same
+// chunk to several column tiles.
+template <int D>
+__device__ __forceinline__ void pv_operands(const uint32_t (&vw)[4][D / 32], uint32_t (&b)[D / 16][2]) {
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) {
+    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+    b[m][0] = __builtin_amdgcn_perm(vw[1][m >> 1], vw[0][m >> 1], sel);
+    b[m][1] = __builtin_amdgcn_perm(vw[3][m >> 1], vw[2][m >> 1], sel);
+  }
+}
+
+// softmax_pv with the B operands already built (pv_operands).
+template <Ty KV, Ty QT, int D>
+__device__ __forceinline__ void softmax_pv_b(const float (&z)[4], const uint32_t (&b)[D / 16][2],
+                                             f32x4_t (&acc)[D / 16], float& m_ref, float& l_sum,
+                                             int lane) {
+  constexpr int VPL = D / 16;
+  constexpr Op OPV = ChunkOps<KV, QT>::PV;
+  const int g = lane >> 4;
+  const float lmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+  if (__any(lmax > m_ref + SM_TAU)) {
+    float hm = fmaxf(lmax, __shfl_xor(lmax, 16));
+    hm = fmaxf(hm, __shfl_xor(hm, 32));
+    const float mn = fmaxf(m_ref, hm);
+    const float al = (mn == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
+    m_ref = mn;
+    l_sum *= al;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(al, 4 * g + r);
+#pragma unroll
+      for (int m = 0; m < VPL; ++m) acc[m][r] *= ar;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    p[r] = (z[r] == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(z[r] - m_ref);
+  const uint32_t pa0 = pack2<OPV>(p[0], p[1]);
+  const uint32_t pa1 = pack2<OPV>(p[2], p[3]);
+  {
+    float q0, q1, q2, q3;
+    unpack2<OPV>(pa0, q0, q1);
+    unpack2<OPV>(pa1, q2, q3);
+    l_sum += (q0 + q1) + (q2 + q3);
+  }
+#pragma unroll
+  for (int m = 0; m < VPL; ++m) acc[m] = mfma_k16<OPV>(pa0, pa1, b[m][0], b[m][1], acc[m]);
+}
+
 // v_operand followed by softmax_pv (one column tile per chunk).
 template <Ty KV, Ty QT, int D>
 __device__ __forceinline__ void chunk_softmax_pv(const float (&z)[4],

@@ -37,6 +37,23 @@ constexpr int pf_waves_per_simd() { return D == 64 ? 3 : 2; }
 // Column tiles per wave: each loaded key chunk serves NT x 16 columns.
 constexpr int PNT = 2;
 
+// K rows are loaded straight in the score product's operand layout (lane l:
+// token l%16, dims 32k + 8(l/16) of step k): no lane exchange afterwards.
+// The four waves of a workgroup read each chunk, mostly from the caches, so
+// the whole-line reads that decode streams from memory with bring nothing
+// here (measured slightly slower).
+template <int D, int EB>
+struct PfKLayout {
+  static constexpr int KS = D / 32;
+  static constexpr int KDW = 8 * EB / 4;
+  static constexpr int KR = KS;
+  static constexpr int KW = KDW;
+};
+template <int D, int EB>
+__device__ __forceinline__ int pf_kdim(int k, int a) {
+  return 32 * k + 8 * a;
+}
+
 template <Ty KV, Ty QT, int D, int G>
 __global__ void __launch_bounds__(PW * 64)
 __attribute__((amdgpu_waves_per_eu(pf_waves_per_simd<KV, D>())))
@@ -44,7 +61,7 @@ prefill_kernel(const PrefillParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group divides the 16-column tile");
   constexpr int EB = TyInfo<KV>::bytes;
-  using KL = KLayout<D, EB>;
+  using KL = PfKLayout<D, EB>;
   constexpr int KS = KL::KS;
   constexpr int KR = KL::KR;
   constexpr int KW = KL::KW;
@@ -114,13 +131,17 @@ prefill_kernel(const PrefillParams a) {
 
   // q of each tile as the B operand: lane l holds column l%16 (rows past the
   // wave's last repeat it; their scores are masked)
-  uint32_t qr[NT][KS][4];
+  uint4 qr[NT][KS];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int64_t row = (((int64_t)r0 + t0 + min(t * QTOK + n / G, rows - 1)) * a.num_q_heads +
                          (int64_t)kvh * G + n % G) * D;
 #pragma unroll
-    for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim_t<D, EB>(k, g)) >> 1), qr[t][k]);
+    for (int k = 0; k < KS; ++k) {
+      uint32_t w4[4];
+      ld<4>(qw + ((row + pf_kdim<D, EB>(k, g)) >> 1), w4);
+      qr[t][k] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
   }
 
   // block ids of chunk j (clamped to the last chunk): lane i holds the id of
@@ -141,40 +162,27 @@ prefill_kernel(const PrefillParams a) {
     const bool badl = idr < 0 || idr >= a.num_blocks;
     bad = bad || __any(badl);
     const int idv = badl ? 0 : idr;
+
     auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {   // element of token t, dim 0
       t = min(t, ctx - 1);
       const int id = big_blocks ? __builtin_amdgcn_readfirstlane(idv) : __shfl(idv, (t >> lg) - fb);
       return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
     };
-    int64_t ek[KL::FULL ? 2 : 1], ev[4];
+    // K in the operand layout (lane l: token l%16, dims 32k + 8(l/16)); V
+    // rows 4(l/16) .. +3, dims VPL*(l%16) .. +VPL
+    int64_t ek, ev[4];
     if (big_blocks) {
       const int64_t base = elem_of(cb);
-      if constexpr (KL::FULL) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          ek[hf] = base + (int64_t)min(k_load_row<D, EB>(hf, lane), ctx - 1 - cb) * D + k_load_col<D, EB>(0, lane);
-      } else {
-        ek[0] = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
-      }
+      ek = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
     } else {
-      if constexpr (KL::FULL) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) ek[hf] = elem_of(cb + k_load_row<D, EB>(hf, lane)) + k_load_col<D, EB>(0, lane);
-      } else {
-        ek[0] = elem_of(cb + n) + 8 * g;
-      }
+      ek = elem_of(cb + n) + 8 * g;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
     }
-    if constexpr (KL::FULL) {
 #pragma unroll
-      for (int u = 0; u < KR; ++u) ld<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < KS; ++k) ld<KW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
-    }
+    for (int k = 0; k < KS; ++k) ld<KW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
   };
@@ -183,33 +191,54 @@ prefill_kernel(const PrefillParams a) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m_ref[t] = -__builtin_inff();           // reference max of the column (log2 units)
-    l_sum[t] = 0.f;
+    l_sum[t] = 0.f;                         // this lane's share of the column's sum
   }
   auto process = [&](int j, const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW])
       __attribute__((always_inline)) {
     const int cb = j * PCH;
     uint32_t kraw[KS][KL::KDW];
-    k_operand<D, EB>(kr, kraw, lane);
-    bool live[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int x = 0; x < KL::KDW; ++x) kraw[k][x] = kr[k][x];
     uint32_t vw[4][D / 32];
-    v_operand<KV, QT, D>(vr, live, vw);
+    if (cb + PCH <= ctx) {                  // whole chunk: every value row is live
+      const bool live[4] = {true, true, true, true};
+      v_operand<KV, QT, D>(vr, live, vw);
+    } else {
+      bool live[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
+      v_operand<KV, QT, D>(vr, live, vw);
+    }
+    uint32_t vb[VPL][2];                    // P.V B operands, shared by the tiles
+    pv_operands<D>(vw, vb);
+    // a chunk wholly before the wave's first position needs no causal mask
+    const bool below = cb + PCH - 1 <= pos0;
+    const bool full_wave = rows == WTOK;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int tok = t * QTOK + n / G;
       const int pcol = pos0 + tok;          // position of this column
       if (t * QTOK >= rows) break;          // tile past the wave's rows (uniform)
       const f32x4_t sc = chunk_scores_raw<KV, QT, D>(kraw, [&](int k) {
-        return make_uint4(qr[t][k][0], qr[t][k][1], qr[t][k][2], qr[t][k][3]);
+        return qr[t][k];
       });
       float z[4];
+      if (below && full_wave) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tk = cb + 4 * g + r;
-        z[r] = (tok < rows && tk <= pcol) ? sc[r] * qk_scale : -__builtin_inff();
+        for (int r = 0; r < 4; ++r) z[r] = sc[r] * qk_scale;
+      } else if (below) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] = tok < rows ? sc[r] * qk_scale : -__builtin_inff();
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tk = cb + 4 * g + r;
+          z[r] = (tok < rows && tk <= pcol) ? sc[r] * qk_scale : -__builtin_inff();
+        }
       }
-      softmax_pv<KV, QT, D>(z, vw, acc[t], m_ref[t], l_sum[t], lane);
+      softmax_pv_b<KV, QT, D>(z, vb, acc[t], m_ref[t], l_sum[t], lane);
     }
   };
 
@@ -229,13 +258,12 @@ prefill_kernel(const PrefillParams a) {
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float lt = l_sum[t] + __shfl_xor(l_sum[t], 16);
-    lt += __shfl_xor(lt, 32);
     float norm[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float lh = __shfl(lt, 4 * g + r);
-      norm[r] = bad ? __builtin_nanf("") : a.v_scale / lh;
+      float lt = l_sum[t] + __shfl_xor(l_sum[t], 16);
+      lt += __shfl_xor(lt, 32);
+      norm[r] = bad ? __builtin_nanf("") : a.v_scale / __shfl(lt, 4 * g + r);
     }
     store_rows(t, norm);
   }
