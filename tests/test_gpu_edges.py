@@ -487,3 +487,35 @@ def test_batch_with_nothing_to_attend_over_stale_workspace(fill):
     torch.cuda.synchronize()
     got = codecs.decode(tensor_codes(out), "bf16")
     assert np.all(got == 0) if fill == "empty" else np.all(np.isnan(got))
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_repeat_calls_on_junk_workspace_are_identical(cfg):
+    """Back-to-back decodes over one workspace that starts out filled with
+    junk: every call writes each piece and merge descriptor it later reads,
+    so nothing left by the junk or by the previous call reaches the output.
+    All calls give bit-identical output, equal to the oracle."""
+    wl = workloads.make(cfg, **({"num_seqs": 64} if cfg == 3 else {}))
+    st = DeviceState(wl)
+    for op in workloads.fill_plan(wl):
+        if op[0] == "write":
+            st.write(op[1], op[2], op[3])
+        else:
+            st.copy_d2d(op[1])
+    q = codes_to_tensor(wl.q, wl.q_dtype)
+    tt = torch.from_numpy(wl.block_tables).cuda()
+    ct = torch.from_numpy(wl.context_lens).cuda()
+    mc = wl.max_context_len
+    n = pa.decode_workspace_size(st.cache, wl.num_seqs, wl.num_q_heads, mc)
+    ws = torch.full((n,), 0x5a, dtype=torch.uint8, device="cuda")
+    outs = [tensor_codes(pa.decode(st.cache, 0, q, tt, ct, mc, wl.scale, workspace=ws))
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    seqs = sorted(np.random.default_rng(cfg).choice(wl.num_seqs, 6, replace=False).tolist())
+    ref = st.oracle_decode(seqs=seqs)
+    got = codecs.decode(outs[2], wl.q_dtype)
+    ex = max_err_stored(got, ref, wl.q_dtype, rows=seqs)
+    tol = TOL["fp8_e4m3"] if wl.pool_dtype == "fp8_e4m3" else TOL[wl.q_dtype]
+    say(f"config {cfg}: error beyond output rounding {ex:.3e}")
+    assert ex <= tol
