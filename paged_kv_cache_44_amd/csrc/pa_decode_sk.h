@@ -454,13 +454,13 @@ attend_sk_kernel(const DecodeParams a) {
     }
     if constexpr (KFULL) {
 #pragma unroll
-      for (int u = 0; u < KR; ++u) ld<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
+      for (int u = 0; u < KR; ++u) ld_stream<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
     } else {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) ld<KDW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
+      for (int k = 0; k < KS; ++k) ld_stream<KDW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+    for (int r = 0; r < 4; ++r) ld_stream<VDW>(vpool + ev[r] * EB / 4, vr[r]);
     if (ok) {
       lbad = lbad || bad;
       if (lbad && (d.f & F_LAST)) d.f |= F_BAD;
