@@ -268,8 +268,13 @@ attend_sk_kernel(const DecodeParams a) {
   const int64_t team = w / T;
   const int ti = (int)(w - team * T);                           // KV head within the group
 
-  const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
-  const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
+  // pools as bytes: element offsets (never negative) scale by EB, with no
+  // signed division on the load path
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  auto dw = [](const char* p, int64_t e) __attribute__((always_inline)) {
+    return reinterpret_cast<const uint32_t*>(p + e * EB);
+  };
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
   const int lg = a.log2_block_size;
   const int bmask = a.block_size - 1;
@@ -345,8 +350,10 @@ attend_sk_kernel(const DecodeParams a) {
   const int32_t* irow = a.block_tables;              // table row of the last indexed chunk
   int ifb = 0, ilb = 0;                              // its first and last block
   auto index_chunk = [&](Desc& d, int& idr) __attribute__((always_inline)) {
+    // past the range: no flags, no tokens (processing it changes nothing)
     d.f = 0;
     d.x = 0;
+    d.seq = d.hg = d.nc = d.ctx = d.j = 0;
     if (iact) {
       const int cb = (first_chunk(is.x) + ij) * CH;
       ifb = cb >> lg;
@@ -454,13 +461,13 @@ attend_sk_kernel(const DecodeParams a) {
     }
     if constexpr (KFULL) {
 #pragma unroll
-      for (int u = 0; u < KR; ++u) ld_stream<4>(kpool + (ek[u & 1] + (u >> 1) * (128 / EB)) * EB / 4, kr[u]);
+      for (int u = 0; u < KR; ++u) ld_stream<4>(dw(kpool, ek[u & 1] + (u >> 1) * (128 / EB)), kr[u]);
     } else {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) ld_stream<KDW>(kpool + (ek[0] + 32 * k) * EB / 4, kr[k]);
+      for (int k = 0; k < KS; ++k) ld_stream<KDW>(dw(kpool, ek[0] + 32 * k), kr[k]);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ld_stream<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+    for (int r = 0; r < 4; ++r) ld_stream<VDW>(dw(vpool, ev[r]), vr[r]);
     if (ok) {
       lbad = lbad || bad;
       if (lbad && (d.f & F_LAST)) d.f |= F_BAD;
@@ -561,6 +568,12 @@ attend_sk_kernel(const DecodeParams a) {
   // issued first so that it cannot shorten the waits that follow); the ids
   // of chunk i+2 and the K/V of chunk i+1 are fetched; chunk i is processed.
   // The waits before processing leave every load of the step in flight.
+  // The loop leaves only after a B step: a chunk past the end is processed
+  // as a no-op (every score masked, no piece flags). A leave after the A
+  // step would reach the loop latch with B's loads unread (the compiler
+  // gives a loop with divergent branches a single exit through its latch),
+  // and the wait analysis would then drain A's loads at the top of every
+  // step before reusing B's registers: one chunk in flight instead of two.
   uint32_t kA[KR][KW], vA[4][VDW], kB[KR][KW], vB[4][VDW];
   Desc dA, dB;                                       // chunk in (or bound for) each buffer
   int iA = 0, iB = 0;
@@ -574,15 +587,14 @@ attend_sk_kernel(const DecodeParams a) {
     load_q(dB);
     index_chunk(dn, iA);
     load_chunk(dB, iB, kB, vB);
-    process_chunk(kA, vA, dA);
-    if (!(dB.f & F_VALID)) break;
+    process_chunk(kA, vA, dA);                       // always a chunk of the range
     dA = dn;
     flush_q();
     load_q(dA);
     index_chunk(dn, iB);
     load_chunk(dA, iA, kA, vA);
-    process_chunk(kB, vB, dB);
-    if (!(dA.f & F_VALID)) break;
+    process_chunk(kB, vB, dB);                       // past the end: no effect
+    if (!(dA.f & F_VALID)) return;                   // (dB past the end implies dA too)
     dB = dn;
   }
 }

@@ -82,14 +82,12 @@ __device__ __forceinline__ void unpack2(uint32_t w, float& a, float& b) {
 // 4 E4M3 codes -> two packed 16-bit pairs of operand type O (exact)
 template <Op O>
 __device__ __forceinline__ void fp8x4_to(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
   if constexpr (O == Op::BF16) {
-    lo = __builtin_amdgcn_perm(f2u(a[1]), f2u(a[0]), 0x07060302u);   // upper halves
-    hi = __builtin_amdgcn_perm(f2u(b[1]), f2u(b[0]), 0x07060302u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
   } else {
-    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
-    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1]));
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
   }
 }
 
