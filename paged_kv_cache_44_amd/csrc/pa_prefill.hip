@@ -117,8 +117,13 @@ prefill_kernel(const PrefillParams a) {
     return;
   }
 
-  const uint32_t* kpool = reinterpret_cast<const uint32_t*>(a.k_pool);
-  const uint32_t* vpool = reinterpret_cast<const uint32_t*>(a.v_pool);
+  // pools as bytes: element offsets (never negative) scale by EB, with no
+  // signed division on the load path
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  auto dw = [](const char* p, int64_t e) __attribute__((always_inline)) {
+    return reinterpret_cast<const uint32_t*>(p + e * EB);
+  };
   const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
   const int bmask = a.block_size - 1;
   const bool big_blocks = a.block_size >= PCH;
@@ -182,9 +187,9 @@ prefill_kernel(const PrefillParams a) {
       for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
     }
 #pragma unroll
-    for (int k = 0; k < KS; ++k) ld<KW>(kpool + (ek + 32 * k) * EB / 4, kr[k]);
+    for (int k = 0; k < KS; ++k) ld<KW>(dw(kpool, ek + 32 * k), kr[k]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ld<VDW>(vpool + ev[r] * EB / 4, vr[r]);
+    for (int r = 0; r < 4; ++r) ld<VDW>(dw(vpool, ev[r]), vr[r]);
   };
 
   float m_ref[NT], l_sum[NT];
@@ -246,11 +251,16 @@ prefill_kernel(const PrefillParams a) {
   int iA = fetch_ids(0);
   int iB = fetch_ids(1);
   load_kv(0, iA, kA, vA);
+  // One exit, at the end of the pair: chunk nch (odd nch) is processed as a
+  // no-op (its rows are past the context: V reads as zero, every score is
+  // masked). A leave after the first chunk of the pair would reach the loop
+  // latch with B's loads unread (the divergent loop is put in single-exit
+  // form), and the wait analysis would then drain A's loads at the top of
+  // every pair before B's registers are reused.
   for (int j = 0; j < nch; j += 2) {
     iA = fetch_ids(j + 2);
     load_kv(j + 1, iB, kB, vB);
     process(j, kA, vA);
-    if (j + 1 >= nch) break;
     iB = fetch_ids(j + 3);
     load_kv(j + 2, iA, kA, vA);
     process(j + 1, kB, vB);
