@@ -346,6 +346,34 @@ __device__ __forceinline__ void pv_operands(const uint32_t (&vw)[4][D / 32], uin
   }
 }
 
+// The same B operands straight from FP8 value codes (f16 operands, exact):
+// the raw codes of token rows 0 and 1 (and 2 and 3) are byte-interleaved,
+// one permute per two dims, and each interleaved dword converts to two
+// operand pairs, so a dim costs three instructions instead of four. vr is
+// the lane's value loads (slice [VPL*(l%16), +VPL) of tokens 4(l/16)+r);
+// live[r] false for rows that must read as zero (code 0 is +0).
+template <int D>
+__device__ __forceinline__ void pv_operands_fp8(const uint32_t (&vr)[4][D / 64], const bool (&live)[4],
+                                                uint32_t (&b)[D / 16][2]) {
+#pragma unroll
+  for (int x = 0; x < D / 64; ++x) {
+    uint32_t a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = live[r] ? vr[r][x] : 0u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // bytes {row 2p dim 2h, row 2p+1 dim 2h, row 2p dim 2h+1, row 2p+1 dim 2h+1}
+      const uint32_t sel = h ? 0x07030602u : 0x05010400u;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const uint32_t t = __builtin_amdgcn_perm(a[2 * p + 1], a[2 * p], sel);
+        b[4 * x + 2 * h][p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 1.0f, false));
+        b[4 * x + 2 * h + 1][p] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(t, 1.0f, true));
+      }
+    }
+  }
+}
+
 // softmax_pv with the B operands already built (pv_operands).
 template <Ty KV, Ty QT, int D>
 __device__ __forceinline__ void softmax_pv_b(const float (&z)[4], const uint32_t (&b)[D / 16][2],
@@ -391,9 +419,16 @@ __device__ __forceinline__ void chunk_softmax_pv(const float (&z)[4],
                                                  const uint32_t (&vr)[4][D / 16 * TyInfo<KV>::bytes / 4],
                                                  const bool (&live)[4], f32x4_t (&acc)[D / 16],
                                                  float& m_ref, float& l_sum, int lane) {
-  uint32_t vw[4][D / 32];
-  v_operand<KV, QT, D>(vr, live, vw);
-  softmax_pv<KV, QT, D>(z, vw, acc, m_ref, l_sum, lane);
+  if constexpr (KV == Ty::FP8) {
+    static_assert(ChunkOps<KV, QT>::PV == Op::F16, "FP8 values are multiplied as f16");
+    uint32_t b[D / 16][2];
+    pv_operands_fp8<D>(vr, live, b);
+    softmax_pv_b<KV, QT, D>(z, b, acc, m_ref, l_sum, lane);
+  } else {
+    uint32_t vw[4][D / 32];
+    v_operand<KV, QT, D>(vr, live, vw);
+    softmax_pv<KV, QT, D>(z, vw, acc, m_ref, l_sum, lane);
+  }
 }
 
 }  // namespace pa

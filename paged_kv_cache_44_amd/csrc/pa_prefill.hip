@@ -206,18 +206,25 @@ prefill_kernel(const PrefillParams a) {
     for (int k = 0; k < KS; ++k)
 #pragma unroll
       for (int x = 0; x < KL::KDW; ++x) kraw[k][x] = kr[k][x];
-    uint32_t vw[4][D / 32];
-    if (cb + PCH <= ctx) {                  // whole chunk: every value row is live
-      const bool live[4] = {true, true, true, true};
-      v_operand<KV, QT, D>(vr, live, vw);
-    } else {
+    uint32_t vb[VPL][2];                    // P.V B operands, shared by the tiles
+    if constexpr (KV == Ty::FP8) {
       bool live[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
-      v_operand<KV, QT, D>(vr, live, vw);
+      pv_operands_fp8<D>(vr, live, vb);
+    } else {
+      uint32_t vw[4][D / 32];
+      if (cb + PCH <= ctx) {                // whole chunk: every value row is live
+        const bool live[4] = {true, true, true, true};
+        v_operand<KV, QT, D>(vr, live, vw);
+      } else {
+        bool live[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
+        v_operand<KV, QT, D>(vr, live, vw);
+      }
+      pv_operands<D>(vw, vb);
     }
-    uint32_t vb[VPL][2];                    // P.V B operands, shared by the tiles
-    pv_operands<D>(vw, vb);
     // a chunk wholly before the wave's first position needs no causal mask
     const bool below = cb + PCH - 1 <= pos0;
     const bool full_wave = rows == WTOK;
