@@ -1,5 +1,6 @@
 """Seeded random shapes against the oracle: plain decode (one call and the
-two-launch form, which must agree bit for bit) and shared-prefix decode,
+two-launch form, which must agree bit for bit), shared-prefix decode and
+prefill (whole prompts, later chunks, single rows, empty query sets),
 over every supported pool / query dtype pair, head dim, group size, KV head
 count (odd ones too), block size from 1 to 128, batch size and context mix
 (short, long-tailed, one long sequence among tiny ones, empty rows). Each
@@ -16,7 +17,7 @@ import torch
 
 import paged_kv_cache_44_amd as pa
 import workloads
-from oracle import codecs
+from oracle import codecs, paged
 from tests.gpu_helpers import (DeviceState, TOL, codes_to_tensor, max_err, max_err_stored, say,
                                tensor_codes)
 
@@ -137,3 +138,48 @@ def test_random_shape_shared_decode(seed):
     # the same batch through the plain decode agrees within the tolerance too
     plain = st.decode()
     assert max_err_stored(plain, ref, q) <= _tol(pool, q)
+
+
+def _prefill_case(seed):
+    r = np.random.default_rng(11000 + seed)
+    pool, q = [("f16", "f16"), ("bf16", "bf16"), ("fp8_e4m3", "bf16"), ("fp8_e4m3", "f16")][
+        int(r.integers(4))]
+    D = int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4, 8, 16]))
+    hkv = int(r.choice([1, 2, 3]))
+    B = int(r.choice([1, 2, 4, 8, 16, 32, 64, 128]))
+    S = int(r.integers(1, 13))
+    ctx = r.integers(1, 700, S)
+    # query rows: the whole context, a later chunk, one row, or none
+    nq = np.array([[c, int(r.integers(1, c + 1)), 1, 0][int(r.integers(4))] for c in ctx])
+    while int((ctx * nq).sum()) * G * hkv > 20 * BUDGET:
+        ctx = np.maximum(ctx // 2, 1)
+        nq = np.minimum(nq, ctx)
+    return pool, q, D, G, hkv, B, ctx, nq
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_shape_prefill(seed):
+    pool, q, D, G, hkv, B, ctx, nq = _prefill_case(seed)
+    say(f"pool {pool} q {q} D {D} G {G} H_kv {hkv} B {B} ctx {ctx.tolist()} rows {nq.tolist()}")
+    wl = workloads.custom(seed, ctx, pool_dtype=pool, q_dtype=q, num_q_heads=G * hkv,
+                          num_kv_heads=hkv, head_dim=D, block_size=B)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    qc, qsl = workloads.prefill_queries(wl, nq.tolist(), seed + 1)
+    if int(qsl[-1]) == 0:
+        return                                   # nothing to attend for
+    qt = codes_to_tensor(qc, q)
+    out = torch.empty_like(qt)
+    tt = torch.from_numpy(np.ascontiguousarray(wl.block_tables, dtype=np.int32)).cuda()
+    ct = torch.from_numpy(np.ascontiguousarray(wl.context_lens, dtype=np.int32)).cuda()
+    qs = torch.from_numpy(np.ascontiguousarray(qsl, dtype=np.int32)).cuda()
+    pa.prefill(st.cache, wl.layer, qt, tt, ct, int(ctx.max()), qs, max(int(np.max(np.diff(qsl))), 1),
+               wl.scale, out=out)
+    torch.cuda.synchronize()
+    got = codecs.decode(tensor_codes(out), q)
+    ref = paged.prefill(qc, q, st.ok, st.ov, st.geom, pool, wl.layer, wl.block_tables,
+                        wl.context_lens, qsl, wl.scale, wl.k_scale, wl.v_scale)
+    err = max_err_stored(got, ref, q)
+    say(f"{int(qsl[-1])} rows, max error beyond output rounding {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
