@@ -172,10 +172,11 @@ pa_status pa_write_kv(const pa_kv_cache* cache, int32_t layer, const void* k,
 /*  max_context_len  host upper bound on context_lens; sizes the launch.     */
 /*  workspace     device scratch of >= pa_decode_workspace_size(...) bytes,  */
 /*                256-byte aligned; contents need no initialisation.         */
-/* Supported today: head_dim 64 or 128 (64 only for PA_F32 pools);          */
-/* num_q_heads / num_kv_heads in {1, 2, 4, 8}; q_dtype equal to the pool     */
-/* dtype, or any of the three with a PA_FP8_E4M3 pool. Others return         */
-/* PA_ERR_UNSUPPORTED.                                                       */
+/* Supported today: head_dim 64 or 128 (PA_F32 pools: 64 only);             */
+/* num_q_heads / num_kv_heads in {1, 2, 4, 8}, and 16 with PA_F16, PA_BF16   */
+/* or PA_FP8_E4M3 pools and 16-bit queries for up to 8192 sequences; q_dtype */
+/* equal to the pool dtype, or any of the three with a PA_FP8_E4M3 pool.     */
+/* Others return PA_ERR_UNSUPPORTED.                                         */
 /*                                                                           */
 /* pa_decode is exactly pa_decode_attend followed by pa_decode_merge with    */
 /* the same arguments. The split lets a caller time or schedule the two      */

@@ -109,7 +109,8 @@ size_t ws_rows(const DecodePlan& p, int num_seqs, int num_q_heads, int num_kv_he
 pa_status decode_supported(const pa_kv_cache* c, int num_q_heads, pa_dtype q_dtype, int* g_out) {
   if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads) return PA_ERR_INVALID_ARG;
   const int g = num_q_heads / c->num_kv_heads;
-  if (!(g == 1 || g == 2 || g == 4 || g == 8)) return PA_ERR_UNSUPPORTED;
+  // 16 only where the matrix-core path runs (checked by the callers)
+  if (!(g == 1 || g == 2 || g == 4 || g == 8 || g == 16)) return PA_ERR_UNSUPPORTED;
   if (!(q_dtype == PA_F32 || q_dtype == PA_F16 || q_dtype == PA_BF16)) return PA_ERR_INVALID_ARG;
   const bool pair_ok = (c->dtype == q_dtype) || (c->dtype == PA_FP8_E4M3);
   if (!pair_ok) return PA_ERR_UNSUPPORTED;
@@ -160,6 +161,7 @@ pa_status plan_decode(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dt
         ws_layout(rows, c->head_dim, (size_t)plan->sk_blocks * 4).total;
     return PA_OK;
   }
+  if (g > 8) return PA_ERR_UNSUPPORTED;                      // the VALU kernel's limit
   plan->sk_blocks = 0;
   plan->part_tokens = choose_part_tokens(c, g, num_seqs, max_ctx);
   plan->num_parts = std::max(1, (max_ctx + plan->part_tokens - 1) / plan->part_tokens);

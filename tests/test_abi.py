@@ -76,7 +76,10 @@ def test_decode_argument_errors(pa_lib):
     c = _cache()
     assert _decode(pa_lib, c, seqs=0) == B.PA_OK                      # nothing to do
     assert _decode(pa_lib, c, hq=30) == B.PA_ERR_INVALID_ARG          # not a multiple of 8
-    assert _decode(pa_lib, c, hq=8 * 16) == B.PA_ERR_UNSUPPORTED      # group of 16
+    assert _decode(pa_lib, c, hq=8 * 16) == B.PA_ERR_WORKSPACE        # group of 16: matrix cores
+    assert _decode(pa_lib, c, hq=8 * 32) == B.PA_ERR_UNSUPPORTED      # group of 32
+    f32 = _cache(dtype=B.PA_F32, dim=64, heads=4)
+    assert _decode(pa_lib, f32, q_dtype=B.PA_F32, hq=4 * 16) == B.PA_ERR_UNSUPPORTED   # VALU: <= 8
     assert _decode(pa_lib, c, q_dtype=B.PA_F16) == B.PA_ERR_UNSUPPORTED
     assert _decode(pa_lib, c, layer=1) == B.PA_ERR_INVALID_ARG
     assert _decode(pa_lib, c, q=None) == B.PA_ERR_INVALID_ARG

@@ -183,3 +183,34 @@ def test_random_shape_prefill(seed):
     err = max_err_stored(got, ref, q)
     say(f"{int(qsl[-1])} rows, max error beyond output rounding {err:.3e}")
     assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
+
+
+@pytest.mark.parametrize("pool,q,D,hkv,B", [
+    ("bf16", "bf16", 128, 8, 16),
+    ("f16", "f16", 64, 1, 8),
+    ("fp8_e4m3", "bf16", 128, 2, 32),
+    ("fp8_e4m3", "f16", 64, 3, 1),
+])
+def test_group_of_16_decode(pool, q, D, hkv, B):
+    """Sixteen query heads per KV head (the whole matrix-core tile holds one
+    group, no padding columns)."""
+    r = np.random.default_rng(hkv * 131 + B)
+    S = 20
+    ctx = np.concatenate([r.integers(1, 40, 10), r.integers(200, 1500, 10)]).astype(np.int64)
+    while ctx.sum() * 16 * hkv > BUDGET:
+        ctx = np.maximum(ctx // 2, 1)
+    wl = workloads.custom(int(hkv * 17 + B), ctx, pool_dtype=pool, q_dtype=q,
+                          num_q_heads=16 * hkv, num_kv_heads=hkv, head_dim=D, block_size=B)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    run = wl.context_lens.copy()
+    run[3] = 0
+    mc = int(wl.context_lens.max())
+    got = st.decode(ctx=run, max_ctx=mc)
+    assert np.array_equal(got, st.decode(ctx=run, max_ctx=mc, split=True))
+    assert np.all(got[3] == 0)
+    live = [s for s in range(S) if run[s] > 0]
+    ref = st.oracle_decode(ctx=run, seqs=live)
+    err = max_err_stored(got, ref, q, rows=live)
+    say(f"{S} sequences, max error beyond output rounding {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
