@@ -531,7 +531,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the library has no multi-GPU path; each GPU would decode its own share)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import paged_kv_cache_44_amd as pa
