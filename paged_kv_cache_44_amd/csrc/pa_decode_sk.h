@@ -604,11 +604,13 @@ attend_sk_kernel(const DecodeParams a) {
 // merges KV head i of the group of the segment recorded by team t (if any),
 // over its pieces from teams t .. r1. Threads form PG groups, each covering
 // all GC x D outputs (DPT dims per thread) over every PG-th piece with a
-// running (online) combination; the groups are combined in LDS. (The prefix
-// pass of the shared-prefix decode has no merge: the suffix pass combines
-// its pieces.)
-template <Ty QT, int D, int G, int MODE>
-__global__ void __launch_bounds__(256)
+// running (online) combination; the groups are combined in LDS. NT threads:
+// 256, or 64 (one group, no LDS step, a quarter of the waves to dispatch)
+// when segments average under 4 pieces, as in batches of many sequences.
+// (The prefix pass of the shared-prefix decode has no merge: the suffix pass
+// combines its pieces.)
+template <Ty QT, int D, int G, int MODE, int NT = 256>
+__global__ void __launch_bounds__(NT)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
   static_assert(MODE != M_PREFIX, "prefix pieces are combined by the suffix pass");
   constexpr int GC = G;
@@ -616,8 +618,8 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
   constexpr int DPT = GD >= 1024 ? 16 : (GD >= 512 ? 8 : 4);   // dims per thread
   constexpr int NV4 = DPT / 4;
   constexpr int TPG = GD / DPT;                        // threads per group
-  static_assert(TPG <= 256 && 256 % TPG == 0, "group size");
-  constexpr int PG = 256 / TPG;                        // piece groups
+  static_assert(TPG <= NT && NT % TPG == 0, "group size");
+  constexpr int PG = NT / TPG;                         // piece groups
   __shared__ float s_m[PG][GC], s_l[PG][GC];
   __shared__ float s_o[PG > 1 ? PG : 1][GD];
 
@@ -793,14 +795,25 @@ static int sk_blocks_mode(int kv_ty, int q_ty, int head_dim, int g, int num_seqs
   return by_d(F8{}, BF{});
 }
 
+template <Ty QT, int D, int G, int MODE>
+static void sk_launch_merge_t(const DecodeParams& a, int64_t W, bool lean, hipStream_t st) {
+  const dim3 grid((unsigned)(W / a.team), (unsigned)a.team);
+  if (lean)
+    hipLaunchKernelGGL((merge_sk_kernel<QT, D, G, MODE, 64>), grid, dim3(64), 0, st, a, W);
+  else
+    hipLaunchKernelGGL((merge_sk_kernel<QT, D, G, MODE, 256>), grid, dim3(256), 0, st, a, W);
+}
+
 template <Ty QT, int D, int MODE>
 static hipError_t sk_launch_merge_d(const DecodeParams& a, int64_t W, int g, hipStream_t st) {
   dim3 grid((unsigned)(W / a.team), (unsigned)a.team);
+  const int64_t segs = (int64_t)a.num_seqs * (a.num_kv_heads / a.team);
+  const bool lean = W / a.team < 4 * segs;            // segments average under 4 pieces
   switch (g) {
-    case 1: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 1, MODE>), grid, dim3(256), 0, st, a, W); break;
-    case 2: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 2, MODE>), grid, dim3(256), 0, st, a, W); break;
-    case 4: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 4, MODE>), grid, dim3(256), 0, st, a, W); break;
-    case 8: hipLaunchKernelGGL((merge_sk_kernel<QT, D, 8, MODE>), grid, dim3(256), 0, st, a, W); break;
+    case 1: sk_launch_merge_t<QT, D, 1, MODE>(a, W, lean, st); break;
+    case 2: sk_launch_merge_t<QT, D, 2, MODE>(a, W, lean, st); break;
+    case 4: sk_launch_merge_t<QT, D, 4, MODE>(a, W, lean, st); break;
+    case 8: sk_launch_merge_t<QT, D, 8, MODE>(a, W, lean, st); break;
     case 16:
       if constexpr (MODE == M_PLAIN) {
         hipLaunchKernelGGL((merge_sk_kernel<QT, D, 16, MODE>), grid, dim3(256), 0, st, a, W);
