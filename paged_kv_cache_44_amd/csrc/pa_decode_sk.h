@@ -660,26 +660,56 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     }
     M = mn;
   };
-  // pieces of teams t0 + grp, t0 + grp + PG, ...; U loads in flight per group
-  // (every nonempty team in t0 .. t1 holds a piece: the segment covers it)
+  // pieces of teams t0 + grp, t0 + grp + PG, ...; U pieces per round per
+  // group (every nonempty team in t0 .. t1 holds a piece: the segment covers
+  // it). The 256-thread form, which takes the long segments, issues the next
+  // round's loads before this round is combined; every round loads (a lane
+  // past the segment's last piece reads team t0's piece, always written, and
+  // drops it), so the waits never cover the next round. The 64-thread form's
+  // segments have a round or two: it loads and combines round by round.
   constexpr int U = 4;
-  for (int64_t tb = t0 + grp; tb <= t1; tb += (int64_t)PG * U) {
-    float mv[U], lv[U];
-    float4 ov[U][NV4];
+  const int64_t safe = ((t0 + cseg) * T + ti) * GC + h;
+  auto fetch = [&](int64_t tb, float (&mv)[U], float (&lv)[U], float4 (&ov)[U][NV4])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t tm = tb + (int64_t)u * PG;
       const bool ok = tm <= t1 && (Cs == 0 || team_begin(tm, Cs, Wt) != team_begin(tm + 1, Cs, Wt));
-      const int64_t slot = ((tm + cseg) * T + ti) * GC + h;
-      mv[u] = ok ? a.ws_m[slot] : -__builtin_inff();
-      lv[u] = ok ? a.ws_l[slot] : 0.f;
+      const int64_t slot = ok ? ((tm + cseg) * T + ti) * GC + h : safe;
+      const float m = a.ws_m[slot], l = a.ws_l[slot];
+      mv[u] = ok ? m : -__builtin_inff();
+      lv[u] = ok ? l : 0.f;
 #pragma unroll
-      for (int v = 0; v < NV4; ++v)
-        ov[u][v] = ok ? reinterpret_cast<const float4*>(a.ws_o + slot * D + d0)[v]
-                      : make_float4(0, 0, 0, 0);
+      for (int v = 0; v < NV4; ++v) {
+        const float4 o = reinterpret_cast<const float4*>(a.ws_o + slot * D + d0)[v];
+        ov[u][v] = ok ? o : make_float4(0, 0, 0, 0);
+      }
     }
+  };
+  if constexpr (NT == 64) {
+    for (int64_t tb = t0 + grp; tb <= t1; tb += (int64_t)PG * U) {
+      float mv[U], lv[U];
+      float4 ov[U][NV4];
+      fetch(tb, mv, lv, ov);
 #pragma unroll
-    for (int u = 0; u < U; ++u) combine(mv[u], lv[u], ov[u]);
+      for (int u = 0; u < U; ++u) combine(mv[u], lv[u], ov[u]);
+    }
+  } else {
+  float mA[U], lA[U], mB[U], lB[U];
+  float4 oA[U][NV4], oB[U][NV4];
+  int64_t tb = t0 + grp;
+  fetch(tb, mA, lA, oA);
+  while (tb <= t1) {
+    fetch(tb + (int64_t)PG * U, mB, lB, oB);
+#pragma unroll
+    for (int u = 0; u < U; ++u) combine(mA[u], lA[u], oA[u]);
+    tb += (int64_t)PG * U;
+    if (tb > t1) break;
+    fetch(tb + (int64_t)PG * U, mA, lA, oA);
+#pragma unroll
+    for (int u = 0; u < U; ++u) combine(mB[u], lB[u], oB[u]);
+    tb += (int64_t)PG * U;
+  }
   }
   if constexpr (PG > 1) {
     if (d0 == 0) { s_m[grp][h] = M; s_l[grp][h] = L; }
