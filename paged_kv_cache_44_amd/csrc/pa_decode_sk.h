@@ -609,7 +609,7 @@ attend_sk_kernel(const DecodeParams a) {
 // when segments average under 4 pieces, as in batches of many sequences.
 // (The prefix pass of the shared-prefix decode has no merge: the suffix pass
 // combines its pieces.)
-template <Ty QT, int D, int G, int MODE, int NT = 256>
+template <Ty QT, int D, int G, int MODE, int NT = 256, bool BYSEG = false>
 __global__ void __launch_bounds__(NT)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
   static_assert(MODE != M_PREFIX, "prefix pieces are combined by the suffix pass");
@@ -623,15 +623,46 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
   __shared__ float s_m[PG][GC], s_l[PG][GC];
   __shared__ float s_o[PG > 1 ? PG : 1][GD];
 
-  const int64_t t0 = blockIdx.x;
+  static_assert(!BYSEG || MODE == M_PLAIN, "segment-indexed merge of the plain decode only");
   const int ti = blockIdx.y;
-  const int4 md = reinterpret_cast<const int4*>(a.ws_team)[t0];
-  const int64_t t1 = md.x;
-  if (t1 <= t0) return;                                // no segment to merge here
   const int T = a.team;
   const int HG = a.num_kv_heads / T;
   const int64_t Wt = W / T;
-  const int seq = md.y, hg = md.z;
+  int64_t t0, t1, Cs;
+  int seq, hg;
+  if constexpr (BYSEG) {
+    // workgroup x merges segment x (sequence x / HG, head group x % HG) of
+    // a batch of at most 64 sequences: every wave counts the sequences'
+    // chunks as the attention kernel does and finds the teams holding the
+    // segment's first and last columns (segments lie end to end,
+    // sequence-major)
+    seq = (int)(blockIdx.x / HG);
+    hg = (int)(blockIdx.x - (unsigned)seq * HG);
+    const int lane = threadIdx.x & 63;
+    const int v = lane < a.num_seqs ? seq_chunks(a, a.context_lens[lane]) : 0;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    const int nc = __shfl(v, seq);
+    if (nc == 0) return;                               // nothing to attend to (uniform)
+    const int64_t Cc = (int64_t)__shfl(x, 63) * HG;
+    const int64_t c0 = (int64_t)(__shfl(x, seq) - nc) * HG + (int64_t)hg * nc;
+    t0 = team_of(c0, Cc, Wt);
+    t1 = team_of(c0 + nc - 1, Cc, Wt);
+    if (t1 <= t0) return;                              // one team: written by the attention kernel
+    Cs = Cc < Wt ? Cc : 0;
+  } else {
+    t0 = blockIdx.x;
+    const int4 md = reinterpret_cast<const int4*>(a.ws_team)[t0];
+    t1 = md.x;
+    if (t1 <= t0) return;                              // no segment to merge here
+    seq = md.y;
+    hg = md.z;
+    Cs = md.w;                                         // nonzero: some team ranges are empty
+  }
   const int kvh = hg * T + ti;
   const int tid = threadIdx.x;
   const int grp = tid / TPG;
@@ -640,7 +671,6 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
   const int d0 = (t - h * (D / DPT)) * DPT;
   const int64_t orow = ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h) * D + d0;
   const int64_t cseg = (int64_t)seq * HG + hg;
-  const int64_t Cs = md.w;                             // nonzero: some team ranges are empty
 
   float M = -__builtin_inff(), L = 0.f, O[DPT];
 #pragma unroll
@@ -828,6 +858,16 @@ static int sk_blocks_mode(int kv_ty, int q_ty, int head_dim, int g, int num_seqs
 template <Ty QT, int D, int G, int MODE>
 static void sk_launch_merge_t(const DecodeParams& a, int64_t W, bool lean, hipStream_t st) {
   const dim3 grid((unsigned)(W / a.team), (unsigned)a.team);
+  const int64_t segs = (int64_t)a.num_seqs * (a.num_kv_heads / a.team);
+  if constexpr (MODE == M_PLAIN) {
+    // few, long segments: one workgroup per (segment, KV head) instead of
+    // one per (team, KV head), almost all of which would find nothing
+    if (a.num_seqs <= 64 && segs > 0 && W / a.team >= 16 * segs) {
+      hipLaunchKernelGGL((merge_sk_kernel<QT, D, G, MODE, 256, true>), dim3((unsigned)segs, (unsigned)a.team),
+                         dim3(256), 0, st, a, W);
+      return;
+    }
+  }
   if (lean)
     hipLaunchKernelGGL((merge_sk_kernel<QT, D, G, MODE, 64>), grid, dim3(64), 0, st, a, W);
   else
