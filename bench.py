@@ -612,10 +612,16 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
+    # the attention kernel's own duration: the same K steps again, with HIP
+    # events on the launch stream around every attention launch (recording
+    # an event costs the stream ~3 us, so the timed steps above carry none)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
     attend_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     # flushed per-call decode time: a 512 MiB scratch write evicts the L2s and
