@@ -214,3 +214,39 @@ def test_group_of_16_decode(pool, q, D, hkv, B):
     err = max_err_stored(got, ref, q, rows=live)
     say(f"{S} sequences, max error beyond output rounding {err:.3e}")
     assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
+
+
+@pytest.mark.parametrize("pool,q", [("bf16", "bf16"), ("fp8_e4m3", "f16"), ("f32", "f32")])
+def test_block_size_256(pool, q):
+    """The largest block size the pool takes: decode (both forms) and, for
+    the matrix-core dtypes, prefill."""
+    D = 64 if pool == "f32" else 128
+    ctx = np.array([1, 255, 256, 257, 700, 1300, 40, 512])
+    wl = workloads.custom(256, ctx, pool_dtype=pool, q_dtype=q, num_q_heads=8, num_kv_heads=2,
+                          head_dim=D, block_size=256)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    assert st.pools_equal_oracle()[0]
+    got = st.decode()
+    assert np.array_equal(got, st.decode(split=True))
+    ref = st.oracle_decode()
+    err = _err(got, ref, q, None)
+    say(f"decode max error {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
+    if pool == "f32":
+        return
+    nq = [1, 255, 3, 257, 1, 600, 40, 0]
+    qc, qsl = workloads.prefill_queries(wl, nq, 257)
+    qt = codes_to_tensor(qc, q)
+    out = torch.empty_like(qt)
+    tt = torch.from_numpy(np.ascontiguousarray(wl.block_tables, dtype=np.int32)).cuda()
+    ct = torch.from_numpy(np.ascontiguousarray(wl.context_lens, dtype=np.int32)).cuda()
+    qs = torch.from_numpy(np.ascontiguousarray(qsl, dtype=np.int32)).cuda()
+    pa.prefill(st.cache, wl.layer, qt, tt, ct, int(ctx.max()), qs, max(nq), wl.scale, out=out)
+    torch.cuda.synchronize()
+    got = codecs.decode(tensor_codes(out), q)
+    ref = paged.prefill(qc, q, st.ok, st.ov, st.geom, pool, wl.layer, wl.block_tables,
+                        wl.context_lens, qsl, wl.scale, wl.k_scale, wl.v_scale)
+    err = max_err_stored(got, ref, q)
+    say(f"prefill max error beyond output rounding {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
