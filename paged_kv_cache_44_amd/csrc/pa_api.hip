@@ -294,16 +294,20 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
     a.ws_team = reinterpret_cast<int32_t*>(w + L.team);
 
   }
+  // the same launch size for both phases (a function of the call's sizes)
+  const int blocks = plan.mfma ? pa::sk_launch_blocks(plan.sk_blocks, num_seqs, max_context_len,
+                                                      cache->num_kv_heads)
+                               : 0;
   if (phases & PHASE_ATTEND) {
     const hipError_t e =
         plan.mfma ? pa::launch_attend_mfma(a, (int)cache->dtype, (int)q_dtype, plan.g,
-                                           plan.sk_blocks, stream)
+                                           blocks, stream)
                   : pa::launch_attend(a, (int)cache->dtype, (int)q_dtype, plan.g, stream);
     if (e != hipSuccess) return PA_ERR_HIP;
   }
   if (phases & PHASE_MERGE) {
     if (plan.mfma) {
-      if (pa::launch_merge_mfma(a, (int)q_dtype, plan.g, plan.sk_blocks, stream) != hipSuccess)
+      if (pa::launch_merge_mfma(a, (int)q_dtype, plan.g, blocks, stream) != hipSuccess)
         return PA_ERR_HIP;
     } else if (plan.num_parts > 1) {
       if (pa::launch_merge(a, (int)q_dtype, stream) != hipSuccess) return PA_ERR_HIP;

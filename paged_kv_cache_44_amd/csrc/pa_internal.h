@@ -139,6 +139,7 @@ hipError_t launch_attend(const DecodeParams& a, int kv_ty, int q_ty, int g, hipS
 hipError_t launch_merge(const DecodeParams& a, int q_ty, hipStream_t st);
 bool mfma_supported(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
 int sk_blocks(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
+int sk_launch_blocks(int blocks_max, int num_seqs, int max_ctx, int num_kv_heads);
 size_t sk_slots(int blocks, int num_seqs, int num_kv_heads);
 int sk_team(int num_kv_heads);
 hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
