@@ -607,13 +607,16 @@ attend_sk_kernel(const DecodeParams a) {
 // running (online) combination; the groups are combined in LDS. NT threads:
 // 256, or 64 (one group, no LDS step, a quarter of the waves to dispatch)
 // when segments average under 4 pieces, as in batches of many sequences.
+// SPLITH: one query head per workgroup (grid z), so a few long segments
+// spread over G times the workgroups, each with G times the piece groups.
 // (The prefix pass of the shared-prefix decode has no merge: the suffix pass
 // combines its pieces.)
-template <Ty QT, int D, int G, int MODE, int NT = 256, bool BYSEG = false>
+template <Ty QT, int D, int G, int MODE, int NT = 256, bool BYSEG = false, bool SPLITH = false>
 __global__ void __launch_bounds__(NT)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
   static_assert(MODE != M_PREFIX, "prefix pieces are combined by the suffix pass");
-  constexpr int GC = G;
+  static_assert(!SPLITH || BYSEG, "one query head per workgroup: segment-indexed merge only");
+  constexpr int GC = SPLITH ? 1 : G;                   // query heads per workgroup
   constexpr int GD = GC * D;
   constexpr int DPT = GD >= 1024 ? 16 : (GD >= 512 ? 8 : 4);   // dims per thread
   constexpr int NV4 = DPT / 4;
@@ -667,8 +670,9 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
   const int tid = threadIdx.x;
   const int grp = tid / TPG;
   const int t = tid - grp * TPG;
-  const int h = t / (D / DPT);
-  const int d0 = (t - h * (D / DPT)) * DPT;
+  const int hl = t / (D / DPT);                        // head within the workgroup's
+  const int h = hl + (SPLITH ? (int)blockIdx.z : 0);   // head within the KV head's group
+  const int d0 = (t - hl * (D / DPT)) * DPT;
   const int64_t orow = ((int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h) * D + d0;
   const int64_t cseg = (int64_t)seq * HG + hg;
 
@@ -698,14 +702,14 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
   // drops it), so the waits never cover the next round. The 64-thread form's
   // segments have a round or two: it loads and combines round by round.
   constexpr int U = 4;
-  const int64_t safe = ((t0 + cseg) * T + ti) * GC + h;
+  const int64_t safe = ((t0 + cseg) * T + ti) * G + h;
   auto fetch = [&](int64_t tb, float (&mv)[U], float (&lv)[U], float4 (&ov)[U][NV4])
       __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t tm = tb + (int64_t)u * PG;
       const bool ok = tm <= t1 && (Cs == 0 || team_begin(tm, Cs, Wt) != team_begin(tm + 1, Cs, Wt));
-      const int64_t slot = ok ? ((tm + cseg) * T + ti) * GC + h : safe;
+      const int64_t slot = ok ? ((tm + cseg) * T + ti) * G + h : safe;
       const float m = a.ws_m[slot], l = a.ws_l[slot];
       mv[u] = ok ? m : -__builtin_inff();
       lv[u] = ok ? l : 0.f;
@@ -742,9 +746,9 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
   }
   }
   if constexpr (PG > 1) {
-    if (d0 == 0) { s_m[grp][h] = M; s_l[grp][h] = L; }
+    if (d0 == 0) { s_m[grp][hl] = M; s_l[grp][hl] = L; }
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) s_o[grp][h * D + d0 + e] = O[e];
+    for (int e = 0; e < DPT; ++e) s_o[grp][hl * D + d0 + e] = O[e];
     __syncthreads();
     if (grp != 0) return;
     M = -__builtin_inff(); L = 0.f;
@@ -752,7 +756,7 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     for (int e = 0; e < DPT; ++e) O[e] = 0.f;
 #pragma unroll
     for (int q = 0; q < PG; ++q)
-      combine(s_m[q][h], s_l[q][h], reinterpret_cast<const float4*>(&s_o[q][h * D + d0]));
+      combine(s_m[q][hl], s_l[q][hl], reinterpret_cast<const float4*>(&s_o[q][hl * D + d0]));
   }
   const float norm = a.v_scale / L;
 #pragma unroll
@@ -860,11 +864,12 @@ static void sk_launch_merge_t(const DecodeParams& a, int64_t W, bool lean, hipSt
   const dim3 grid((unsigned)(W / a.team), (unsigned)a.team);
   const int64_t segs = (int64_t)a.num_seqs * (a.num_kv_heads / a.team);
   if constexpr (MODE == M_PLAIN) {
-    // few, long segments: one workgroup per (segment, KV head) instead of
-    // one per (team, KV head), almost all of which would find nothing
+    // few, long segments: one workgroup per (segment, KV head, query head)
+    // instead of one per (team, KV head), almost all of which would find
+    // nothing
     if (a.num_seqs <= 64 && segs > 0 && W / a.team >= 16 * segs) {
-      hipLaunchKernelGGL((merge_sk_kernel<QT, D, G, MODE, 256, true>), dim3((unsigned)segs, (unsigned)a.team),
-                         dim3(256), 0, st, a, W);
+      hipLaunchKernelGGL((merge_sk_kernel<QT, D, G, MODE, 256, true, true>),
+                         dim3((unsigned)segs, (unsigned)a.team, G), dim3(256), 0, st, a, W);
       return;
     }
   }
