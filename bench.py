@@ -24,6 +24,7 @@ import json
 import os
 import sys
 import time
+import types
 
 import numpy as np
 
@@ -82,6 +83,9 @@ def parse():
                     help="time paged prefill: the GQA bf16 workload's contexts prefilled whole, "
                          "and the long FP8 workload's 1,500-token victim recomputed; one JSON "
                          "line each")
+    ap.add_argument("--block-size-sweep", action="store_true",
+                    help="the GQA bf16 decode step at block sizes 8..256: step and attention-kernel "
+                         "time, and the slots the blocks hold beyond the context (one JSON line each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) a few times: the "
                          "reference kernel for scaling HBM byte counters")
@@ -488,6 +492,95 @@ def prefill_bench(steps: int, warmup: int):
         del cache, q, out
 
 
+def decode_setup(wl, dev):
+    """Device pool filled with every context token (untimed, as the workload
+    prescribes), the step's write of each sequence's newest token, queries,
+    tables, lengths and the output."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+    pool = wl.empty_pool()
+    cache = pa.KVCache(codes_tensor(pool, wl.pool_dtype, dev), codes_tensor(pool, wl.pool_dtype, dev),
+                       wl.pool_dtype, wl.num_blocks, wl.num_layers, wl.num_kv_heads,
+                       wl.block_size, wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    for op in workloads.fill_plan(wl):
+        if op[0] == "write":
+            pa.write_kv(cache, wl.layer, codes_tensor(op[1], wl.src_dtype, dev),
+                        codes_tensor(op[2], wl.src_dtype, dev), torch.from_numpy(op[3]).to(dev))
+        else:
+            pa.copy_blocks(cache, cache, torch.from_numpy(op[1]).to(dev), "d2d")
+    # the step's own write: each sequence's newest token, stored again at its slot
+    step_idx = wl.step_token[wl.step_token >= 0]
+    q = codes_tensor(wl.q, wl.q_dtype, dev)
+    return types.SimpleNamespace(
+        cache=cache, step_idx=step_idx,
+        step_k=codes_tensor(wl.write_k[step_idx], wl.src_dtype, dev),
+        step_v=codes_tensor(wl.write_v[step_idx], wl.src_dtype, dev),
+        step_slots=torch.from_numpy(wl.write_slots[step_idx]).to(dev),
+        q=q, out=torch.empty_like(q), tables=torch.from_numpy(wl.block_tables).to(dev),
+        ctx=torch.from_numpy(wl.context_lens).to(dev), max_ctx=wl.max_context_len)
+
+
+def block_size_sweep(steps: int, warmup: int):
+    """Decode block-size sweep ("Efficient Memory Management for Large Language
+    Model Serving with PagedAttention", block-size paragraph: small blocks
+    give the kernel less to read per block-table entry, large ones leave more
+    of a sequence's last block empty). The GQA bf16 workload's lengths at
+    each block size: the whole step (newest-token write, attend, merge) timed
+    without events, the attention kernel from HIP events in a second pass,
+    and the slots the sequences' blocks hold beyond their contexts."""
+    import torch
+    import paged_kv_cache_44_amd as pa
+    import workloads
+    dev = torch.device("cuda:0")
+    rows = []
+    for B in (8, 16, 32, 64, 128, 256):
+        wl = workloads.config3(block_size=B)
+        print(f"[bench] block size {B}: {wl.num_blocks} blocks", file=sys.stderr, flush=True)
+        d = decode_setup(wl, dev)
+        S, Hq = wl.num_seqs, wl.num_q_heads
+        ws = torch.empty(max(1, pa.decode_workspace_size(d.cache, S, Hq, d.max_ctx)),
+                         dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+
+        def step(i=None):
+            pa.write_kv(d.cache, wl.layer, d.step_k, d.step_v, d.step_slots)
+            if i is not None:
+                ev[i][0].record()
+            pa.decode_attend(d.cache, wl.layer, d.q, d.tables, d.ctx, d.max_ctx, wl.scale, d.out, ws)
+            if i is not None:
+                ev[i][1].record()
+            pa.decode_merge(d.cache, wl.layer, d.q, d.tables, d.ctx, d.max_ctx, wl.scale, d.out, ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        attend_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        step_bytes = workloads.decode_bytes(wl) + workloads.write_bytes(wl, len(d.step_idx))
+        held = int(np.sum(-(-wl.context_lens.astype(np.int64) // B))) * B
+        used = int(wl.context_lens.sum())
+        rec = {"block_size": B, "ms_per_step": round(ms, 5),
+               "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+               "attend_ms": round(attend_ms, 5),
+               "attend_GBps": round(attend_bytes(wl) / (attend_ms * 1e-3) / 1e9, 2),
+               "slots_held": held, "slots_used": used,
+               "slots_unused_pct": round(100.0 * (held - used) / held, 2)}
+        print(json.dumps(rec), flush=True)
+        rows.append(rec)
+        del d, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(wl, target_s: float):
     """The oracle, as it is, on the host cores: its slot write builds the pool
     on the host, then its decode runs sequence by sequence (cycling through
@@ -549,6 +642,9 @@ def main():
         swap_sweep()
         swap_overlap()
         return
+    if args.block_size_sweep:
+        block_size_sweep(args.steps, args.warmup)
+        return
     if args.prefill:
         prefill_bench(args.steps if args.steps != 50 else 20, args.warmup if args.warmup != 10 else 3)
         return
@@ -559,27 +655,9 @@ def main():
           f"{wl.context_lens.mean():.1f} max {wl.max_context_len}, pool {wl.num_blocks} blocks",
           file=sys.stderr, flush=True)
 
-    pool = wl.empty_pool()
-    cache = pa.KVCache(codes_tensor(pool, wl.pool_dtype, dev), codes_tensor(pool, wl.pool_dtype, dev),
-                       wl.pool_dtype, wl.num_blocks, wl.num_layers, wl.num_kv_heads,
-                       wl.block_size, wl.head_dim, k_scale=wl.k_scale, v_scale=wl.v_scale)
-    # fill the pool (untimed) with every context token, as the workload prescribes
-    for op in workloads.fill_plan(wl):
-        if op[0] == "write":
-            pa.write_kv(cache, wl.layer, codes_tensor(op[1], wl.src_dtype, dev),
-                        codes_tensor(op[2], wl.src_dtype, dev), torch.from_numpy(op[3]).to(dev))
-        else:
-            pa.copy_blocks(cache, cache, torch.from_numpy(op[1]).to(dev), "d2d")
-    # the step's own write: each sequence's newest token, stored again at its slot
-    step_idx = wl.step_token[wl.step_token >= 0]
-    step_k = codes_tensor(wl.write_k[step_idx], wl.src_dtype, dev)
-    step_v = codes_tensor(wl.write_v[step_idx], wl.src_dtype, dev)
-    step_slots = torch.from_numpy(wl.write_slots[step_idx]).to(dev)
-    q = codes_tensor(wl.q, wl.q_dtype, dev)
-    out = torch.empty_like(q)
-    tables = torch.from_numpy(wl.block_tables).to(dev)
-    ctx = torch.from_numpy(wl.context_lens).to(dev)
-    max_ctx = wl.max_context_len
+    d = decode_setup(wl, dev)
+    cache, step_idx, step_k, step_v, step_slots = d.cache, d.step_idx, d.step_k, d.step_v, d.step_slots
+    q, out, tables, ctx, max_ctx = d.q, d.out, d.tables, d.ctx, d.max_ctx
     S, Hq = wl.num_seqs, wl.num_q_heads
     ws_n = (pa.decode_shared_workspace_size(cache, S, Hq) if args.shared
             else pa.decode_workspace_size(cache, S, Hq, max_ctx))

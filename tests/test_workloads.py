@@ -48,6 +48,18 @@ def test_config3_length_mix():
     assert wl.num_q_heads == 32 and wl.num_kv_heads == 8
 
 
+def test_config3_block_sizes_keep_the_lengths():
+    # the block-size sweep's layouts: the same lengths, disjoint blocks, and
+    # every slot inside the sequence's own blocks
+    base = workloads.config3(num_seqs=16)
+    for B in (8, 64, 256):
+        wl = workloads.config3(num_seqs=16, block_size=B)
+        assert wl.block_size == B and np.array_equal(wl.context_lens, base.context_lens)
+        used = _check_layout(wl)
+        assert len(np.unique(used)) == len(used)
+        assert np.all(np.isin(wl.write_slots // B, used))
+
+
 def test_config4_sharing_structure():
     wl = workloads.config4(groups=2, samples=8)
     used = _check_layout(wl)

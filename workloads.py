@@ -232,12 +232,13 @@ def gqa_lengths(rng, num_seqs: int, prompt_mean: float = 850.0, sigma: float = 0
     return (prompt + gen).astype(np.int32)
 
 
-def config3(seed: int = 3, num_seqs: int = 256) -> Workload:
-    """GQA bf16: 32/8 x 128, B 16, 256 sequences, ~850-token prompt + answer."""
+def config3(seed: int = 3, num_seqs: int = 256, block_size: int = 16) -> Workload:
+    """GQA bf16: 32/8 x 128, B 16 (other block sizes for the block-size sweep),
+    256 sequences, ~850-token prompt + answer."""
     rng = np.random.default_rng(seed)
     ctx = gqa_lengths(rng, num_seqs)
     return _paged_workload("gqa_bf16", seed, rng, ctx, pool_dtype=BF16, src_dtype=BF16,
-                           q_dtype=BF16, hq=32, hkv=8, d=128, B=16)
+                           q_dtype=BF16, hq=32, hkv=8, d=128, B=block_size)
 
 
 def config4(seed: int = 4, groups: int = 32, samples: int = 8, prefix_tokens: int = 1024,
