@@ -492,6 +492,21 @@ def prefill_bench(steps: int, warmup: int):
         del cache, q, out
 
 
+def launch_avg_ms(fn, reps: int) -> float:
+    """Mean duration of one launch of fn: reps launches back to back between
+    two HIP events on the launch stream (torch's current stream, which the
+    binding launches on), so the events' own cost is spread over reps."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def decode_setup(wl, dev):
     """Device pool filled with every context token (untimed, as the workload
     prescribes), the step's write of each sequence's newest token, queries,
@@ -527,7 +542,8 @@ def block_size_sweep(steps: int, warmup: int):
     give the kernel less to read per block-table entry, large ones leave more
     of a sequence's last block empty). The GQA bf16 workload's lengths at
     each block size: the whole step (newest-token write, attend, merge) timed
-    without events, the attention kernel from HIP events in a second pass,
+    without events, the attention kernel alone from HIP events around a run
+    of back-to-back launches,
     and the slots the sequences' blocks hold beyond their contexts."""
     import torch
     import paged_kv_cache_44_amd as pa
@@ -541,16 +557,12 @@ def block_size_sweep(steps: int, warmup: int):
         S, Hq = wl.num_seqs, wl.num_q_heads
         ws = torch.empty(max(1, pa.decode_workspace_size(d.cache, S, Hq, d.max_ctx)),
                          dtype=torch.uint8, device=dev)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-
-        def step(i=None):
-            pa.write_kv(d.cache, wl.layer, d.step_k, d.step_v, d.step_slots)
-            if i is not None:
-                ev[i][0].record()
+        def attend():
             pa.decode_attend(d.cache, wl.layer, d.q, d.tables, d.ctx, d.max_ctx, wl.scale, d.out, ws)
-            if i is not None:
-                ev[i][1].record()
+
+        def step():
+            pa.write_kv(d.cache, wl.layer, d.step_k, d.step_v, d.step_slots)
+            attend()
             pa.decode_merge(d.cache, wl.layer, d.q, d.tables, d.ctx, d.max_ctx, wl.scale, d.out, ws)
 
         for _ in range(warmup):
@@ -561,10 +573,7 @@ def block_size_sweep(steps: int, warmup: int):
             step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
-        for i in range(steps):
-            step(i)
-        torch.cuda.synchronize()
-        attend_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        attend_ms = launch_avg_ms(attend, steps)
         step_bytes = workloads.decode_bytes(wl) + workloads.write_bytes(wl, len(d.step_idx))
         held = int(np.sum(-(-wl.context_lens.astype(np.int64) // B))) * B
         used = int(wl.context_lens.sum())
@@ -667,23 +676,18 @@ def main():
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; partition {part} tokens",
           file=sys.stderr, flush=True)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-
-    def step(i=None):
-        pa.write_kv(cache, wl.layer, step_k, step_v, step_slots)
-        if i is not None:
-            ev[i][0].record()
+    def attend():
         if args.shared:     # planning, prefix pass, suffix pass and merges: all timed
             pa.decode_shared(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out=out,
                              workspace=ws)
-            if i is not None:
-                ev[i][1].record()
-            return
-        pa.decode_attend(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
-        if i is not None:
-            ev[i][1].record()
-        pa.decode_merge(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
+        else:
+            pa.decode_attend(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
+
+    def step():
+        pa.write_kv(cache, wl.layer, step_k, step_v, step_slots)
+        attend()
+        if not args.shared:
+            pa.decode_merge(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
 
     for _ in range(args.warmup):
         step()
@@ -694,13 +698,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    # the attention kernel's own duration: the same K steps again, with HIP
-    # events on the launch stream around every attention launch (recording
-    # an event costs the stream ~3 us, so the timed steps above carry none)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    attend_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # the attention kernel's own duration (the timed steps above carry no
+    # events: recording one costs the stream ~3 us)
+    attend_ms = launch_avg_ms(attend, args.steps)
 
     # flushed per-call decode time: a 512 MiB scratch write evicts the L2s and
     # the Infinity Cache before each call (untimed)
