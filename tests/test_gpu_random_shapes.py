@@ -250,3 +250,41 @@ def test_block_size_256(pool, q):
     err = max_err_stored(got, ref, q)
     say(f"prefill max error beyond output rounding {err:.3e}")
     assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
+
+
+SMALL_BATCHES = [
+    ("bf16", "bf16", 128, 4, 8, [1000]),
+    ("bf16", "bf16", 128, 4, 8, [7000]),
+    ("fp8_e4m3", "bf16", 128, 8, 2, [6000, 7000]),
+    ("f16", "f16", 64, 1, 4, [1, 17, 30000]),
+    ("f16", "f16", 128, 2, 1, [40000, 3, 60000]),
+    ("bf16", "bf16", 64, 16, 2, [5000]),
+    ("fp8_e4m3", "f16", 64, 2, 3, [1, 2, 3, 4, 5, 6, 7, 8]),
+    ("f16", "f16", 128, 8, 4, [16, 17, 15, 1, 2000, 33]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_BATCHES)))
+def test_small_batch_grids(case):
+    """Batches of a few sequences: the call launches only as many workgroups
+    as its chunk count needs (sized from max_context_len), and few long
+    segments are merged one workgroup per (segment, KV head, query head).
+    The same batch decoded with a 4x larger max_context_len (a larger grid,
+    a different split) must match the oracle as well."""
+    pool, q, D, G, hkv, ctx = SMALL_BATCHES[case]
+    ctx = np.asarray(ctx, dtype=np.int64)
+    assert ctx.sum() * G * hkv <= BUDGET
+    say(f"pool {pool} q {q} D {D} G {G} H_kv {hkv} contexts {ctx.tolist()}")
+    wl = workloads.custom(900 + case, ctx, pool_dtype=pool, q_dtype=q, num_q_heads=G * hkv,
+                          num_kv_heads=hkv, head_dim=D, block_size=16)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    mc = int(ctx.max())
+    live = list(range(len(ctx)))
+    ref = st.oracle_decode(seqs=live)
+    for bound in (mc, 4 * mc):
+        got = st.decode(max_ctx=bound)
+        assert np.array_equal(got, st.decode(max_ctx=bound, split=True))
+        err = max_err_stored(got, ref, q, rows=live)
+        say(f"max_context_len {bound}: error beyond output rounding {err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= _tol(pool, q)
