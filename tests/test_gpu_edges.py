@@ -519,3 +519,62 @@ def test_repeat_calls_on_junk_workspace_are_identical(cfg):
     tol = TOL["fp8_e4m3"] if wl.pool_dtype == "fp8_e4m3" else TOL[wl.q_dtype]
     say(f"config {cfg}: error beyond output rounding {ex:.3e}")
     assert ex <= tol
+
+
+@pytest.mark.parametrize("pool,q", [("bf16", "bf16"), ("fp8_e4m3", "bf16")])
+def test_graph_replay_of_a_decode_step_matches_eager(pool, q):
+    """A decode step (newest-token write, attend, merge) captured once in a
+    HIP graph: the library's launches go to the capture stream, allocate
+    nothing and issue no memsets. Every replay, with eager steps and
+    synchronisations between replays, gives the eager step's output bit for
+    bit, and that output matches the oracle."""
+    ctx = np.array([1, 15, 16, 17, 300, 2500, 900, 64, 4100, 33], dtype=np.int64)
+    wl = workloads.custom(31, ctx, pool_dtype=pool, q_dtype=q, num_q_heads=32, num_kv_heads=8,
+                          head_dim=128, block_size=16)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    S, Hq = wl.num_seqs, wl.num_q_heads
+    mc = int(ctx.max())
+    qt = codes_to_tensor(wl.q, q)
+    tt = torch.from_numpy(wl.block_tables).cuda()
+    ct = torch.from_numpy(wl.context_lens).cuda()
+    out = torch.empty_like(qt)
+    ws = torch.full((pa.decode_workspace_size(st.cache, S, Hq, mc),), 0x5a, dtype=torch.uint8,
+                    device="cuda")
+    last = wl.step_token[wl.step_token >= 0]
+    sk = codes_to_tensor(wl.write_k[last], wl.src_dtype)
+    sv = codes_to_tensor(wl.write_v[last], wl.src_dtype)
+    ss = torch.from_numpy(wl.write_slots[last]).cuda()
+
+    def step():
+        pa.write_kv(st.cache, wl.layer, sk, sv, ss)
+        pa.decode_attend(st.cache, wl.layer, qt, tt, ct, mc, wl.scale, out, ws)
+        pa.decode_merge(st.cache, wl.layer, qt, tt, ct, mc, wl.scale, out, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        ws.fill_(0x5a)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"eager step after replay {r}"
+    live = list(range(S))
+    ref = st.oracle_decode(seqs=live)
+    err = max_err_stored(codecs.decode(tensor_codes(out), q), ref, q, rows=live)
+    tol = TOL["fp8_e4m3"] if pool == "fp8_e4m3" else TOL[q]
+    say(f"{pool}: error beyond output rounding {err:.3e}")
+    assert err <= tol
