@@ -181,7 +181,9 @@ pa_status pa_write_kv(const pa_kv_cache* cache, int32_t layer, const void* k,
 /* pa_decode is exactly pa_decode_attend followed by pa_decode_merge with    */
 /* the same arguments. The split lets a caller time or schedule the two      */
 /* launches separately; pa_decode_merge must follow pa_decode_attend on the  */
-/* same stream with unchanged inputs and workspace.                          */
+/* same stream with unchanged inputs and workspace (num_seqs and             */
+/* max_context_len also set how many workgroups both launch: a merge given   */
+/* other values gives undefined output rows, though it stays in bounds).     */
 /* ------------------------------------------------------------------------ */
 pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q,
                     pa_dtype q_dtype, void* out, const int32_t* block_tables,

@@ -665,6 +665,10 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     seq = md.y;
     hg = md.z;
     Cs = md.w;                                         // nonzero: some team ranges are empty
+    // a descriptor the attention launch did not write (a merge launched with
+    // other sizes than it) is dropped rather than followed out of range
+    if (t1 >= Wt || seq < 0 || seq >= a.num_seqs || hg < 0 || hg >= HG || Cs < 0 || Cs >= Wt)
+      return;
   }
   const int kvh = hg * T + ti;
   const int tid = threadIdx.x;
