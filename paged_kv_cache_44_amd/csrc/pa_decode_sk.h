@@ -602,11 +602,12 @@ attend_sk_kernel(const DecodeParams a) {
 // Merge of segments cut by team range boundaries: M = max_p m_p,
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p. Workgroup (t, i)
 // merges KV head i of the group of the segment recorded by team t (if any),
-// over its pieces from teams t .. r1. Threads form PG groups, each covering
-// all GC x D outputs (DPT dims per thread) over every PG-th piece with a
-// running (online) combination; the groups are combined in LDS. NT threads:
-// 256, or 64 (one group, no LDS step, a quarter of the waves to dispatch)
-// when segments average under 4 pieces, as in batches of many sequences.
+// over its pieces from teams t .. t1 (the last team the segment reaches).
+// Threads form PG groups, each covering all GC x D outputs (DPT dims per
+// thread) over every PG-th piece with a running (online) combination; the
+// groups are combined in LDS. NT threads: 256, or 64 (one group, no LDS
+// step, a quarter of the waves to dispatch) when segments average under 4
+// pieces, as in batches of many sequences.
 // SPLITH: one query head per workgroup (grid z), so a few long segments
 // spread over G times the workgroups, each with G times the piece groups.
 // (The prefix pass of the shared-prefix decode has no merge: the suffix pass
