@@ -83,7 +83,14 @@ pa_status pa_bm_append(pa_bm* bm, int64_t seq, int32_t n, int64_t* slots, int64_
 int32_t pa_bm_blocks_needed(const pa_bm* bm, int64_t seq, int32_t n);
 
 /* Copy-on-write of the last block now, even if full (privatising a shared
- * last block up front). pair[0], pair[1] = (src, dst). */
+ * last block up front; "Efficient Memory Management for Large Language Model
+ * Serving with PagedAttention", sampling paragraph). pair[0], pair[1] =
+ * (src, dst): dst is taken from the head of the free list and replaces src as
+ * the sequence's last table entry; src loses this sequence's one reference.
+ * The caller copies src into dst (pa_copy_blocks, PA_COPY_D2D) before writing
+ * into it. PA_ERR_INVALID_ARG (nothing changed) when the sequence is unknown,
+ * not running, holds no block, or is the only holder of its last block;
+ * PA_ERR_NO_SPACE when no device block is free. */
 pa_status pa_bm_copy_last_block(pa_bm* bm, int64_t seq, int64_t* pair);
 
 /* Release every block of a sequence and forget it (finished, or preempted to

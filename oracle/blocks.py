@@ -143,7 +143,15 @@ class Sequence:
     def copy_last_block(self):
         """Copy-on-write of the last block now, even if it is full (used for a
         workload that privatises the last shared block up front). Returns the
-        (src, dst) pair."""
+        (src, dst) pair: dst is a freshly allocated block (reference count 1)
+        that replaces src as the table's last entry, and src loses exactly the
+        one reference this sequence held. Only a shared block is copied ("a
+        private copy for a writer to a shared block"); a sequence with no
+        block, or whose last block it alone holds, raises ValueError."""
+        if not self.table:
+            raise ValueError("copy-on-write of a sequence that holds no block")
+        if self.pool.refcount[self.table[-1]] <= 1:
+            raise ValueError("copy-on-write of a block no other sequence shares")
         new = self.pool.allocate()
         old = self.table[-1]
         self.pool.release(old)

@@ -155,6 +155,8 @@ pa_status pa_bm_copy_last_block(pa_bm* bm, int64_t seq, int64_t* pair) {
   if (!bm || !pair) return PA_ERR_INVALID_ARG;
   Seq* s = bm->find(seq);
   if (!s || s->state != State::Running || s->table.empty()) return PA_ERR_INVALID_ARG;
+  // only a block another sequence also holds is copied
+  if (bm->dev.refcount[s->table.back()] <= 1) return PA_ERR_INVALID_ARG;
   if (bm->dev.free_list.empty()) return PA_ERR_NO_SPACE;
   const int32_t old = s->table.back();
   const int32_t nb = bm->dev.allocate();

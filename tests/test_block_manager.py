@@ -197,8 +197,18 @@ def test_differential_against_oracle_manager():
                 next_id += 1
             elif op == "cow" and running:
                 sid = rnd.choice(running)
-                if m.seqs[sid].table and m.pool.num_free:
-                    assert bm.copy_last_block(sid) == m.seqs[sid].copy_last_block()
+                sq = m.seqs[sid]
+                if sq.table and m.pool.refcount[sq.table[-1]] > 1 and m.pool.num_free:
+                    assert bm.copy_last_block(sid) == sq.copy_last_block()
+                elif not sq.table or m.pool.refcount[sq.table[-1]] <= 1:
+                    # nothing shared to copy: both refuse and change nothing
+                    with pytest.raises(ValueError):
+                        sq.copy_last_block()
+                    with pytest.raises(B.PaError) as e:
+                        bm.copy_last_block(sid)
+                    assert e.value.status == B.PA_ERR_INVALID_ARG
+                else:
+                    _no_space(bm.copy_last_block, sid)
             elif op == "release" and m.seqs:
                 sid = rnd.choice(list(m.seqs))
                 bm.release(sid)
