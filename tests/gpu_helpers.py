@@ -120,6 +120,14 @@ class DeviceState:
                             seqs=seqs)
 
 
+    def oracle_prefill(self, q_codes, qsl, tables=None, ctx=None, seqs=None, rows=None):
+        wl = self.wl
+        return paged.prefill(q_codes, wl.q_dtype, self.ok, self.ov, self.geom, wl.pool_dtype,
+                             wl.layer, wl.block_tables if tables is None else tables,
+                             wl.context_lens if ctx is None else ctx, qsl, wl.scale,
+                             wl.k_scale, wl.v_scale, seqs=seqs, rows=rows)
+
+
 def max_err(gpu, ref, rows=None):
     if rows is not None:
         gpu, ref = gpu[rows], ref[rows]
@@ -138,12 +146,18 @@ def half_ulp(x, out_dtype):
     return np.ldexp(1.0, (np.floor(np.log2(a)) - mant - 1).astype(np.int64))
 
 
-def max_err_stored(gpu, ref, out_dtype, rows=None):
-    """Largest error beyond the output format's own rounding: max |gpu - ref|
-    - half_ulp(gpu). An output stored in bf16 or f16 is the kernel's value
-    rounded once more; for large outputs that rounding alone can exceed a
-    fixed absolute tolerance (half a bf16 ulp is 1/64 on [4, 8))."""
+def max_err_stored(gpu, ref, out_dtype, tol, rows=None):
+    """Largest error against the stated bound `tol`, forgiving the output
+    format's own rounding only where that rounding alone could break the
+    bound: an element whose half ulp (in the format the result is stored in)
+    exceeds tol / 2 is checked as |gpu - ref| - half_ulp(gpu); every other
+    element as the plain |gpu - ref|. (A bf16 result on [4, 8) is the
+    kernel's value rounded to a spacing of 2^-5, half of which, 2^-6, is
+    more than the whole bf16 bound 1e-2 leaves; on [1, 2) half an ulp is
+    2^-9, well inside it, and no allowance is made there.)"""
     if rows is not None:
         gpu, ref = gpu[rows], ref[rows]
-    ex = np.abs(gpu - ref) - half_ulp(gpu, out_dtype)
+    hu = half_ulp(gpu, out_dtype)
+    allow = np.where(hu > tol / 2, hu, 0.0)
+    ex = np.abs(gpu - ref) - allow
     return float(np.max(ex, initial=0.0))

@@ -144,7 +144,7 @@ def test_block_manager_drives_write_copy_decode_prefill():
                     torch.from_numpy(ctx).cuda(), int(ctx.max()), 0.09)
     got = codecs.decode(tensor_codes(out), DT)
     ref = paged.decode(q, DT, w.ok, w.ov, w.geom, DT, 0, tab, ctx, 0.09)
-    ex = max_err_stored(got, ref, DT)
+    ex = max_err_stored(got, ref, DT, TOL[DT])
     say(f"contexts {ctx.tolist()}, decode error beyond output rounding {ex:.3e}")
     assert np.all(np.isfinite(got)) and ex <= TOL[DT]
     # the recomputed sequence's prefill pass over its whole history
@@ -156,6 +156,6 @@ def test_block_manager_drives_write_copy_decode_prefill():
                       torch.from_numpy(qsl).cuda(), int(ctx[i2]), 0.09)
     gotp = codecs.decode(tensor_codes(outp), DT)
     refp = paged.prefill(qp, DT, w.ok, w.ov, w.geom, DT, 0, tab[i2:i2 + 1], ctx[i2:i2 + 1], qsl, 0.09)
-    exp = max_err_stored(gotp, refp, DT)
+    exp = max_err_stored(gotp, refp, DT, TOL[DT])
     say(f"recompute prefill of {int(ctx[i2])} positions: error beyond output rounding {exp:.3e}")
     assert np.all(np.isfinite(gotp)) and exp <= TOL[DT]

@@ -79,7 +79,7 @@ def test_shared_decode_matches_oracle(combo):
     st = _state(wl)
     got = _shared(st)
     ref = st.oracle_decode()
-    ex = max_err_stored(got, ref, wl.q_dtype)
+    ex = max_err_stored(got, ref, wl.q_dtype, _tol(wl))
     say(f"{combo}: {wl.num_seqs} seqs, error beyond output rounding {ex:.3e}")
     assert np.all(np.isfinite(got)) and ex <= _tol(wl)
 
@@ -98,7 +98,7 @@ def test_empty_and_invalid_rows_inside_runs_and_plan_reuse():
     ref = st.oracle_decode(ctx=np.where(ctx > mc, 0, ctx), seqs=ok)
     assert np.all(got[1] == 0)
     assert np.all(np.isnan(got[5]))
-    ex = max_err_stored(got, ref, "bf16", rows=ok)
+    ex = max_err_stored(got, ref, "bf16", TOL["bf16"], rows=ok)
     say(f"error beyond output rounding {ex:.3e}")
     assert ex <= TOL["bf16"]
     # a second call with other queries reuses the plan left in the workspace
@@ -108,7 +108,7 @@ def test_empty_and_invalid_rows_inside_runs_and_plan_reuse():
     q2 = workloads.normal_codes(np.random.default_rng(5), wl.q.shape, "bf16")
     got2 = _shared(st, q_codes=q2, ws=ws, reuse=True)
     ref2 = st.oracle_decode(q_codes=q2)
-    ex2 = max_err_stored(got2, ref2, "bf16")
+    ex2 = max_err_stored(got2, ref2, "bf16", TOL["bf16"])
     say(f"reused plan: error beyond output rounding {ex2:.3e}")
     assert ex2 <= TOL["bf16"]
 
@@ -120,7 +120,7 @@ def test_shared_prefix_workload_full_size_sampled():
     rng = np.random.default_rng(4)
     seqs = sorted(rng.choice(wl.num_seqs, 12, replace=False).tolist())
     ref = st.oracle_decode(seqs=seqs)
-    ex = max_err_stored(got, ref, wl.q_dtype, rows=seqs)
+    ex = max_err_stored(got, ref, wl.q_dtype, TOL[wl.q_dtype], rows=seqs)
     say(f"shared-prefix workload, sequences {seqs}: error beyond output rounding {ex:.3e}")
     assert np.all(np.isfinite(got)) and ex <= TOL[wl.q_dtype]
     plain = st.decode()

@@ -96,6 +96,6 @@ def test_copy_stream_swap_ordered_by_events(dt):
     for layer in range(L):
         got = codecs.decode(tensor_codes(outs[layer]), "f16")
         ref = paged.decode(q, "f16", ok, ov, geom, dt, layer, tables, ctx, 0.088, ks, vs)
-        ex = max_err_stored(got, ref, "f16")
+        ex = max_err_stored(got, ref, "f16", TOL[dt if dt == "fp8_e4m3" else "f16"])
         say(f"{dt} layer {layer}: decode error beyond output rounding {ex:.3e}")
         assert np.all(np.isfinite(got)) and ex <= TOL[dt if dt == "fp8_e4m3" else "f16"]
