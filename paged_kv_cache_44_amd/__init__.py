@@ -43,6 +43,18 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc_on(stream, fn):
+    """Run the allocation `fn` with `stream` current, so torch's caching
+    allocator ties the memory to the stream the kernels run on: once the
+    tensor is dropped, the block is handed out again only in that stream's
+    order (after the kernels that use it), never to another stream while
+    they may still run."""
+    if stream is None:
+        return fn()
+    with torch.cuda.stream(stream):
+        return fn()
+
+
 def dtype_name(t: torch.Tensor) -> str:
     for k, v in TORCH_DTYPE.items():
         if t.dtype == v:
@@ -176,10 +188,11 @@ def _decode_call(fn_name, cache, layer, q, block_tables, context_lens, max_conte
         _on_device(out)
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_on(stream, lambda: torch.empty_like(q))
     if workspace is None:
         n = decode_workspace_size(cache, S, Hq, max_context_len)
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_on(stream, lambda: torch.empty(max(n, 1), dtype=torch.uint8,
+                                                          device=q.device))
     else:
         _on_device(workspace)
     c = cache.struct()
@@ -223,13 +236,14 @@ def decode_shared(cache: KVCache, layer: int, q: torch.Tensor, block_tables: tor
     _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
           "context_lens must be int32 [S]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_on(stream, lambda: torch.empty_like(q))
     else:
         _on_device(out)
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     if workspace is None:
         n = decode_shared_workspace_size(cache, S, Hq)
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        workspace = _alloc_on(stream, lambda: torch.empty(max(n, 1), dtype=torch.uint8,
+                                                          device=q.device))
     else:
         _on_device(workspace)
     c = cache.struct()
@@ -244,14 +258,18 @@ def decode_shared(cache: KVCache, layer: int, q: torch.Tensor, block_tables: tor
 
 def decode_attend(cache, layer, q, block_tables, context_lens, max_context_len, scale,
                   out, workspace, stream=None):
-    """Phase 1 of :func:`decode` (partition attention)."""
+    """Phase 1 of :func:`decode` (partition attention). ``out`` and
+    ``workspace`` are required: :func:`decode_merge` must see the same ones."""
+    _need(out is not None and workspace is not None, "decode_attend needs out and workspace")
     _decode_call("pa_decode_attend", cache, layer, q, block_tables, context_lens,
                  max_context_len, scale, out, workspace, stream)
 
 
 def decode_merge(cache, layer, q, block_tables, context_lens, max_context_len, scale,
                  out, workspace, stream=None):
-    """Phase 2 of :func:`decode` (merge of partition partials)."""
+    """Phase 2 of :func:`decode` (merge of partition partials): the ``out``
+    and ``workspace`` that :func:`decode_attend` was given."""
+    _need(out is not None and workspace is not None, "decode_merge needs out and workspace")
     _decode_call("pa_decode_merge", cache, layer, q, block_tables, context_lens,
                  max_context_len, scale, out, workspace, stream)
 
@@ -274,7 +292,7 @@ def prefill(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Ten
     _need(query_start_loc.dtype == torch.int32 and tuple(query_start_loc.shape) == (S + 1,),
           "query_start_loc must be int32 [S + 1]")
     if out is None:
-        out = torch.empty_like(q)
+        out = _alloc_on(stream, lambda: torch.empty_like(q))
     else:
         _on_device(out)
         _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
