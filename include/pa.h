@@ -31,7 +31,8 @@
  *  - Ownership: the caller owns every buffer (pools, tables, workspace). The
  *    library never allocates, never frees, never synchronises the host and
  *    keeps no pointer after a call returns. It holds no global state and is
- *    reentrant.
+ *    reentrant, except for pa_decode_no_alloc's fixed device array (see
+ *    there).
  *  - Streams: all device work is enqueued on the caller's `stream` and is
  *    asynchronous with respect to the host; stream order gives the ordering
  *    between calls (e.g. a swap-out copy finishes before a later write that
@@ -230,6 +231,33 @@ int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs,
 /* that device current.                                                      */
 size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t max_context_len);
+
+/* ------------------------------------------------------------------------ */
+/* pa_decode_no_alloc — pa_decode for callers that cannot allocate memory:    */
+/* code under HIP graph capture, tight serving loops, and hosts that forbid  */
+/* device allocation after start-up. Same arguments and result as pa_decode, */
+/* without the workspace: the library keeps a fixed device array of          */
+/* PA_DECODE_NO_ALLOC_MAX_BYTES on every GPU it runs on (held until the      */
+/* process ends) and uses that instead. Nothing is allocated or freed.       */
+/*                                                                           */
+/*  - Sizes whose pa_decode_workspace_size exceeds                           */
+/*    PA_DECODE_NO_ALLOC_MAX_BYTES return PA_ERR_WORKSPACE before any HIP    */
+/*    call (use pa_decode with a workspace of your own for those).           */
+/*  - The first call on a device that needs the array looks its address up  */
+/*    (PA_ERR_HIP if that fails); later calls reuse it.                      */
+/*  - All calls on one GPU share its array, and the array keeps whatever the */
+/*    last call left (the kernels need no initialised workspace). Calls that */
+/*    overlap on one GPU -- on different streams, or from several threads    */
+/*    without ordering between them -- race on it and give undefined        */
+/*    output rows; order them on one stream.                                 */
+/* ------------------------------------------------------------------------ */
+#define PA_DECODE_NO_ALLOC_MAX_BYTES ((size_t)64 << 20)
+
+pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void* q,
+                             pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, int32_t num_seqs,
+                             int32_t num_q_heads, float scale, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* pa_decode_shared — pa_decode that reads a prefix shared by several        */

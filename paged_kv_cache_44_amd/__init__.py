@@ -26,7 +26,7 @@ TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat1
                "fp8_e4m3": torch.uint8}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
 
-__all__ = ["KVCache", "write_kv", "decode", "decode_attend", "decode_merge",
+__all__ = ["KVCache", "write_kv", "decode", "decode_attend", "decode_merge", "decode_no_alloc",
            "decode_workspace_size", "decode_partition_tokens", "copy_blocks", "version"]
 
 
@@ -212,6 +212,31 @@ def decode(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Tens
     """Paged decode attention: q [S][H_q][D] -> out [S][H_q][D] (q's dtype)."""
     return _decode_call("pa_decode", cache, layer, q, block_tables, context_lens,
                         max_context_len, scale, out, workspace, stream)[0]
+
+
+def decode_no_alloc(cache: KVCache, layer: int, q: torch.Tensor, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, max_context_len: int, scale: float,
+                    out: torch.Tensor, stream=None) -> torch.Tensor:
+    """pa_decode_no_alloc: the result of :func:`decode` into the caller's
+    ``out``, with the library's fixed device array as workspace (no
+    allocation anywhere; see include/pa.h for the size limit and for calls
+    that overlap on one GPU)."""
+    _need(cache.is_device, "decode needs a device pool")
+    _need(q.dim() == 3 and q.shape[2] == cache.head_dim, "q must be [S][H_q][head_dim]")
+    S, Hq, D = q.shape
+    _on_device(q, block_tables, context_lens, out)
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and block_tables.shape[0] == S, "block_tables must be int32 [S][max_blocks]")
+    _need(context_lens.dtype == torch.int32 and tuple(context_lens.shape) == (S,),
+          "context_lens must be int32 [S]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    c = cache.struct()
+    st = _lib().pa_decode_no_alloc(
+        ctypes.byref(c), layer, _ptr(q), DTYPES[dtype_name(q)], _ptr(out), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), S, Hq,
+        float(scale), _stream(stream))
+    B.check(st, "pa_decode_no_alloc")
+    return out
 
 
 def decode_shared_workspace_size(cache: KVCache, num_seqs: int, num_q_heads: int) -> int:

@@ -7,11 +7,13 @@ import os
 from .build import LIB_PATH
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_NO_SPACE = range(6)
+#: size of the fixed device array pa_decode_no_alloc uses (PA_DECODE_NO_ALLOC_MAX_BYTES)
+DECODE_NO_ALLOC_MAX_BYTES = 64 << 20
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = range(4)
 PA_COPY_D2D, PA_COPY_H2D, PA_COPY_D2H, PA_COPY_H2D_KERNEL, PA_COPY_D2H_KERNEL = range(5)
 
 #: every function the header declares
-EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_attend", "pa_decode_merge",
+EXPORTED = ("pa_write_kv", "pa_decode", "pa_decode_attend", "pa_decode_merge", "pa_decode_no_alloc",
             "pa_decode_partition_tokens", "pa_decode_workspace_size", "pa_decode_shared",
             "pa_decode_shared_workspace_size", "pa_prefill",
             "pa_copy_blocks", "pa_copy_blocks_staged", "pa_copy_staging_size",
@@ -61,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     for name in ("pa_decode", "pa_decode_attend", "pa_decode_merge"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = ctypes.c_int
+    lib.pa_decode_no_alloc.argtypes = dec[:12] + [vp]
+    lib.pa_decode_no_alloc.restype = ctypes.c_int
     lib.pa_decode_shared.argtypes = dec[:12] + [i32] + dec[12:]
     lib.pa_decode_shared.restype = ctypes.c_int
     lib.pa_decode_shared_workspace_size.argtypes = [P, i32, i32]

@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "pa.h"
@@ -12,7 +14,38 @@
 
 using pa::DecodeParams;
 
+// Workspace of pa_decode_no_alloc: a fixed array in this library's device
+// code, one copy on every GPU the library runs on, held until the process
+// ends. Host code never passes `scratch` itself (in host code the name only
+// stands for the symbol): it looks up the array's address on each device
+// once and hands that address to the kernels.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_NO_ALLOC_MAX_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`: looked up with that device current
+// on the first call that needs it, then kept.
+pa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+      p = ptr;
+    }
+  }
+  *out = p;
+  return PA_OK;
+}
 
 int elem_bytes(pa_dtype t) {
   switch (t) {
@@ -251,12 +284,15 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
   return PA_OK;
 }
 
+// use_scratch: the workspace is the library's own `scratch` array (the
+// workspace arguments are ignored); sizes that need more return
+// PA_ERR_WORKSPACE before any HIP call.
 pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const void* q,
                       pa_dtype q_dtype, void* out, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens,
                       int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                       float scale, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+                      hipStream_t stream, bool use_scratch = false) {
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
   if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
@@ -269,9 +305,17 @@ pa_status decode_impl(int phases, const pa_kv_cache* cache, int32_t layer, const
   DecodePlan plan;
   st = plan_decode(cache, num_seqs, num_q_heads, q_dtype, max_context_len, &plan);
   if (st != PA_OK) return st;
-  const int qb = elem_bytes(q_dtype);
   if (!aligned(q, 16) || !aligned(out, 4)) return PA_ERR_UNSUPPORTED;
-  (void)qb;
+  if (use_scratch) {
+    if (plan.ws_bytes > PA_DECODE_NO_ALLOC_MAX_BYTES) return PA_ERR_WORKSPACE;
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (plan.ws_bytes > 0) {
+      st = scratch_of_current_device(&workspace);
+      if (st != PA_OK) return st;
+      workspace_bytes = PA_DECODE_NO_ALLOC_MAX_BYTES;
+    }
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 256))
       return PA_ERR_WORKSPACE;
@@ -536,6 +580,16 @@ pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q, pa_d
   return decode_impl(PHASE_BOTH, cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
                      context_lens, max_context_len, num_seqs, num_q_heads, scale, workspace,
                      workspace_bytes, stream);
+}
+
+pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void* q,
+                             pa_dtype q_dtype, void* out, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                             float scale, hipStream_t stream) {
+  return decode_impl(PHASE_BOTH, cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, num_seqs, num_q_heads, scale, nullptr, 0,
+                     stream, true);
 }
 
 pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* q,

@@ -192,3 +192,22 @@ def test_shared_decode_arguments(pa_lib):
     assert run(nbytes=n - 256) == B.PA_ERR_WORKSPACE
     assert run(ws=None) == B.PA_ERR_WORKSPACE
     assert run(ws=FAKE + 64) == B.PA_ERR_WORKSPACE
+
+
+def test_decode_no_alloc_argument_errors(pa_lib):
+    """pa_decode_no_alloc checks its arguments as pa_decode does, and refuses
+    sizes whose workspace exceeds its fixed array, all before any HIP call."""
+    c = _cache()
+
+    def call(seqs=4, hq=32, max_ctx=100, q_dtype=B.PA_BF16, q=FAKE, out=FAKE):
+        return pa_lib.pa_decode_no_alloc(ctypes.byref(c), 0, q, q_dtype, out, FAKE, 8, FAKE,
+                                         max_ctx, seqs, hq, 0.1, None)
+    assert call(seqs=0) == B.PA_OK
+    assert call(hq=30) == B.PA_ERR_INVALID_ARG
+    assert call(q=None) == B.PA_ERR_INVALID_ARG
+    assert call(q_dtype=B.PA_F16) == B.PA_ERR_UNSUPPORTED           # bf16 pool, f16 queries
+    assert call(hq=8 * 32) == B.PA_ERR_UNSUPPORTED
+    # 8,192 sequences x 8 KV heads x groups of 4 need far more than the array
+    big = pa_lib.pa_decode_workspace_size(ctypes.byref(c), 8192, 32, 4000)
+    assert big > B.DECODE_NO_ALLOC_MAX_BYTES
+    assert call(seqs=8192, max_ctx=4000) == B.PA_ERR_WORKSPACE
