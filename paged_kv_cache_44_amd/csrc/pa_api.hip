@@ -59,6 +59,23 @@ int elem_bytes(pa_dtype t) {
 
 bool valid_dtype(int t) { return t >= PA_F32 && t <= PA_FP8_E4M3; }
 
+// The integer a caller stored in an enum-typed argument or field, read
+// without going through the enum type: a C caller may pass any int, and in
+// C++ reading a value outside the enumerators' range through the enum type
+// is undefined. Every enum input is checked this way before it is used.
+template <class E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enums of the C ABI are int-sized");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
+bool valid_q_dtype(const pa_dtype& q) {
+  const int v = raw(q);
+  return v == PA_F32 || v == PA_F16 || v == PA_BF16;
+}
+
 int ilog2(int x) {
   int l = 0;
   while ((1 << l) < x) ++l;
@@ -72,27 +89,36 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Geometry checks shared by every call. `need_ptrs` requires k and v.
 pa_status check_cache(const pa_kv_cache* c, bool need_ptrs) {
   if (!c) return PA_ERR_INVALID_ARG;
-  if (!valid_dtype(c->dtype)) return PA_ERR_INVALID_ARG;
+  if (!valid_dtype(raw(c->dtype))) return PA_ERR_INVALID_ARG;
   if (need_ptrs && (!c->k || !c->v)) return PA_ERR_INVALID_ARG;
   if (c->num_blocks <= 0 || c->num_layers <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
     return PA_ERR_INVALID_ARG;
   if (!is_pow2(c->block_size) || c->block_size > 256) return PA_ERR_INVALID_ARG;
-  const int64_t slab = (int64_t)c->num_kv_heads * c->block_size * c->head_dim;
   if (c->layer_stride < 0 || c->block_stride < 0) return PA_ERR_INVALID_ARG;
+  // sizes in 128-bit arithmetic: extreme strides must be refused, not wrap
+  using i128 = __int128;
+  const i128 slab = (i128)c->num_kv_heads * c->block_size * c->head_dim;
   // no two (block, layer) slabs may overlap: block-major (a block's layers
   // nested inside its stride) or layer-major (a layer's blocks nested inside
   // the layer stride)
   const bool one_l = c->num_layers == 1, one_b = c->num_blocks == 1;
   const bool block_major =
-      (one_l || c->layer_stride >= slab) &&
-      (one_b || c->block_stride >= (int64_t)(c->num_layers - 1) * c->layer_stride + slab);
+      (one_l || (i128)c->layer_stride >= slab) &&
+      (one_b || (i128)c->block_stride >= (i128)(c->num_layers - 1) * c->layer_stride + slab);
   const bool layer_major =
-      (one_b || c->block_stride >= slab) &&
-      (one_l || c->layer_stride >= (int64_t)(c->num_blocks - 1) * c->block_stride + slab);
+      (one_b || (i128)c->block_stride >= slab) &&
+      (one_l || (i128)c->layer_stride >= (i128)(c->num_blocks - 1) * c->block_stride + slab);
   if (!block_major && !layer_major) return PA_ERR_INVALID_ARG;
   const int eb = elem_bytes(c->dtype);
+  // kernels address the pool with 64-bit byte offsets: its extent and both
+  // strides in bytes must fit
+  const i128 extent = ((i128)(c->num_blocks - 1) * c->block_stride +
+                       (i128)(c->num_layers - 1) * c->layer_stride + slab) * eb;
+  const i128 lim = (i128)INT64_MAX;
+  if (extent > lim || (i128)c->block_stride * eb > lim || (i128)c->layer_stride * eb > lim)
+    return PA_ERR_UNSUPPORTED;
   if ((c->block_stride * eb) % 16 || (c->layer_stride * eb) % 16) return PA_ERR_UNSUPPORTED;
-  if ((c->head_dim * eb) % 16) return PA_ERR_UNSUPPORTED;
+  if (((int64_t)c->head_dim * eb) % 16) return PA_ERR_UNSUPPORTED;
   if (need_ptrs && (!aligned(c->k, 16) || !aligned(c->v, 16))) return PA_ERR_UNSUPPORTED;
   if (c->dtype == PA_FP8_E4M3) {
     if (!(c->k_scale > 0.f) || !isfinite(c->k_scale) || !(c->v_scale > 0.f) || !isfinite(c->v_scale))
@@ -507,11 +533,11 @@ extern "C" {
 pa_status pa_write_kv(const pa_kv_cache* cache, int32_t layer, const void* k, const void* v,
                       pa_dtype src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
                       hipStream_t stream) {
+  if (!valid_dtype(raw(src_dtype))) return PA_ERR_INVALID_ARG;
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
   if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
   if (num_tokens < 0) return PA_ERR_INVALID_ARG;
-  if (!valid_dtype(src_dtype)) return PA_ERR_INVALID_ARG;
   const bool conv = src_dtype != cache->dtype;
   if (conv && !(cache->dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3)) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
@@ -556,7 +582,7 @@ size_t pa_decode_workspace_size(const pa_kv_cache* cache, int32_t num_seqs, int3
 int32_t pa_decode_partition_tokens(const pa_kv_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context_len) {
   DecodePlan plan;
-  if (!cache) return 0;
+  if (!cache || check_cache(cache, false) != PA_OK) return 0;
   pa_dtype qd = cache->dtype == PA_FP8_E4M3 ? PA_BF16 : cache->dtype;
   if (plan_decode(cache, num_seqs, num_q_heads, qd, max_context_len, &plan) != PA_OK) return 0;
   return plan.part_tokens;
@@ -567,6 +593,7 @@ pa_status pa_prefill(const pa_kv_cache* cache, int32_t layer, const void* q, pa_
                      const int32_t* context_lens, int32_t max_context_len,
                      const int32_t* query_start_loc, int32_t max_query_len, int32_t num_seqs,
                      int32_t num_q_tokens, int32_t num_q_heads, float scale, hipStream_t stream) {
+  if (!valid_q_dtype(q_dtype)) return PA_ERR_INVALID_ARG;
   return prefill_impl(cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq, context_lens,
                       max_context_len, query_start_loc, max_query_len, num_seqs, num_q_tokens,
                       num_q_heads, scale, stream);
@@ -577,6 +604,7 @@ pa_status pa_decode(const pa_kv_cache* cache, int32_t layer, const void* q, pa_d
                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
                     int32_t num_q_heads, float scale, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
+  if (!valid_q_dtype(q_dtype)) return PA_ERR_INVALID_ARG;
   return decode_impl(PHASE_BOTH, cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
                      context_lens, max_context_len, num_seqs, num_q_heads, scale, workspace,
                      workspace_bytes, stream);
@@ -587,6 +615,7 @@ pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void
                              int32_t max_blocks_per_seq, const int32_t* context_lens,
                              int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                              float scale, hipStream_t stream) {
+  if (!valid_q_dtype(q_dtype)) return PA_ERR_INVALID_ARG;
   return decode_impl(PHASE_BOTH, cache, layer, q, q_dtype, out, block_tables, max_blocks_per_seq,
                      context_lens, max_context_len, num_seqs, num_q_heads, scale, nullptr, 0,
                      stream, true);
@@ -598,6 +627,7 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                            float scale, int32_t reuse_plan, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_q_dtype(q_dtype)) return PA_ERR_INVALID_ARG;
   pa_status st = check_cache(cache, true);
   if (st != PA_OK) return st;
   if (layer < 0 || layer >= cache->num_layers) return PA_ERR_INVALID_ARG;
@@ -671,6 +701,7 @@ pa_status pa_decode_attend(const pa_kv_cache* cache, int32_t layer, const void* 
                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                            float scale, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
+  if (!valid_q_dtype(q_dtype)) return PA_ERR_INVALID_ARG;
   return decode_impl(PHASE_ATTEND, cache, layer, q, q_dtype, out, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                      scale, workspace, workspace_bytes, stream);
@@ -682,6 +713,7 @@ pa_status pa_decode_merge(const pa_kv_cache* cache, int32_t layer, const void* q
                           int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                           float scale, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
+  if (!valid_q_dtype(q_dtype)) return PA_ERR_INVALID_ARG;
   return decode_impl(PHASE_MERGE, cache, layer, q, q_dtype, out, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
                      scale, workspace, workspace_bytes, stream);
@@ -689,6 +721,10 @@ pa_status pa_decode_merge(const pa_kv_cache* cache, int32_t layer, const void* q
 
 pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src, const int64_t* pairs,
                          int32_t num_pairs, pa_copy_dir dir, hipStream_t stream) {
+  const int d = raw(dir);
+  if (!(d == PA_COPY_D2D || d == PA_COPY_H2D || d == PA_COPY_D2H || d == PA_COPY_H2D_KERNEL ||
+        d == PA_COPY_D2H_KERNEL))
+    return PA_ERR_INVALID_ARG;
   pa_status st = check_cache(dst, true);
   if (st != PA_OK) return st;
   st = check_cache(src, true);
@@ -778,6 +814,7 @@ pa_status pa_copy_blocks(const pa_kv_cache* dst, const pa_kv_cache* src, const i
 pa_status pa_copy_blocks_staged(const pa_kv_cache* dst, const pa_kv_cache* src,
                                 const int64_t* pairs, int32_t num_pairs, pa_copy_dir dir,
                                 void* staging, size_t staging_bytes, hipStream_t stream) {
+  if (!(raw(dir) == PA_COPY_H2D || raw(dir) == PA_COPY_D2H)) return PA_ERR_INVALID_ARG;
   pa_status st = check_cache(dst, true);
   if (st != PA_OK) return st;
   st = check_cache(src, true);
@@ -850,7 +887,7 @@ int32_t pa_host_pool_mapped(const pa_kv_cache* pool) {
 }
 
 const char* pa_status_string(pa_status s) {
-  switch (s) {
+  switch (raw(s)) {
     case PA_OK: return "PA_OK";
     case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: unsupported size, dtype or alignment";

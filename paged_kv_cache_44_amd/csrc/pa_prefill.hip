@@ -318,8 +318,8 @@ bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g) {
 
 // Workgroups along the query rows: each covers PW * PNT * (16 / g) positions.
 int prefill_tiles(int g, int max_query_len) {
-  const int per = PW * PNT * (16 / g);
-  return (max_query_len + per - 1) / per;
+  const int64_t per = PW * PNT * (16 / g);
+  return (int)(((int64_t)max_query_len + per - 1) / per);
 }
 
 hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
