@@ -32,6 +32,24 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+
+# Figures the pages give for context (reported beside the measurements; none
+# is a target here, and none was measured on this hardware).
+PAGE_CONTEXT = [
+    {"figure": "2-4x the request rate of Orca-class serving systems at similar latency",
+     "context": "the vLLM authors' end-to-end serving measurements on their own GPUs, models "
+                "(e.g. OPT-13B) and request traces (ShareGPT, Alpaca); whole serving systems, "
+                "not one kernel",
+     "source": "Efficient Memory Management for Large Language Model Serving with PagedAttention "
+               "(summary page), results paragraph"},
+    {"figure": "about 24 ms to recompute a 1,500-token request",
+     "context": "idealised: 1,500 tokens x 16 GFLOP per token = 24 TFLOP for Llama 3.1 8B, all "
+                "layers, at the 989 TFLOP/s H100 dense peak",
+     "source": "41 - Preemption, Recomputation & KV Pressure, section 3"},
+    {"figure": "about 3 ms each way to swap the same request",
+     "context": "94 blocks x 2 MiB (all layers) = 188 MiB over PCIe Gen5 x16 at ~64 GB/s nominal",
+     "source": "41 - Preemption, Recomputation & KV Pressure, section 3"},
+]
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_44_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_decode_sk.h", "pa_mfma.h", "pa_device.h",
@@ -63,7 +81,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target seconds of CPU oracle work for the baseline sample")
     ap.add_argument("--flush-iters", type=int, default=20)
     ap.add_argument("--print-source-hash", action="store_true",
@@ -86,6 +104,9 @@ def parse():
     ap.add_argument("--block-size-sweep", action="store_true",
                     help="the GQA bf16 decode step at block sizes 8..256: step and attention-kernel "
                          "time, and the slots the blocks hold beyond the context (one JSON line each)")
+    ap.add_argument("--counters-summary", nargs=2, metavar=("KERNEL_WORKLOAD", "CSV"),
+                    help="turn rocprofv3 --pmc counter CSVs (comma-separated paths) of a "
+                         "decode run into profiles/traffic_<KERNEL_WORKLOAD>.json")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) a few times: the "
                          "reference kernel for scaling HBM byte counters")
@@ -492,6 +513,93 @@ def prefill_bench(steps: int, warmup: int):
         del cache, q, out
 
 
+def _counter_rows(paths):
+    """Per-dispatch counter sums from rocprofv3 counter_collection CSVs:
+    {(file, dispatch id): {"kernel": name, counter: value}}."""
+    import csv
+    rows = {}
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                key = (path, r["Dispatch_Id"])
+                d = rows.setdefault(key, {"kernel": r["Kernel_Name"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return rows
+
+
+# Read and write request counters of the L2's memory interface (EA): every
+# read request is 32, 64 or 128 bytes (TCC_BUBBLE counts the 128-byte ones,
+# TCC_EA0_RDREQ_32B the 32-byte ones, TCC_EA0_RDREQ all), every write 32 or
+# 64 bytes (TCC_EA0_WRREQ_64B the 64-byte ones). *_DRAM counts the requests
+# that went on to DRAM (the rest were served by the Infinity Cache).
+READ_COUNTERS = ["TCC_BUBBLE_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                 "TCC_EA0_RDREQ_DRAM_sum"]
+WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum"]
+
+
+def request_bytes(c):
+    """(read bytes, write bytes) from one dispatch's request counts."""
+    r128, rall, r32 = c["TCC_BUBBLE_sum"], c["TCC_EA0_RDREQ_sum"], c["TCC_EA0_RDREQ_32B_sum"]
+    read = 128 * r128 + 64 * (rall - r128 - r32) + 32 * r32
+    wall, w64 = c["TCC_EA0_WRREQ_sum"], c["TCC_EA0_WRREQ_64B_sum"]
+    write = 64 * w64 + 32 * (wall - w64)
+    return read, write
+
+
+def counters_summary(spec):
+    """profiles/traffic_<kernel>_<workload>.json from two rocprofv3 --pmc
+    runs of `bench.py --config N` (READ_COUNTERS, then WRITE_COUNTERS): the
+    kernel's memory read and write bytes counted from the L2's requests by
+    size (request_bytes), averaged over its dispatches, against its
+    algorithmic bytes; and the share of read requests that reached DRAM."""
+    name, csvs = spec
+    kernel, workload = name.split(":")
+    rows = _counter_rows(csvs.split(","))
+    mine = [d for d in rows.values() if kernel in d["kernel"]]
+    if not mine:
+        raise SystemExit(f"no dispatch of {kernel} in {csvs}")
+
+    def avg(c):
+        v = [d[c] for d in mine if c in d]
+        return float(np.mean(v)) if v else None
+    counts = {c: avg(c) for c in READ_COUNTERS + WRITE_COUNTERS}
+    missing = [c for c, v in counts.items() if v is None]
+    if missing:
+        raise SystemExit(f"counters missing from {csvs}: {missing}")
+    read, write = request_bytes(counts)
+    import workloads
+    if workload == "copy_1GiB":         # bench.py --copy-calibration: 1 GiB read, 1 GiB written
+        ab = 2 << 30
+    else:
+        wl = workloads.make(wl_config(workload))
+        ab = unique_decode_bytes(wl) - (workloads.decode_bytes(wl) - attend_bytes(wl))
+    rec = {"kernel": mine[0]["kernel"], "workload": workload,
+           "kernel_source_sha": kernel_source_hash(),
+           "dispatches": len(mine) // 2,
+           "requests_per_launch": {c: round(v, 1) for c, v in counts.items()},
+           "hbm_read_bytes_per_launch": int(read),
+           "hbm_write_bytes_per_launch": int(write),
+           "hbm_bytes_per_launch": int(read + write),
+           "dram_share_of_read_requests": round(counts["TCC_EA0_RDREQ_DRAM_sum"] /
+                                                counts["TCC_EA0_RDREQ_sum"], 4),
+           "algorithmic_bytes_per_launch": ab,
+           "traffic_over_algorithmic": round((read + write) / ab, 4),
+           "commands": [f"rocprofv3 --pmc {' '.join(cs)} --output-format csv -d <out> -o run -- "
+                        + ("python bench.py --copy-calibration" if workload == "copy_1GiB" else
+                           f"python bench.py --no-cpu-baseline --config {wl_config(workload)} "
+                           "--steps 5 --warmup 2 --flush-iters 0")
+                        for cs in (READ_COUNTERS, WRITE_COUNTERS)]}
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def wl_config(workload: str) -> int:
+    return {"tiny_fp32": 1, "mha_fp16": 2, "gqa_bf16": 3, "shared_prefix_fp16": 4,
+            "long_fp8": 5}[workload]
+
+
 def launch_avg_ms(fn, reps: int) -> float:
     """Mean duration of one launch of fn: reps launches back to back between
     two HIP events on the launch stream (torch's current stream, which the
@@ -590,11 +698,34 @@ def block_size_sweep(steps: int, warmup: int):
     return rows
 
 
-def cpu_baseline(wl, target_s: float):
-    """The oracle, as it is, on the host cores: its slot write builds the pool
-    on the host, then its decode runs sequence by sequence (cycling through
-    the workload) until about target_s seconds of decode work are done."""
-    from threadpoolctl import threadpool_limits
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def host_workers() -> int:
+    """Worker processes for the pooled oracle run: the cores this process may
+    run on, capped by OMP_NUM_THREADS where the host sets it (the CPU share
+    a GPU machine gives one GPU)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+# the oracle's pools for the pooled run, inherited by forked workers
+_ORACLE = {}
+
+
+def _oracle_pools(wl):
     from oracle import paged
     import workloads
     geom = paged.Geometry(wl.num_blocks, wl.num_layers, wl.num_kv_heads, wl.block_size,
@@ -607,23 +738,72 @@ def cpu_baseline(wl, target_s: float):
                                     wl.src_dtype, op[3], wl.k_scale, wl.v_scale)
         else:
             ok, ov = paged.copy_blocks(ok, ov, geom, ok, ov, geom, op[1], same_pool=True)
+    return geom, ok, ov
+
+
+def _oracle_seq(s: int) -> int:
+    """One sequence's decode by the oracle (in a worker); returns its bytes."""
+    from oracle import paged
+    import workloads
+    wl, geom, ok, ov = _ORACLE["wl"], _ORACLE["geom"], _ORACLE["ok"], _ORACLE["ov"]
+    paged.decode(wl.q, wl.q_dtype, ok, ov, geom, wl.pool_dtype, wl.layer, wl.block_tables,
+                 wl.context_lens, wl.scale, wl.k_scale, wl.v_scale, seqs=[s])
+    return workloads.decode_bytes(wl, wl.context_lens[s:s + 1])
+
+
+def _one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle, as it is, on the host cores. Its slot write builds the pool
+    on the host; then its decode runs sequence by sequence (cycling through
+    the workload) for about target_s seconds in one process with BLAS on one
+    thread, and again for about target_s seconds in a pool of host_workers()
+    forked processes (one BLAS thread each) that take sequences in turn.
+    Must run before this process initialises the GPU (the pool forks)."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    geom, ok, ov = _oracle_pools(wl)
+    _ORACLE.update(wl=wl, geom=geom, ok=ok, ov=ov)
+    S = wl.num_seqs
+    # one process
     done_bytes, seqs = 0, 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        s = 0
         while time.perf_counter() - t0 < target_s:
-            paged.decode(wl.q, wl.q_dtype, ok, ov, geom, wl.pool_dtype, wl.layer,
-                         wl.block_tables, wl.context_lens, wl.scale, wl.k_scale, wl.v_scale,
-                         seqs=[s])
-            done_bytes += workloads.decode_bytes(wl, wl.context_lens[s:s + 1])
+            done_bytes += _oracle_seq(seqs % S)
             seqs += 1
-            s = (s + 1) % wl.num_seqs
-        dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{seqs} single-sequence decodes (sequences 0..{min(seqs, wl.num_seqs) - 1} "
-                      f"of the workload) in {dt:.1f} s; numpy fp64, BLAS limited to 1 thread",
-            "seq_per_s": round(seqs / dt, 3)}
+        dt1 = time.perf_counter() - t0
+    one = {"value": round(done_bytes / dt1 / 1e9, 4), "seq_per_s": round(seqs / dt1, 3),
+           "seconds": round(dt1, 2), "sequences": seqs}
+    # a pool of forked workers, in rounds of whole passes over the batch (or
+    # of one sequence per worker when a pass is long) until target_s is spent
+    n = host_workers()
+    ctx = mp.get_context("fork")
+    pbytes, pseqs = 0, 0
+    with ctx.Pool(n, initializer=_one_blas_thread) as pool:
+        pool.map(_oracle_seq, [0] * n)                      # start-up outside the timing
+        chunk = max(S, n)
+        t0 = time.perf_counter()
+        nxt = 0
+        while time.perf_counter() - t0 < target_s:
+            idx = [(nxt + i) % S for i in range(chunk)]
+            nxt += chunk
+            pbytes += sum(pool.map(_oracle_seq, idx, chunksize=max(1, len(idx) // (4 * n))))
+            pseqs += chunk
+        dtn = time.perf_counter() - t0
+    _ORACLE.clear()
+    pooled = {"value": round(pbytes / dtn / 1e9, 4), "seq_per_s": round(pseqs / dtn, 3),
+              "seconds": round(dtn, 2), "sequences": pseqs, "workers": n}
+    return {"value": pooled["value"], "unit": "GB/s", "cores": n, "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cores": len(os.sched_getaffinity(0)),
+            "sample": (f"the workload's sequences decoded one at a time by the numpy fp64 oracle, "
+                       f"cycling through the batch: {pseqs} decodes in {dtn:.1f} s over {n} "
+                       f"worker processes (one BLAS thread each); single process: {seqs} "
+                       f"decodes in {dt1:.1f} s"),
+            "single_process": one, "pooled": pooled}
 
 
 def main():
@@ -640,6 +820,18 @@ def main():
     import paged_kv_cache_44_amd as pa
     import workloads
 
+    if args.counters_summary:
+        counters_summary(args.counters_summary)
+        return
+    plain = not (args.copy_calibration or args.swap or args.swap_sweep or args.block_size_sweep
+                 or args.prefill)
+    # the CPU oracle first, before this process touches the GPU (its worker
+    # pool forks); the host measurement does not depend on the order
+    cpu = None
+    if plain and not args.no_cpu_baseline:
+        cpu = cpu_baseline(workloads.make(args.config), args.cpu_seconds)
+        print(f"[bench] cpu baseline: {cpu['value']} GB/s over {cpu['cores']} workers, "
+              f"{cpu['single_process']['value']} GB/s in one process", file=sys.stderr, flush=True)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
@@ -717,16 +909,20 @@ def main():
         fl.append(a.elapsed_time(b))
     del scratch
 
-    step_bytes = workloads.decode_bytes(wl) + workloads.write_bytes(wl, len(step_idx))
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # the method's bytes: every physical slot in use read once, however many
+    # sequences share it (equal to the logical count unless blocks are
+    # shared, as the shared-prefix workload's prompts are)
     uniq = unique_decode_bytes(wl)
-    ab = attend_bytes(wl)
+    wbytes = workloads.write_bytes(wl, len(step_idx))
+    step_bytes = uniq + wbytes
+    logical_step_bytes = workloads.decode_bytes(wl) + wbytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    ab = uniq - (workloads.decode_bytes(wl) - attend_bytes(wl))
     kname = attend_kernel_name(wl)
     traffic = load_traffic(kname, wl.name)
     if args.shared:
-        # the whole shared decode against the bytes it must read at the least:
-        # every physical slot in use once
-        ab = uniq - (workloads.decode_bytes(wl) - attend_bytes(wl))
+        # the whole shared decode (planning, both passes, merges) against the
+        # bytes it must read at the least
         kname = "decode_shared (plan, prefix and suffix passes, merges)"
         traffic = None
     achieved = ab / (attend_ms * 1e-3) / 1e9
@@ -755,7 +951,9 @@ def main():
         "seq_per_s": round(S / (ms_per_step * 1e-3), 1),
         "step_bytes": step_bytes,
         "unique_decode_bytes": uniq,
-        "unique_GBps": round((uniq + step_bytes - workloads.decode_bytes(wl)) / (ms_per_step * 1e-3) / 1e9, 2),
+        "logical_step_bytes": logical_step_bytes,
+        "logical_GBps": round(logical_step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "attend_logical_GBps": round(attend_bytes(wl) / (attend_ms * 1e-3) / 1e9, 2),
         "decode_flushed_ms": ({"median": round(float(np.median(fl)), 5),
                                "p10": round(float(np.percentile(fl, 10)), 5),
                                "p90": round(float(np.percentile(fl, 90)), 5)} if fl else None),
@@ -764,11 +962,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab,
                      "avg_launch_ms": round(attend_ms, 5)},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
+        "page_context": PAGE_CONTEXT,
     }
-    if not args.no_cpu_baseline:
-        del cache
-        rec["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 
