@@ -527,11 +527,15 @@ def _counter_rows(paths):
     return rows
 
 
-# Read and write request counters of the L2's memory interface (EA): every
-# read request is 32, 64 or 128 bytes (TCC_BUBBLE counts the 128-byte ones,
-# TCC_EA0_RDREQ_32B the 32-byte ones, TCC_EA0_RDREQ all), every write 32 or
-# 64 bytes (TCC_EA0_WRREQ_64B the 64-byte ones). *_DRAM counts the requests
-# that went on to DRAM (the rest were served by the Infinity Cache).
+# Read and write request counters of the L2's memory interface (EA).
+# TCC_EA0_RDREQ counts every read request, TCC_EA0_RDREQ_32B the 32-byte
+# ones; on MI355X every other read request is 128 bytes: a 1 GiB device copy
+# issues exactly 2^23 of them, and TCC_BUBBLE, which rocprofv3's FETCH_SIZE
+# takes for the 128-byte count (valuing the rest at 64 bytes), reads 0 --
+# hence FETCH_SIZE reports half the bytes read. Writes are 32 or 64 bytes
+# (TCC_EA0_WRREQ_64B the 64-byte ones; the copy writes 2^24 of them for
+# 1 GiB). *_DRAM counts the requests that went on to DRAM (the rest were
+# served by the Infinity Cache).
 READ_COUNTERS = ["TCC_BUBBLE_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
                  "TCC_EA0_RDREQ_DRAM_sum"]
 WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_DRAM_sum"]
@@ -540,7 +544,10 @@ WRITE_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum", "TCC_EA0_WRREQ_D
 def request_bytes(c):
     """(read bytes, write bytes) from one dispatch's request counts."""
     r128, rall, r32 = c["TCC_BUBBLE_sum"], c["TCC_EA0_RDREQ_sum"], c["TCC_EA0_RDREQ_32B_sum"]
-    read = 128 * r128 + 64 * (rall - r128 - r32) + 32 * r32
+    if r128 == 0:             # MI355X: every read request that is not 32 bytes is 128
+        read = 128 * (rall - r32) + 32 * r32
+    else:
+        read = 128 * r128 + 64 * (rall - r128 - r32) + 32 * r32
     wall, w64 = c["TCC_EA0_WRREQ_sum"], c["TCC_EA0_WRREQ_64B_sum"]
     write = 64 * w64 + 32 * (wall - w64)
     return read, write
