@@ -328,8 +328,10 @@ size_t pa_decode_shared_workspace_size(const pa_kv_cache* cache, int32_t num_seq
 /*  max_query_len    host bound on the n_s; sizes the launch (rows of a      */
 /*                   sequence beyond it are not computed).                   */
 /*  context_lens, block_tables, max_context_len: as for pa_decode.           */
-/* A sequence whose context is invalid (as for pa_decode), shorter than n_s, */
-/* or whose table names a block outside the pool gets NaN rows. Rows outside */
+/* A sequence whose context is invalid (as for pa_decode) or shorter than   */
+/* n_s gets NaN rows; a table entry naming a block outside the pool gives    */
+/* NaN in every row that attends to that block (and may in other rows of    */
+/* the same sequence: rows are computed in groups of 128 / g). Rows outside */
 /* [0, num_q_tokens) are never written; a sequence whose query_start_loc     */
 /* entries leave that range is skipped. No workspace is needed.             */
 /* Supported: pools PA_F16 / PA_BF16 with the same q_dtype, or PA_FP8_E4M3   */

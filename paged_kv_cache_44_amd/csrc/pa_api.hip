@@ -407,8 +407,9 @@ pa_status prefill_impl(const pa_kv_cache* cache, int32_t layer, const void* q, p
   const int g = num_q_heads / cache->num_kv_heads;
   if (!pa::prefill_supported((int)cache->dtype, (int)q_dtype, cache->head_dim, g))
     return PA_ERR_UNSUPPORTED;
-  if (pa::prefill_tiles(g, max_query_len) > 65535) return PA_ERR_UNSUPPORTED;   // grid y limit
-  if ((int64_t)num_seqs * cache->num_kv_heads > (int64_t)4 * 0x7fffffff) return PA_ERR_UNSUPPORTED;   // grid x limit
+  // one workgroup per (sequence, KV head, row tile), in a one-dimensional grid
+  if ((int64_t)num_seqs * cache->num_kv_heads * pa::prefill_tiles(g, max_query_len) > 0x7ffffff8)
+    return PA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(out, 4)) return PA_ERR_UNSUPPORTED;
   pa::PrefillParams a;
   memset(&a, 0, sizeof(a));

@@ -74,6 +74,7 @@ struct PrefillParams {
   const int32_t* context_lens;
   int32_t max_context_len;
   const int32_t* query_start_loc;   // [num_seqs + 1]
+  int32_t row_tiles;                // workgroups per (sequence, KV head) along the query rows
   int32_t num_q_tokens;
   int32_t num_seqs;
   int32_t num_q_heads;

@@ -9,18 +9,6 @@
 // every position p attends to positions 0 .. p. Query rows are packed
 // sequence by sequence (query_start_loc); the n_s rows of sequence s are its
 // positions ctx_s - n_s .. ctx_s - 1.
-//
-// A column tile is 16/G consecutive query positions x the G query heads of a
-// KV head; one wave owns 2 consecutive tiles of one (sequence, KV head), so
-// each 16-key chunk of K and V it loads serves 32 columns, and the 4 waves of
-// a workgroup own consecutive tiles of the same (sequence, KV head), so they
-// stream the same key chunks at about the same time and share them in the
-// caches. Per chunk the score tiles S[16 keys][16 columns] and P.V run on the
-// matrix cores as in decode (pa_mfma.h), with the causal mask key <=
-// position(column). A three-stage pipeline keeps the block ids of chunk j+2
-// and the K/V of chunk j+1 in flight while chunk j is processed; every step
-// issues the same loads. Workgroups launch last-first, so the longest causal
-// ranges start first.
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_mfma.h"
@@ -28,281 +16,396 @@
 namespace pa {
 namespace {
 
-constexpr int PW = 4;           // waves per workgroup
-constexpr int PCH = 16;         // keys per chunk
+// ---------------------------------------------------------------------------
+// Tiled prefill: each workgroup takes 128 query rows of one (sequence, KV
+// head) -- 128 / G consecutive positions x the G query heads -- 32 rows per
+// wave, and walks the keys of the causal range in tiles of FKT = 32 or 64
+// keys. The four
+// waves stage each tile once in LDS, gathered through the block table (FP8
+// codes widened there, exactly, to the query's 16-bit type): K as rows, V
+// transposed (a row per dim), double buffered, one barrier per tile. Both
+// products run on the 32x32x16 matrix cores, transposed so that a query row
+// owns a lane pair:
+//   S^T[FKT keys][32 rows] = K[FKT][D] . Q^T[D][32]    (A = K rows from LDS)
+//   O^T[D][32 rows]      += V^T[D][FKT] . P^T[FKT][32] (A = V^T rows from LDS,
+//                                                       B = P from registers)
+// Lane l holds row l % 32 in the columns of both outputs (the other half of
+// each 32 keys, or of the dims, in lane l ^ 32), so the row's softmax state,
+// maximum, sum, rescale and normalisation never leave the lane pair. The
+// k-slots of P^T's operand follow the score tile's own key order (lane half h
+// holds keys 4h + j and 8 + 4h + j of each 16); V^T is staged with its keys
+// in that order, so each of its operands is one 16-byte LDS read.
+constexpr int NXCD_PF = 8;        // XCDs of an MI355X
+constexpr int FW = 4;             // waves per workgroup
+constexpr int FR = 32;            // query rows per wave
+// score of a masked key: finite, so exp2(score * c - m) is exactly 0 without
+// a select for any c > 0 and any reference m reached by a real score
+constexpr float MASKED = -3.0e38f;
 
-template <Ty KV, int D>
-constexpr int pf_waves_per_simd() { return D == 64 ? 3 : 2; }
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Column tiles per wave: each loaded key chunk serves NT x 16 columns.
-constexpr int PNT = 2;
-
-// K rows are loaded straight in the score product's operand layout (lane l:
-// token l%16, dims 32k + 8(l/16) of step k): no lane exchange afterwards.
-// The four waves of a workgroup read each chunk, mostly from the caches, so
-// the whole-line reads that decode streams from memory with bring nothing
-// here (measured slightly slower).
-template <int D, int EB>
-struct PfKLayout {
-  static constexpr int KS = D / 32;
-  static constexpr int KDW = 8 * EB / 4;
-  static constexpr int KR = KS;
-  static constexpr int KW = KDW;
-};
-template <int D, int EB>
-__device__ __forceinline__ int pf_kdim(int k, int a) {
-  return 32 * k + 8 * a;
+template <Op O>
+__device__ __forceinline__ f32x16_t mfma32(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x16_t c) {
+  const u32x4_t av = {a[0], a[1], a[2], a[3]}, bv = {b[0], b[1], b[2], b[3]};
+  if constexpr (O == Op::BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, bv), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, av),
+                                                   __builtin_bit_cast(f16x8_t, bv), c, 0, 0, 0);
 }
 
-template <Ty KV, Ty QT, int D, int G>
-__global__ void __launch_bounds__(PW * 64)
-__attribute__((amdgpu_waves_per_eu(pf_waves_per_simd<KV, D>())))
-prefill_kernel(const PrefillParams a) {
+// sum of a packed pair of 16-bit values, added to acc
+template <Op O>
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  if constexpr (O == Op::BF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w), __builtin_bit_cast(half2_t, 0x3c003c00u),
+                                  acc, false);
+}
+
+// Position of key kk (0..15 in a 16-key block) in the staged V^T rows: bits
+// 2 and 3 swapped, so that lane half h's 8 keys (4h + j, 8 + 4h + j) are
+// contiguous at 8h.
+__device__ __forceinline__ int vt_slot(int kk) {
+  return (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+}
+
+template <int D, int FKT>
+struct FaLds {
+  static constexpr int PK = D * 2 + 16;           // bytes per staged K row (a key)
+  static constexpr int PV = FKT * 2 + 16;         // bytes per staged V^T row (a dim)
+  static constexpr int KT = FKT * PK;
+  static constexpr int VT = D * PV;
+  static constexpr int BUF = KT + VT;
+  static constexpr int BYTES = 2 * BUF;           // double buffered
+};
+
+// Keys per tile, and occupancy: 32-key tiles fit 3 waves per SIMD (at most
+// 168 registers and 37 KB of LDS at D = 128), which hides more latency when
+// the grid has many workgroups; 64-key tiles run at 2 and halve the barriers
+// and per-tile work of each workgroup, which wins when there are few (a
+// single long recompute).
+template <int FKT>
+constexpr int pf_waves_per_simd() { return FKT == 32 ? 3 : 2; }
+
+template <Ty KV, Ty QT, int D, int G, int FKT>
+__global__ void __launch_bounds__(FW * 64)
+__attribute__((amdgpu_waves_per_eu(pf_waves_per_simd<FKT>())))
+prefill_tiled_kernel(const PrefillParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group divides the 16-column tile");
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr Op OP = QT == Ty::F16 ? Op::F16 : Op::BF16;   // both products in the query's type
   constexpr int EB = TyInfo<KV>::bytes;
-  using KL = PfKLayout<D, EB>;
-  constexpr int KS = KL::KS;
-  constexpr int KR = KL::KR;
-  constexpr int KW = KL::KW;
-  constexpr int VPL = D / 16;
-  constexpr int VDW = VPL * EB / 4;
-  constexpr int NT = PNT;
-  constexpr int QTOK = 16 / G;              // query positions per column tile
-  constexpr int WTOK = NT * QTOK;           // query positions per wave
+  constexpr int KSTEPS = D / 16;                  // score products per 32 keys
+  constexpr int NB = D / 32;                      // output dim blocks = P.V products per 16 keys
+  constexpr int TPOS = FW * FR / G;               // positions per workgroup
+  constexpr int CD = 16 / EB;                     // dims per 16-byte pool chunk
+  constexpr int CPR = D / CD;                     // chunks per key row
+  constexpr int PAIRS = FKT / 2;                  // key pairs per tile
+  constexpr int NSB = FKT / 32;                   // score blocks of 32 keys per tile
+  constexpr int NKB = FKT / 16;                   // key blocks of 16 per tile
+  constexpr int JOBS = PAIRS * CPR;               // staging jobs per tile: (key pair, chunk)
+  constexpr int NJ = (JOBS + FW * 64 - 1) / (FW * 64);   // jobs per thread
+  static_assert(FKT == 32 || FKT == 64, "keys per tile");
+  using L = FaLds<D, FKT>;
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4;
-  const int n = lane & 15;                  // column: position n / G, head n % G
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;                        // row of the wave (output column)
+  const int h = lane >> 5;                        // lane half: keys / dims it holds
   const int H = a.num_kv_heads;
-  const int s = (int)(blockIdx.x / H);
-  const int kvh = (int)(blockIdx.x - (unsigned)s * H);
-  // the workgroup's waves take consecutive position groups of one (sequence,
-  // KV head): they stream the same key chunks at about the same time
-  const int t0 = ((int)(gridDim.y - 1 - blockIdx.y) * PW + wave) * WTOK;
+  // Workgroup numbering: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous stretch of the virtual order, which takes every row tile of
+  // one (sequence, KV head) in turn, longest causal range first, so the
+  // tiles that stream the same keys and values run together and share them
+  // in that XCD's L2.
+  const unsigned per_xcd = gridDim.x / NXCD_PF;
+  const unsigned vb = (blockIdx.x % NXCD_PF) * per_xcd + blockIdx.x / NXCD_PF;
+  const unsigned tiles = (unsigned)a.row_tiles;
+  const unsigned sh = vb / tiles;
+  if (sh >= (unsigned)a.num_seqs * (unsigned)H) return;          // padding to whole XCD rounds
+  const int s = (int)(sh / H);
+  const int kvh = (int)(sh - (unsigned)s * H);
+  const int tpos0 = (int)(tiles - 1 - (vb - sh * tiles)) * TPOS;   // first query index of the tile
   const int r0 = a.query_start_loc[s];
   const int nq = a.query_start_loc[s + 1] - r0;
   // rows outside the packed query array are never touched
-  if (nq <= 0 || t0 >= nq || r0 < 0 || (int64_t)r0 + nq > a.num_q_tokens) return;
-  const int rows = min(WTOK, nq - t0);      // query positions of this wave
+  if (nq <= 0 || tpos0 >= nq || r0 < 0 || (int64_t)r0 + nq > a.num_q_tokens) return;
   const int ctx = a.context_lens[s];
   const int lg = a.log2_block_size;
   const bool ctx_ok = ctx >= nq && ctx <= a.max_context_len &&
                       (((int64_t)ctx + a.block_size - 1) >> lg) <= a.max_blocks_per_seq;
 
-  f32x4_t acc[NT][VPL];
+  // this lane's query row: position index qi of the sequence's rows, head hh
+  const int R = wave * FR + n;
+  const int qi = tpos0 + R / G;
+  const int hh = R % G;
+  const bool rvalid = qi < nq;
+  const int64_t orow = (((int64_t)r0 + min(qi, nq - 1)) * a.num_q_heads + (int64_t)kvh * G + hh) * D;
+  // the wave's first and last query index, and the workgroup's last
+  const int wq0 = tpos0 + wave * FR / G;
+  const int wq1 = min(tpos0 + (wave * FR + FR - 1) / G, nq - 1);
+  const bool wave_live = wq0 < nq;
+  const int wg_last = min(tpos0 + TPOS - 1, nq - 1);
+
+  auto store_row = [&](const f32x16_t (&o)[NB], float norm) __attribute__((always_inline)) {
+    // output block mb, element v: dim 32 mb + 8(v/4) + 4h + v%4
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
-    for (int m = 0; m < VPL; ++m) acc[t][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  // output rows of tile t: column c = 4g + r of its accumulators
-  auto store_rows = [&](int t, const float (&norm)[4]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = 4 * g + r;
-      const int tok = t * QTOK + c / G;
-      if (tok < rows) {
-        const int64_t o = (((int64_t)r0 + t0 + tok) * a.num_q_heads + (int64_t)kvh * G + c % G) * D +
-                          VPL * n;
-#pragma unroll
-        for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[t][m][r] * norm[r]);
-      }
-    }
+      for (int v = 0; v < 16; ++v)
+        store_out<QT>(a.out, orow + 32 * mb + (v >> 2) * 8 + 4 * h + (v & 3), o[mb][v] * norm);
   };
-  if (!ctx_ok) {                            // invalid context or query count: NaN rows
-    const float nan4[4] = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+  if (!ctx_ok) {                                  // invalid context or query count: NaN rows
+    if (rvalid) {
+      f32x16_t o[NB];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) store_rows(t, nan4);
+      for (int m = 0; m < NB; ++m) o[m] = (f32x16_t){};
+      store_row(o, __builtin_nanf(""));
+    }
     return;
   }
+  const int pos_row = rvalid ? ctx - nq + qi : -1;     // this lane's row attends to keys <= it
+  const int wmin = ctx - nq + wq0, wmax = ctx - nq + wq1;
+  const int nkt = (ctx - nq + wg_last) / FKT + 1;      // key tiles of the workgroup (uniform)
 
-  // pools as bytes: element offsets (never negative) scale by EB, with no
-  // signed division on the load path
+  // scale in log2 units; a negative scale is folded into the query's sign,
+  // and a zero one replaced by a tiny positive one (every weight equal, as
+  // for zero, while masked keys still get exactly 0)
+  float c = a.qk_scale_log2;
+  const uint32_t qflip = c < 0.f ? 0x80008000u : 0u;
+  c = fmaxf(fabsf(c), 1e-30f);
+
+  // q of this lane's row as the B operand of the score product: dims
+  // 16k + 8h .. +8 of step k
+  uint32_t qr[KSTEPS][4];
+  {
+    const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) {
+      ld<4>(qw + ((orow + 16 * k + 8 * h) >> 1), qr[k]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qr[k][x] ^= qflip;
+    }
+  }
+
+  // ---- staging: job j = (key pair j % PAIRS, chunk j / PAIRS): both keys' chunk
+  // of K and of V. K goes to its rows as is; V's two keys are interleaved
+  // per dim (one dword per dim) into the V^T rows.
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
-  auto dw = [](const char* p, int64_t e) __attribute__((always_inline)) {
-    return reinterpret_cast<const uint32_t*>(p + e * EB);
-  };
-  const uint32_t* qw = reinterpret_cast<const uint32_t*>(a.q);
   const int bmask = a.block_size - 1;
-  const bool big_blocks = a.block_size >= PCH;
-  const float qk_scale = a.qk_scale_log2;
-  const int pos0 = ctx - nq + t0;           // position of the wave's first row
-  const int p_last = pos0 + rows - 1;
-  const int nch = p_last / PCH + 1;         // key chunks the wave needs
   const int32_t* trow = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int64_t head_off = a.layer_offset + (int64_t)kvh * a.block_size * D;
-
-  // q of each tile as the B operand: lane l holds column l%16 (rows past the
-  // wave's last repeat it; their scores are masked)
-  uint4 qr[NT][KS];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int64_t row = (((int64_t)r0 + t0 + min(t * QTOK + n / G, rows - 1)) * a.num_q_heads +
-                         (int64_t)kvh * G + n % G) * D;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      uint32_t w4[4];
-      ld<4>(qw + ((row + pf_kdim<D, EB>(k, g)) >> 1), w4);
-      qr[t][k] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-  }
-
-  // block ids of chunk j (clamped to the last chunk): lane i holds the id of
-  // the chunk's i-th block, lanes past its last block repeat the last one
-  auto fetch_ids = [&](int j) __attribute__((always_inline)) -> int {
-    j = min(j, nch - 1);
-    const int cb = j * PCH;
-    const int fb = cb >> lg;
-    const int lb = (min(cb + PCH, ctx) - 1) >> lg;
-    return trow[min(fb + lane, lb)];
+  // keys past the context (the last tile's tail) read the last key again:
+  // finite values behind masked scores; table entries past the context are
+  // never read
+  auto key_at = [&](int kt, int jb, int odd) __attribute__((always_inline)) {
+    return min(kt * FKT + 2 * (jb % PAIRS) + odd, ctx - 1);
   };
-  bool bad = false;                         // a bad block id was seen
-  auto load_kv = [&](int j, int idr, uint32_t (&kr)[KR][KW], uint32_t (&vr)[4][VDW])
-      __attribute__((always_inline)) {
-    j = min(j, nch - 1);
-    const int cb = j * PCH;
-    const int fb = cb >> lg;
-    const bool badl = idr < 0 || idr >= a.num_blocks;
-    bad = bad || __any(badl);
-    const int idv = badl ? 0 : idr;
-
-    auto elem_of = [&](int t) __attribute__((always_inline)) -> int64_t {   // element of token t, dim 0
-      t = min(t, ctx - 1);
-      const int id = big_blocks ? __builtin_amdgcn_readfirstlane(idv) : __shfl(idv, (t >> lg) - fb);
-      return (int64_t)id * a.block_stride + head_off + (int64_t)(t & bmask) * D;
-    };
-    // K in the operand layout (lane l: token l%16, dims 32k + 8(l/16)); V
-    // rows 4(l/16) .. +3, dims VPL*(l%16) .. +VPL
-    int64_t ek, ev[4];
-    if (big_blocks) {
-      const int64_t base = elem_of(cb);
-      ek = base + (int64_t)min(n, ctx - 1 - cb) * D + 8 * g;
+  auto job_of = [&](int i) __attribute__((always_inline)) { return tid + FW * 64 * i; };
+  auto fetch_ids = [&](int kt, int (&ids)[NJ][2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ev[r] = base + (int64_t)min(4 * g + r, ctx - 1 - cb) * D + VPL * n;
-    } else {
-      ek = elem_of(cb + n) + 8 * g;
+    for (int i = 0; i < NJ; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ev[r] = elem_of(cb + 4 * g + r) + VPL * n;
-    }
-#pragma unroll
-    for (int k = 0; k < KS; ++k) ld<KW>(dw(kpool, ek + 32 * k), kr[k]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ld<VDW>(dw(vpool, ev[r]), vr[r]);
+      for (int o = 0; o < 2; ++o) ids[i][o] = trow[key_at(kt, job_of(i) % JOBS, o) >> lg];
   };
-
-  float m_ref[NT], l_sum[NT];
+  bool bad = false;                               // a bad block id was staged
+  uint32_t stk[NJ][2][4], stv[NJ][2][4];
+  auto load_tile = [&](int kt, const int (&ids)[NJ][2]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    m_ref[t] = -__builtin_inff();           // reference max of the column (log2 units)
-    l_sum[t] = 0.f;                         // this lane's share of the column's sum
-  }
-  auto process = [&](int j, const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW])
-      __attribute__((always_inline)) {
-    const int cb = j * PCH;
-    uint32_t kraw[KS][KL::KDW];
+    for (int i = 0; i < NJ; ++i) {
+      const int jb = job_of(i) % JOBS;            // (a thread past the jobs repeats one)
 #pragma unroll
-    for (int k = 0; k < KS; ++k)
-#pragma unroll
-      for (int x = 0; x < KL::KDW; ++x) kraw[k][x] = kr[k][x];
-    uint32_t vb[VPL][2];                    // P.V B operands, shared by the tiles
-    if constexpr (KV == Ty::FP8) {
-      bool live[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
-      pv_operands_fp8<D>(vr, live, vb);
-    } else {
-      uint32_t vw[4][D / 32];
-      if (cb + PCH <= ctx) {                // whole chunk: every value row is live
-        const bool live[4] = {true, true, true, true};
-        v_operand<KV, QT, D>(vr, live, vw);
-      } else {
-        bool live[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) live[r] = cb + 4 * g + r < ctx;
-        v_operand<KV, QT, D>(vr, live, vw);
+      for (int o = 0; o < 2; ++o) {
+        const int k = key_at(kt, jb, o);
+        const bool ok = ids[i][o] >= 0 && ids[i][o] < a.num_blocks;
+        bad = bad || !ok;
+        const int64_t e = (int64_t)(ok ? ids[i][o] : 0) * a.block_stride + head_off +
+                          (int64_t)(k & bmask) * D + (jb / PAIRS) * CD;
+        ld<4>(reinterpret_cast<const uint32_t*>(kpool + e * EB), stk[i][o]);
+        ld<4>(reinterpret_cast<const uint32_t*>(vpool + e * EB), stv[i][o]);
       }
-      pv_operands<D>(vw, vb);
     }
-    // a chunk wholly before the wave's first position needs no causal mask
-    const bool below = cb + PCH - 1 <= pos0;
-    const bool full_wave = rows == WTOK;
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    char* kb = lds + buf * L::BUF;
+    char* vb = kb + L::KT;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tok = t * QTOK + n / G;
-      const int pcol = pos0 + tok;          // position of this column
-      if (t * QTOK >= rows) break;          // tile past the wave's rows (uniform)
-      const f32x4_t sc = chunk_scores_raw<KV, QT, D>(kraw, [&](int k) {
-        return qr[t][k];
-      });
-      float z[4];
-      if (below && full_wave) {
+    for (int i = 0; i < NJ; ++i) {
+      if (JOBS % (FW * 64) != 0 && job_of(i) >= JOBS) continue;
+      const int jb = job_of(i);
+      const int key = 2 * (jb % PAIRS), ch = jb / PAIRS;
+      // the two keys' values as 16-bit pairs (dims 2q, 2q+1 in dword q)
+      uint32_t w[2][CD / 2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = sc[r] * qk_scale;
-      } else if (below) {
+      for (int o = 0; o < 2; ++o) {
+        if constexpr (EB == 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] = tok < rows ? sc[r] * qk_scale : -__builtin_inff();
-      } else {
+          for (int x = 0; x < 4; ++x) w[o][x] = stk[i][o][x];
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tk = cb + 4 * g + r;
-          z[r] = (tok < rows && tk <= pcol) ? sc[r] * qk_scale : -__builtin_inff();
+          for (int x = 0; x < 4; ++x) fp8x4_to<OP>(stk[i][o][x], w[o][2 * x], w[o][2 * x + 1]);
+        }
+        char* dst = kb + (key + o) * L::PK + ch * CD * 2;
+#pragma unroll
+        for (int x = 0; x < CD / 8; ++x)
+          *reinterpret_cast<uint4*>(dst + 16 * x) =
+              make_uint4(w[o][4 * x], w[o][4 * x + 1], w[o][4 * x + 2], w[o][4 * x + 3]);
+        if constexpr (EB == 2) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[o][x] = stv[i][o][x];
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) fp8x4_to<OP>(stv[i][o][x], w[o][2 * x], w[o][2 * x + 1]);
         }
       }
-      softmax_pv_b<KV, QT, D>(z, vb, acc[t], m_ref[t], l_sum[t], lane);
+      // V^T: dim d's dword holds (key, key + 1) at the pair's slot
+      char* vdst = vb + ((key & ~15) + vt_slot(key & 15)) * 2;
+#pragma unroll
+      for (int q = 0; q < CD / 2; ++q) {
+        const int d = ch * CD + 2 * q;
+        *reinterpret_cast<uint32_t*>(vdst + d * L::PV) = __builtin_amdgcn_perm(w[1][q], w[0][q], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vdst + (d + 1) * L::PV) = __builtin_amdgcn_perm(w[1][q], w[0][q], 0x07060302u);
+      }
     }
   };
 
-  uint32_t kA[KR][KW], vA[4][VDW], kB[KR][KW], vB[4][VDW];
-  int iA = fetch_ids(0);
-  int iB = fetch_ids(1);
-  load_kv(0, iA, kA, vA);
-  // One exit, at the end of the pair: chunk nch (odd nch) is processed as a
-  // no-op (its rows are past the context: V reads as zero, every score is
-  // masked). A leave after the first chunk of the pair would reach the loop
-  // latch with B's loads unread (the divergent loop is put in single-exit
-  // form), and the wait analysis would then drain A's loads at the top of
-  // every pair before B's registers are reused.
-  for (int j = 0; j < nch; j += 2) {
-    iA = fetch_ids(j + 2);
-    load_kv(j + 1, iB, kB, vB);
-    process(j, kA, vA);
-    iB = fetch_ids(j + 3);
-    load_kv(j + 2, iA, kA, vA);
-    process(j + 1, kB, vB);
-  }
+  // ---- per-row state: reference max (log2 units), this lane's share of the
+  // sum, and O^T (block mb, element v: dim 32 mb + 8(v/4) + 4h + v%4)
+  float m_ref = -__builtin_inff();
+  float l_sum = 0.f;
+  f32x16_t o[NB];
+#pragma unroll
+  for (int m = 0; m < NB; ++m) o[m] = (f32x16_t){};
 
+  auto compute = [&](int kt, int buf) __attribute__((always_inline)) {
+    const char* kb = lds + buf * L::BUF;
+    const char* vb = kb + L::KT;
+    // scores: sb[b][v] is key 32b + 8(v/4) + 4h + v%4 of the tile, row n
+    f32x16_t sb[NSB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float norm[4];
+    for (int b = 0; b < NSB; ++b) {
+      // all of the block's K operands first, then the products
+      uint4 kv[KSTEPS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float lt = l_sum[t] + __shfl_xor(l_sum[t], 16);
-      lt += __shfl_xor(lt, 32);
-      norm[r] = bad ? __builtin_nanf("") : a.v_scale / __shfl(lt, 4 * g + r);
+      for (int k = 0; k < KSTEPS; ++k)
+        kv[k] = *reinterpret_cast<const uint4*>(kb + (32 * b + n) * L::PK + (16 * k + 8 * h) * 2);
+      sb[b] = (f32x16_t){};
+#pragma unroll
+      for (int k = 0; k < KSTEPS; ++k) {
+        const uint32_t av[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
+        sb[b] = mfma32<OP>(av, qr[k], sb[b]);
+      }
     }
-    store_rows(t, norm);
+    // causal mask: key 32b + 8(v/4) + v%4 + 4h of the tile <= pos_row (a
+    // tile wholly before the wave's first position masks nothing)
+    {
+      const int thr = kt * FKT + FKT - 1 > wmin ? pos_row - kt * FKT - 4 * h : FKT;
+#pragma unroll
+      for (int b = 0; b < NSB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * b + (v >> 2) * 8 + (v & 3) > thr) sb[b][v] = MASKED;
+    }
+    float mx = MASKED;
+#pragma unroll
+    for (int b = 0; b < NSB; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sb[b][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // a row with no key here (all masked) leaves its reference alone
+    const float zmax = mx <= MASKED ? -__builtin_inff() : mx * c;
+    if (__any(zmax > m_ref + SM_TAU)) {
+      const float mn = fmaxf(m_ref, zmax);
+      const float al = mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
+      m_ref = mn;
+      l_sum *= al;
+#pragma unroll
+      for (int m = 0; m < NB; ++m) o[m] *= al;
+    }
+    // probabilities as the B operand of P.V, key block kb (16 keys): k-slot j
+    // is key 16kb + 8(j/4) + 4h + j%4, score element v = 8(kb%2) + j; the row
+    // sum adds exactly the rounded values the matrix core multiplies
+    uint32_t pk[NKB][4];
+    const float nm = -m_ref;
+#pragma unroll
+    for (int b = 0; b < NSB; ++b) {
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(fmaf(sb[b][v], c, nm));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t w = pack2<OP>(p[2 * q], p[2 * q + 1]);
+        pk[2 * b + (q >> 2)][q & 3] = w;
+        l_sum = add_pair<OP>(w, l_sum);
+      }
+    }
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2) {
+      uint4 vv[NB];
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb)
+        vv[mb] = *reinterpret_cast<const uint4*>(vb + (32 * mb + n) * L::PV + (16 * kb2 + 8 * h) * 2);
+#pragma unroll
+      for (int mb = 0; mb < NB; ++mb) {
+        const uint32_t av[4] = {vv[mb].x, vv[mb].y, vv[mb].z, vv[mb].w};
+        o[mb] = mfma32<OP>(av, pk[kb2], o[mb]);
+      }
+    }
+  };
+
+  // ---- the tile loop: loads of tile kt+1 and block ids of tile kt+2 in
+  // flight while tile kt is processed from LDS; one barrier per tile
+  int ids_a[NJ][2], ids_b[NJ][2];
+  fetch_ids(0, ids_a);
+  load_tile(0, ids_a);
+  if (nkt > 1) fetch_ids(1, ids_b);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool more = kt + 1 < nkt;
+    if (more) load_tile(kt + 1, ids_b);
+    if (kt + 2 < nkt) fetch_ids(kt + 2, ids_a);
+    // a wave with no rows, or whose rows all end before this tile, skips it
+    if (wave_live && kt * FKT <= wmax) compute(kt, kt & 1);
+    if (more) store_tile((kt + 1) & 1);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NJ; ++i) {
+      ids_b[i][0] = ids_a[i][0];
+      ids_b[i][1] = ids_a[i][1];
+    }
   }
+  bad = __syncthreads_or(bad);
+  if (!rvalid) return;
+  const float lt = l_sum + __shfl_xor(l_sum, 32);
+  store_row(o, bad ? __builtin_nanf("") : a.v_scale / lt);
 }
 
-template <Ty KV, Ty QT, int D>
+template <Ty KV, Ty QT, int D, int FKT>
 hipError_t launch_g(const PrefillParams& a, int g, dim3 grid, hipStream_t st) {
   switch (g) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 1>), grid, dim3(PW * 64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 2>), grid, dim3(PW * 64), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 4>), grid, dim3(PW * 64), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 8>), grid, dim3(PW * 64), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<KV, QT, D, 16>), grid, dim3(PW * 64), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 1, FKT>), grid, dim3(FW * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 2, FKT>), grid, dim3(FW * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 4, FKT>), grid, dim3(FW * 64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 8, FKT>), grid, dim3(FW * 64), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 16, FKT>), grid, dim3(FW * 64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <Ty KV, Ty QT>
-hipError_t launch_d(const PrefillParams& a, int g, dim3 grid, hipStream_t st) {
-  if (a.head_dim == 64) return launch_g<KV, QT, 64>(a, g, grid, st);
-  if (a.head_dim == 128) return launch_g<KV, QT, 128>(a, g, grid, st);
+hipError_t launch_d(const PrefillParams& a, int g, dim3 grid, bool wide, hipStream_t st) {
+  if (a.head_dim == 64) return wide ? launch_g<KV, QT, 64, 64>(a, g, grid, st) : launch_g<KV, QT, 64, 32>(a, g, grid, st);
+  if (a.head_dim == 128) return wide ? launch_g<KV, QT, 128, 64>(a, g, grid, st) : launch_g<KV, QT, 128, 32>(a, g, grid, st);
   return hipErrorInvalidValue;
 }
 
@@ -316,20 +419,33 @@ bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g) {
          (g == 1 || g == 2 || g == 4 || g == 8 || g == 16);
 }
 
-// Workgroups along the query rows: each covers PW * PNT * (16 / g) positions.
+// Workgroups along the query rows: each covers 128 / g positions.
 int prefill_tiles(int g, int max_query_len) {
-  const int64_t per = PW * PNT * (16 / g);
+  const int64_t per = FW * FR / g;
   return (int)(((int64_t)max_query_len + per - 1) / per);
 }
 
-hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
+hipError_t launch_prefill(const PrefillParams& a0, int kv_ty, int q_ty, int g, int max_query_len,
                           hipStream_t st) {
-  const dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_kv_heads), (unsigned)prefill_tiles(g, max_query_len));
+  PrefillParams a = a0;
+  a.row_tiles = prefill_tiles(g, max_query_len);
+  const int64_t used = (int64_t)a.num_seqs * a.num_kv_heads * a.row_tiles;
+  int64_t wgs = (used + NXCD_PF - 1) / NXCD_PF * NXCD_PF;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs);
+  // 64-key tiles when the grid is at most two rounds of two workgroups per
+  // compute unit (few, long workgroups), 32-key tiles otherwise
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const bool wide = used <= (int64_t)4 * cus;
   const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
-  if (kv == Ty::BF16 && q == Ty::BF16) return launch_d<Ty::BF16, Ty::BF16>(a, g, grid, st);
-  if (kv == Ty::F16 && q == Ty::F16) return launch_d<Ty::F16, Ty::F16>(a, g, grid, st);
-  if (kv == Ty::FP8 && q == Ty::BF16) return launch_d<Ty::FP8, Ty::BF16>(a, g, grid, st);
-  if (kv == Ty::FP8 && q == Ty::F16) return launch_d<Ty::FP8, Ty::F16>(a, g, grid, st);
+  if (kv == Ty::BF16 && q == Ty::BF16) return launch_d<Ty::BF16, Ty::BF16>(a, g, grid, wide, st);
+  if (kv == Ty::F16 && q == Ty::F16) return launch_d<Ty::F16, Ty::F16>(a, g, grid, wide, st);
+  if (kv == Ty::FP8 && q == Ty::BF16) return launch_d<Ty::FP8, Ty::BF16>(a, g, grid, wide, st);
+  if (kv == Ty::FP8 && q == Ty::F16) return launch_d<Ty::FP8, Ty::F16>(a, g, grid, wide, st);
   return hipErrorInvalidValue;
 }
 

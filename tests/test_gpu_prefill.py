@@ -149,3 +149,37 @@ def test_prefill_argument_errors():
         pa.prefill(st.cache, 3, q, tt, ct, 8, qt, 8, 0.1)
     with pytest.raises(ValueError):                    # query_start_loc of the wrong length
         pa.prefill(st.cache, 0, q, tt, ct, 8, qt[:1], 8, 0.1)
+
+
+LARGE_GRID = [
+    # pool,      q,      D,   G, B
+    ("bf16", "bf16", 128, 4, 16),
+    ("f16", "f16", 64, 2, 8),
+    ("fp8_e4m3", "bf16", 128, 8, 16),
+    ("fp8_e4m3", "f16", 64, 1, 4),
+    ("bf16", "bf16", 128, 16, 32),
+]
+
+
+@pytest.mark.parametrize("pool,q,D,G,B", LARGE_GRID)
+def test_prefill_large_grid_matches_oracle(pool, q, D, G, B):
+    """A batch whose grid has more than four workgroups per compute unit
+    (200 sequences x 8 KV heads), so the kernel runs its 32-key tiles at
+    three waves per SIMD; whole prompts, later chunks and single rows, every
+    row against the oracle."""
+    rng = np.random.default_rng(zlib.crc32(repr((pool, q, D, G, B)).encode()) % 1000)
+    ctx = rng.integers(1, 200, 200)
+    nq = np.where(rng.random(200) < 0.5, ctx, np.maximum(1, (ctx * rng.random(200)).astype(np.int64)))
+    wl = workloads.custom(int(rng.integers(1000)), ctx, pool_dtype=pool, q_dtype=q,
+                          num_q_heads=8 * G, num_kv_heads=8, head_dim=D, block_size=B)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    qc, qsl = workloads.prefill_queries(wl, nq, 17)
+    out = _run(st, qc, qsl)
+    got = codecs.decode(tensor_codes(out), q)
+    ref = _oracle(st, qc, qsl)
+    assert np.all(np.isfinite(got))
+    err = max_err(got, ref)
+    ex = max_err_stored(got, ref, q, TOL[pool])
+    say(f"{int(qsl[-1])} rows, max abs err {err:.3e}, with the output-rounding allowance {ex:.3e}")
+    assert ex <= TOL[pool]
