@@ -261,7 +261,7 @@ pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void
 
 /* ------------------------------------------------------------------------ */
 /* pa_decode_shared — pa_decode that reads a prefix shared by several        */
-/* sequences once per group of up to 16 / g of them.                         */
+/* sequences once per group of up to 32 / g of them.                         */
 /*                                                                           */
 /* Same arguments and same result as pa_decode. Parallel samples of one      */
 /* prompt share the prompt's blocks ("Efficient Memory Management ... with   */
@@ -271,9 +271,9 @@ pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void
 /* found in the block tables: a run of consecutive sequences, each naming    */
 /* the same leading blocks as the one before for at least 16 tokens, shares */
 /* the common prefix of all its members (rounded down to a multiple of 16   */
-/* tokens and capped by every member's context). Up to 16 / g members at a   */
-/* time attend to that prefix together, their queries side by side in one   */
-/* matrix-core tile, so each prefix block is read once per group; each      */
+/* tokens and capped by every member's context). Up to 32 / g members at a   */
+/* time attend to that prefix together, their queries side by side in two   */
+/* matrix-core tiles, so each prefix block is read once per group; each     */
 /* member then attends to the rest of its context, starting from the        */
 /* prefix's partial result. Put the samples of one prompt next to each      */
 /* other in the batch; sequences that share nothing cost one extra pass     */

@@ -268,7 +268,7 @@ DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* 
 }
 
 // Shared-prefix decode: the suffix pass's pieces and merge descriptors (the
-// usual decode workspace), the prefix pass's pieces (16 columns per slot),
+// usual decode workspace), the prefix pass's pieces (32 columns per slot),
 // the plan (shared lengths, starts, slot records) and the team range of
 // each prefix segment.
 struct SharedLayout {
@@ -295,7 +295,7 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
   L->suf = ws_layout(pa::sk_slots(L->blocks_suf, num_seqs, H) * g, c->head_dim,
                      (size_t)L->blocks_suf * 4);
   L->pre_base = L->suf.total;
-  L->pre = ws_layout(pa::sk_slots(L->blocks_pre, num_seqs, H) * 16, c->head_dim,
+  L->pre = ws_layout(pa::sk_slots(L->blocks_pre, num_seqs, H) * pa::PA_PREFIX_COLS, c->head_dim,
                      (size_t)L->blocks_pre * 4);
   const size_t S = (size_t)num_seqs;
   L->lcp = L->pre_base + L->pre.total;
@@ -657,7 +657,18 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   a.pre_m = reinterpret_cast<float*>(w + L.pm);
   a.pre_l = reinterpret_cast<float*>(w + L.pl);
   a.pre_o = reinterpret_cast<float*>(w + L.po);
-  a.pre_teams = L.blocks_pre * 4 / a.team;
+  // The prefix pass runs on at most half the resident workgroups: a prefix
+  // chunk serves up to 32 query columns (two matrix tiles), twice a plain
+  // decode chunk's arithmetic, and fewer, longer team ranges halve the
+  // pieces the combine reads (32 prompts x 8 samples, fp16: prefix pass plus
+  // combine 41 us on half the grid, 49 us on all of it, 53 us on a quarter).
+  // A batch has at most num_seqs / 2 prefix slots, which caps small batches
+  // as in the plain decode.
+  const int pre_blocks =
+      std::min(pa::sk_launch_blocks(L.blocks_pre, std::max(1, num_seqs / 2), max_context_len,
+                                    cache->num_kv_heads),
+               std::max(8, L.blocks_pre / 2 / 8 * 8));
+  a.pre_teams = pre_blocks * 4 / a.team;
   const int kv = (int)cache->dtype, qt = (int)q_dtype;
   if (!reuse_plan && pa::launch_share_plan(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
   // prefix pass: pieces into its own region
@@ -666,7 +677,7 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   a.ws_m = reinterpret_cast<float*>(wp + L.pre.m);
   a.ws_l = reinterpret_cast<float*>(wp + L.pre.l);
   a.ws_team = reinterpret_cast<int32_t*>(wp + L.pre.team);
-  if (pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_pre, 1, stream) != hipSuccess)
+  if (pa::launch_attend_shared(a, kv, qt, L.g, pre_blocks, 1, stream) != hipSuccess)
     return PA_ERR_HIP;
   // the prefix pieces, combined per sequence and head
   a.pre_ws_o = a.ws_o;

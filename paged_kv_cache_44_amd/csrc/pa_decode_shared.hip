@@ -1,5 +1,5 @@
 // pa_decode_shared.hip — decode that reads a prefix shared by several
-// sequences once per group of up to 16/G of them ("Efficient Memory
+// sequences once per group of up to 32/G of them ("Efficient Memory
 // Management for Large Language Model Serving with PagedAttention",
 // sampling paragraph: parallel samples of one prompt share its blocks;
 // "Continuous Batching and PagedAttention", section "Sharing, the part that
@@ -15,7 +15,7 @@
 //     sharing at least 16 tokens with the one before; a run shares the
 //     minimum of those lengths (the common prefix of all its members),
 //     rounded down to a multiple of 16. Each member starts its own pass
-//     after it (share_start), and each group of up to 16/G consecutive
+//     after it (share_start), and each group of up to 32/G consecutive
 //     members is one prefix slot, kept at its first member's index; every
 //     member records its slot (share_desc).
 // Then the matrix-core kernel's prefix pass, prefix_combine_kernel, and the
@@ -96,7 +96,7 @@ __device__ __forceinline__ int scan_min_bwd(int v, int* s_wave) {
 
 template <int G>
 __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
-  constexpr int NS = 16 / G;                     // sequences per prefix slot
+  constexpr int NS = PA_PREFIX_COLS / G;         // sequences per prefix slot
   constexpr int E = (PA_SK_MAX_SEQS + PT - 1) / PT;   // sequences per thread at most
   extern __shared__ int s_min[];                 // [num_seqs]: run minimum, at its first member
   __shared__ int s_buf[PT];
@@ -190,14 +190,14 @@ __global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams 
   float M = -__builtin_inff(), L = 0.f, O[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) O[i] = 0.f;
-  if (!prefix_segment(a, s, kvh / T, HG, 16 / G, G, cs, col0, t0, t1, ccp)) L = __builtin_nanf("");
+  if (!prefix_segment(a, s, kvh / T, HG, PA_PREFIX_COLS / G, G, cs, col0, t0, t1, ccp)) L = __builtin_nanf("");
   for (int tb = t0; tb <= t1; tb += NB) {
     float mv[NB], lv[NB], ov[NB][DPL];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int tm = tb + u;
       const bool ok = tm <= t1 && team_begin(tm, ccp, a.pre_teams) != team_begin(tm + 1, ccp, a.pre_teams);
-      const int64_t sl = ((tm + cs) * T + kvh % T) * 16 + col0 + hh;
+      const int64_t sl = ((tm + cs) * T + kvh % T) * PA_PREFIX_COLS + col0 + hh;
       mv[u] = ok ? a.pre_ws_m[ok ? sl : 0] : -__builtin_inff();
       lv[u] = ok ? a.pre_ws_l[ok ? sl : 0] : 0.f;
       const float* po = a.pre_ws_o + (ok ? sl : 0) * D + d0;

@@ -50,12 +50,13 @@
 // Serving with PagedAttention", sampling paragraph: parallel samples share
 // the prompt's blocks; "Continuous Batching and PagedAttention", section
 // "Sharing, the part that goes beyond fixing what broke") are read once per
-// up to 16/G sequences instead of once per sequence, in two passes of the
+// up to 32/G sequences instead of once per sequence, in two passes of the
 // same kernel:
-//  * M_PREFIX: a segment is a slot of up to 16/G consecutive sequences
-//    whose tables share the prefix blocks; their queries fill the 16 tile
-//    columns side by side (column c: sequence first + c/G, head c%G), so
-//    each K/V chunk of the prefix is loaded once for all of them. Every
+//  * M_PREFIX: a segment is a slot of up to 32/G consecutive sequences
+//    whose tables share the prefix blocks; their queries fill the 32
+//    columns of two tiles side by side (column c: sequence first + c/G,
+//    head c%G), so each K/V chunk of the prefix is loaded once for all of
+//    them (its operands built once, both tiles' products from them). Every
 //    piece is left as a partial (m, l, o) per column, and the team range of
 //    each prefix segment is recorded.
 //  * prefix_combine_kernel (pa_decode_shared.hip) combines each sequence's
@@ -151,7 +152,8 @@ attend_sk_kernel(const DecodeParams a) {
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
   static_assert(MODE == M_PLAIN || MODE == M_PREFIX || MODE == M_SUFFIX, "mode");
-  constexpr int GC = MODE == M_PREFIX ? 16 : G;   // tile columns holding queries
+  constexpr int GC = MODE == M_PREFIX ? PA_PREFIX_COLS : G;   // columns holding queries
+  constexpr int NT = MODE == M_PREFIX ? PA_PREFIX_COLS / 16 : 1;   // 16-column tiles per chunk
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int EB = TyInfo<KV>::bytes;
   constexpr int KS = D / 32;              // score MFMA steps
@@ -170,8 +172,8 @@ attend_sk_kernel(const DecodeParams a) {
   // in each segment's last chunk (1..16), so a segment spans 16 (chunks - 1)
   // + tail tokens
   extern __shared__ int s_cum[];
-  // per wave: the q B-operand of the piece being processed, [step][lane]
-  __shared__ uint4 s_q[NWM][KS][64];
+  // per wave: the q B-operand of the piece being processed, [tile][step][lane]
+  __shared__ uint4 s_q[NWM][NT][KS][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -195,7 +197,7 @@ attend_sk_kernel(const DecodeParams a) {
           // slot s: its sequences and the prefix they share (a multiple of
           // 16); a descriptor that does not fit the batch and table is idle
           const int4 sd = reinterpret_cast<const int4*>(a.share_desc)[s];
-          const bool fits = sd.y >= 1 && sd.y <= 16 / G && sd.x >= 0 && sd.x + sd.y <= S &&
+          const bool fits = sd.y >= 1 && sd.y <= GC / G && sd.x >= 0 && sd.x + sd.y <= S &&
                             sd.z > 0 && seq_chunks(a, sd.z) > 0 && (sd.z & (CH - 1)) == 0;
           v = fits ? sd.z / CH : 0;
           s_aux[s] = fits ? (uint32_t)sd.x | ((uint32_t)sd.y << 16) : 0u;
@@ -394,27 +396,34 @@ attend_sk_kernel(const DecodeParams a) {
   };
 
   // q of this wave's KV head in chunk d's segment as the B operand (lane l:
-  // head l%16, dims 32k + 8(l/16) .. +8), fetched into qn with a piece's
-  // first chunk and put into LDS at the start of the next pipeline step,
-  // after the piece before it has been processed. Columns past the G heads
-  // repeat a real head's row: their scores are masked out. M_PREFIX: column
-  // l%16 is head (l%16)%G of the slot's sequence (l%16)/G.
-  uint32_t qn[KS][4];
+  // column 16t + l%16 of tile t, dims 32k + 8(l/16) .. +8), fetched into qn
+  // with a piece's first chunk and put into LDS at the start of the next
+  // pipeline step, after the piece before it has been processed. Columns
+  // past the G heads repeat a real head's row: their scores are masked out.
+  // M_PREFIX: column c is head c%G of the slot's sequence c/G.
+  uint32_t qn[NT][KS][4];
   bool qpend = false;
   auto load_q = [&](const Desc& d) __attribute__((always_inline)) {
     if ((d.f & (F_VALID | F_FIRST)) == (F_VALID | F_FIRST)) {
-      int qseq = d.seq;
-      if constexpr (MODE == M_PREFIX) qseq = (d.x & 0xffff) + min(n / G, (d.x >> 16) - 1);
-      const int64_t row = ((int64_t)qseq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G + (n % G)) * D;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim(k, g)) >> 1), qn[k]);
+      for (int t = 0; t < NT; ++t) {
+        const int col = 16 * t + n;
+        int qseq = d.seq;
+        if constexpr (MODE == M_PREFIX) qseq = (d.x & 0xffff) + min(col / G, (d.x >> 16) - 1);
+        const int64_t row = ((int64_t)qseq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G + (col % G)) * D;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) ld<4>(qw + ((row + kdim(k, g)) >> 1), qn[t][k]);
+      }
       qpend = true;
     }
   };
   auto flush_q = [&]() __attribute__((always_inline)) {
     if (qpend) {
 #pragma unroll
-      for (int k = 0; k < KS; ++k) s_q[wave][k][lane] = make_uint4(qn[k][0], qn[k][1], qn[k][2], qn[k][3]);
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          s_q[wave][t][k][lane] = make_uint4(qn[t][k][0], qn[t][k][1], qn[t][k][2], qn[t][k][3]);
       qpend = false;
     }
   };
@@ -475,20 +484,23 @@ attend_sk_kernel(const DecodeParams a) {
     }
   };
 
-  // ---- compute stage state of the current piece
+  // ---- compute stage state of the current piece, per column tile
   int pj0 = 0;                                       // first chunk of the piece
-  f32x4_t acc[VPL];
+  f32x4_t acc[NT][VPL];
+  float m_ref[NT], l_sum[NT];                        // reference max of column n (log2 units),
+                                                     // this lane's probability sum
 #pragma unroll
-  for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m_ref = -__builtin_inff();                   // reference max of head n (log2 units)
-  float l_sum = 0.f;                                 // this lane's probability sum (head n)
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int m = 0; m < VPL; ++m) acc[t][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    m_ref[t] = -__builtin_inff();
+    l_sum[t] = 0.f;
+  }
 
   // Write the piece that ends with chunk d (final rows or a partial) and
   // reset the state.
   auto finish_piece = [&](const Desc& d) __attribute__((always_inline)) {
     const bool bad = d.f & F_BAD;
-    float lt = l_sum + __shfl_xor(l_sum, 16);
-    lt += __shfl_xor(lt, 32);
     const int j0 = first_chunk(d.x);
     const bool whole = (pj0 == j0) && (d.j + 1 == j0 + d.nc);
     const int kvh = d.hg * T + ti;
@@ -496,32 +508,38 @@ attend_sk_kernel(const DecodeParams a) {
     const int64_t cseg = (int64_t)d.seq * HG + d.hg;
     const int ncol = MODE == M_PREFIX ? G * (d.x >> 16) : G;   // columns holding queries
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 4 * g + r;                      // accumulator row = column (head)
-      const float lh = __shfl(lt, h);
-      const float mh = __shfl(m_ref, h);
-      if (h < ncol) {
-        if (whole && MODE != M_PREFIX) {
-          const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
-          const int64_t o = out_row0 + (int64_t)h * D + VPL * n;
+    for (int t = 0; t < NT; ++t) {
+      float lt = l_sum[t] + __shfl_xor(l_sum[t], 16);
+      lt += __shfl_xor(lt, 32);
 #pragma unroll
-          for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[m][r] * norm);
-        } else {
-          const int64_t slot = ((team + cseg) * T + ti) * GC + h;
-          float* wo = a.ws_o + slot * D + VPL * n;
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * g + r;                    // accumulator row = column of the tile
+        const int col = 16 * t + h;
+        const float lh = __shfl(lt, h);
+        const float mh = __shfl(m_ref[t], h);
+        if (col < ncol) {
+          if (whole && MODE != M_PREFIX) {
+            const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
+            const int64_t o = out_row0 + (int64_t)col * D + VPL * n;
 #pragma unroll
-          for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[m][r];
-          if (n == 0) {
-            a.ws_m[slot] = bad ? 0.f : mh;
-            a.ws_l[slot] = bad ? __builtin_nanf("") : lh;
+            for (int m = 0; m < VPL; ++m) store_out<QT>(a.out, o + m, acc[t][m][r] * norm);
+          } else {
+            const int64_t slot = ((team + cseg) * T + ti) * GC + col;
+            float* wo = a.ws_o + slot * D + VPL * n;
+#pragma unroll
+            for (int m = 0; m < VPL; ++m) wo[m] = bad ? __builtin_nanf("") : acc[t][m][r];
+            if (n == 0) {
+              a.ws_m[slot] = bad ? 0.f : mh;
+              a.ws_l[slot] = bad ? __builtin_nanf("") : lh;
+            }
           }
         }
       }
-    }
 #pragma unroll
-    for (int m = 0; m < VPL; ++m) acc[m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    m_ref = -__builtin_inff();
-    l_sum = 0.f;
+      for (int m = 0; m < VPL; ++m) acc[t][m] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      m_ref[t] = -__builtin_inff();
+      l_sum[t] = 0.f;
+    }
   };
 
   auto process_chunk = [&](const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW],
@@ -533,31 +551,58 @@ attend_sk_kernel(const DecodeParams a) {
         // shared prefix's partial (state layout of softmax_pv: column n =
         // head n's max and sum, accumulator rows 4g + r = heads)
         const int64_t r0 = (int64_t)d.seq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G;
-        m_ref = n < G ? a.pre_m[r0 + n] : -__builtin_inff();
-        l_sum = (n < G && g == 0) ? a.pre_l[r0 + n] : 0.f;
+        m_ref[0] = n < G ? a.pre_m[r0 + n] : -__builtin_inff();
+        l_sum[0] = (n < G && g == 0) ? a.pre_l[r0 + n] : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (4 * g + r < G) {
             const float* po = a.pre_o + (r0 + 4 * g + r) * D + VPL * n;
 #pragma unroll
-            for (int m = 0; m < VPL; ++m) acc[m][r] = po[m];
+            for (int m = 0; m < VPL; ++m) acc[0][m][r] = po[m];
           }
         }
       }
     }
     const int ctx = d.ctx;
     const int cb = d.j * CH;
-    const f32x4_t s = chunk_scores<KV, QT, D>(kr, [&](int k) { return s_q[wave][k][lane]; }, lane);
     const bool tail = cb + CH > ctx;
-    float z[4];
     bool live[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool valid = (n < (MODE == M_PREFIX ? G * (d.x >> 16) : G)) && (cb + 4 * g + r < ctx);
-      z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
-      live[r] = !tail || cb + 4 * g + r < ctx;
+    for (int r = 0; r < 4; ++r) live[r] = !tail || cb + 4 * g + r < ctx;
+    const int ncol = MODE == M_PREFIX ? G * (d.x >> 16) : G;
+    if constexpr (NT == 1) {
+      const f32x4_t s = chunk_scores<KV, QT, D>(kr, [&](int k) { return s_q[wave][0][k][lane]; }, lane);
+      float z[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = n < ncol && cb + 4 * g + r < ctx;
+        z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
+      }
+      chunk_softmax_pv<KV, QT, D>(z, vr, live, acc[0], m_ref[0], l_sum[0], lane);
+    } else {
+      // several column tiles: the chunk's K and V operands are built once
+      uint32_t kraw[KS][KLayout<D, EB>::KDW];
+      k_operand<D, EB>(kr, kraw, lane);
+      uint32_t vb[VPL][2];
+      if constexpr (KV == Ty::FP8) {
+        pv_operands_fp8<D>(vr, live, vb);
+      } else {
+        uint32_t vw[4][D / 32];
+        v_operand<KV, QT, D>(vr, live, vw);
+        pv_operands<D>(vw, vb);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f32x4_t s = chunk_scores_raw<KV, QT, D>(kraw, [&](int k) { return s_q[wave][t][k][lane]; });
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool valid = 16 * t + n < ncol && cb + 4 * g + r < ctx;
+          z[r] = valid ? s[r] * qk_scale : -__builtin_inff();
+        }
+        softmax_pv_b<KV, QT, D>(z, vb, acc[t], m_ref[t], l_sum[t], lane);
+      }
     }
-    chunk_softmax_pv<KV, QT, D>(z, vr, live, acc, m_ref, l_sum, lane);
     if (d.f & F_LAST) finish_piece(d);
   };
 

@@ -12,6 +12,9 @@ constexpr int PA_MAX_PART_BLOCKS = 1024;
 // Largest batch the evenly split matrix-core decode takes (its per-workgroup
 // chunk prefix sums live in LDS).
 constexpr int PA_SK_MAX_SEQS = 8192;
+// Query columns of a shared-prefix slot in the prefix pass: two 16-column
+// matrix-core tiles, so a slot holds up to 32 / G sequences.
+constexpr int PA_PREFIX_COLS = 32;
 
 struct DecodeParams {
   const void* k_pool;

@@ -13,6 +13,8 @@
 #include "pa_internal.h"
 #include "pa_mfma.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace {
 
@@ -64,6 +66,14 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
   else
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, w), __builtin_bit_cast(half2_t, 0x3c003c00u),
                                   acc, false);
+}
+
+// maximum of x over lanes l and l ^ 32: with both operands equal, the
+// half swap leaves each lane its own value in one result and its partner's
+// in the other (a VALU exchange, no LDS round trip)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Position of key kk (0..15 in a 16-key block) in the staged V^T rows: bits
@@ -285,7 +295,11 @@ prefill_tiled_kernel(const PrefillParams a) {
 #pragma unroll
   for (int m = 0; m < NB; ++m) o[m] = (f32x16_t){};
 
-  auto compute = [&](int kt, int buf) __attribute__((always_inline)) {
+  // MASK: the tile may hold keys after some row's position (the causal
+  // diagonal, or past the context); tiles wholly at or before the
+  // workgroup's first position skip the mask arithmetic
+  auto compute = [&](int kt, int buf, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const char* kb = lds + buf * L::BUF;
     const char* vb = kb + L::KT;
     // scores: sb[b][v] is key 32b + 8(v/4) + 4h + v%4 of the tile, row n
@@ -306,7 +320,7 @@ prefill_tiled_kernel(const PrefillParams a) {
     }
     // causal mask: key 32b + 8(v/4) + v%4 + 4h of the tile <= pos_row (a
     // tile wholly before the wave's first position masks nothing)
-    {
+    if constexpr (MASK) {
       const int thr = kt * FKT + FKT - 1 > wmin ? pos_row - kt * FKT - 4 * h : FKT;
 #pragma unroll
       for (int b = 0; b < NSB; ++b)
@@ -319,7 +333,7 @@ prefill_tiled_kernel(const PrefillParams a) {
     for (int b = 0; b < NSB; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sb[b][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     // a row with no key here (all masked) leaves its reference alone
     const float zmax = mx <= MASKED ? -__builtin_inff() : mx * c;
     if (__any(zmax > m_ref + SM_TAU)) {
@@ -369,12 +383,12 @@ prefill_tiled_kernel(const PrefillParams a) {
   if (nkt > 1) fetch_ids(1, ids_b);
   store_tile(0);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
+  auto step = [&](int kt, auto mask_tag) __attribute__((always_inline)) {
     const bool more = kt + 1 < nkt;
     if (more) load_tile(kt + 1, ids_b);
     if (kt + 2 < nkt) fetch_ids(kt + 2, ids_a);
     // a wave with no rows, or whose rows all end before this tile, skips it
-    if (wave_live && kt * FKT <= wmax) compute(kt, kt & 1);
+    if (wave_live && kt * FKT <= wmax) compute(kt, kt & 1, mask_tag);
     if (more) store_tile((kt + 1) & 1);
     __syncthreads();
 #pragma unroll
@@ -382,7 +396,13 @@ prefill_tiled_kernel(const PrefillParams a) {
       ids_b[i][0] = ids_a[i][0];
       ids_b[i][1] = ids_a[i][1];
     }
-  }
+  };
+  // tiles 0 .. nfull - 1 end at or before the workgroup's first position
+  // (every key at or before every row's, none past the context); two loops,
+  // each with its own copy of the tile code, so the full tiles carry no mask
+  const int nfull = min(nkt, (ctx - nq + tpos0 + 1) / FKT);
+  for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
+  for (int kt = nfull; kt < nkt; ++kt) step(kt, std::true_type{});
   bad = __syncthreads_or(bad);
   if (!rvalid) return;
   const float lt = l_sum + __shfl_xor(l_sum, 32);

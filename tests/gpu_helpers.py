@@ -154,7 +154,7 @@ def max_err_stored(gpu, ref, out_dtype, tol, rows=None):
     element as the plain |gpu - ref|. (A bf16 result on [4, 8) is the
     kernel's value rounded to a spacing of 2^-5, half of which, 2^-6, is
     more than the whole bf16 bound 1e-2 leaves; on [1, 2) half an ulp is
-    2^-9, well inside it, and no allowance is made there.)"""
+    2^-8, inside tol / 2, and no allowance is made there.)"""
     if rows is not None:
         gpu, ref = gpu[rows], ref[rows]
     hu = half_ulp(gpu, out_dtype)
