@@ -84,6 +84,28 @@ def test_shared_decode_matches_oracle(combo):
     assert np.all(np.isfinite(got)) and ex <= _tol(wl)
 
 
+# Runs long enough to fill both 16-column tiles of a prefix slot and spill
+# into further slots: a slot holds 32 / G samples (32 at G = 1, 16 at G = 2),
+# so 40 samples take 32 + 8, 33 take 32 + 1; a partly filled last prompt
+# block (200 tokens), and samples whose context is all prompt.
+MANY = [(200, [int(x) for x in np.random.default_rng(5).integers(0, 50, 40)]),
+        (33, [int(x) for x in np.random.default_rng(6).integers(0, 30, 17)]),
+        (16, [0, 0, 0] + [5] * 30)]
+
+
+@pytest.mark.parametrize("pool,q,G,hkv", [("f16", "f16", 1, 2), ("bf16", "bf16", 1, 1),
+                                          ("fp8_e4m3", "bf16", 1, 2), ("bf16", "bf16", 2, 2)])
+def test_runs_filling_both_prefix_tiles(pool, q, G, hkv):
+    wl = workloads.shared_prefix(13, MANY, pool_dtype=pool, q_dtype=q, num_q_heads=hkv * G,
+                                 num_kv_heads=hkv, head_dim=128, block_size=16)
+    st = _state(wl)
+    got = _shared(st)
+    ref = st.oracle_decode()
+    err = max_err_stored(got, ref, wl.q_dtype, _tol(wl))
+    say(f"{wl.num_seqs} sequences, G {G}: error beyond output rounding {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= _tol(wl)
+
+
 def test_empty_and_invalid_rows_inside_runs_and_plan_reuse():
     groups = [(48, [4, 0, 9, 2]), (33, [1, 1, 1])]
     wl = workloads.shared_prefix(12, groups, pool_dtype="bf16", q_dtype="bf16", num_q_heads=8,
