@@ -93,6 +93,10 @@ def parse():
     ap.add_argument("--shared", action="store_true",
                     help="decode with pa_decode_shared (prefixes shared by runs of consecutive "
                          "sequences read once per group; sharing planned every step)")
+    ap.add_argument("--reuse-plan", action="store_true",
+                    help="with --shared: plan the sharing once, then time calls that reuse the "
+                         "plan (the later layers of a decode step, whose tables and lengths are "
+                         "those of the first)")
     ap.add_argument("--swap-sweep", action="store_true",
                     help="swap moves of a 1,500-token FP8 victim for block sizes 8..128, one "
                          "layer and 64 layers, block-major and layer-major pools; then the "
@@ -823,6 +827,9 @@ def main():
               "(the library has no multi-GPU path; each GPU would decode its own share)",
               file=sys.stderr)
         sys.exit(2)
+    if args.reuse_plan and not args.shared:
+        print("--reuse-plan applies to --shared only", file=sys.stderr)
+        sys.exit(2)
     import torch
     import paged_kv_cache_44_amd as pa
     import workloads
@@ -875,10 +882,13 @@ def main():
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; partition {part} tokens",
           file=sys.stderr, flush=True)
 
+    planned = [False]
+
     def attend():
-        if args.shared:     # planning, prefix pass, suffix pass and merges: all timed
+        if args.shared:     # planning (unless reused), prefix pass, suffix pass and merges
             pa.decode_shared(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out=out,
-                             workspace=ws)
+                             workspace=ws, reuse_plan=args.reuse_plan and planned[0])
+            planned[0] = True
         else:
             pa.decode_attend(cache, wl.layer, q, tables, ctx, max_ctx, wl.scale, out, ws)
 
@@ -930,7 +940,8 @@ def main():
     if args.shared:
         # the whole shared decode (planning, both passes, merges) against the
         # bytes it must read at the least
-        kname = "decode_shared (plan, prefix and suffix passes, merges)"
+        kname = ("decode_shared (prefix and suffix passes, merges; plan reused)" if args.reuse_plan
+                 else "decode_shared (plan, prefix and suffix passes, merges)")
         traffic = None
     achieved = ab / (attend_ms * 1e-3) / 1e9
     rec = {
@@ -953,6 +964,8 @@ def main():
             "context_mean": round(float(wl.context_lens.mean()), 1),
             "context_max": max_ctx, "context_tokens": int(wl.context_lens.sum()),
             "partition_tokens": part, "parallelism": "single GPU",
+            **({"decode": "pa_decode_shared" + (", sharing plan reused" if args.reuse_plan else "")}
+               if args.shared else {}),
         },
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_per_s": round(S / (ms_per_step * 1e-3), 1),

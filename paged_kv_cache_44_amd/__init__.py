@@ -250,7 +250,7 @@ def decode_shared(cache: KVCache, layer: int, q: torch.Tensor, block_tables: tor
                   reuse_plan: bool = False, stream=None) -> torch.Tensor:
     """pa_decode_shared: the result of :func:`decode`, reading the prefix that
     runs of consecutive sequences share (same leading blocks in their tables)
-    once per group of up to 16 / G of them. ``reuse_plan`` keeps the sharing
+    once per group of up to 32 / G of them. ``reuse_plan`` keeps the sharing
     found by the previous call with this workspace (same tables and lengths)."""
     _need(cache.is_device, "decode needs a device pool")
     _need(q.dim() == 3 and q.shape[2] == cache.head_dim, "q must be [S][H_q][head_dim]")
