@@ -273,11 +273,12 @@ pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void
 /* the common prefix of all its members (rounded down to a multiple of 16   */
 /* tokens and capped by every member's context). Up to 32 / g members at a   */
 /* time attend to that prefix together, their queries side by side in two   */
-/* matrix-core tiles, so each prefix block is read once per group; each     */
-/* member then attends to the rest of its context, starting from the        */
-/* prefix's partial result. Put the samples of one prompt next to each      */
-/* other in the batch; sequences that share nothing cost one extra pass     */
-/* over the batch's descriptors.                                             */
+/* matrix-core tiles, so each prefix block is read once per group, while,   */
+/* in the same launch on the other workgroups, each member attends to the   */
+/* rest of its context; a final combine joins the two partial results.     */
+/* Put the samples of one prompt next to each other in the batch. A batch   */
+/* with no sharing gets the right result but runs slower than pa_decode     */
+/* (a quarter of the workgroups are set aside for prefixes and find none).  */
 /*                                                                           */
 /*  reuse_plan   0: find the sharing from block_tables / context_lens and    */
 /*               store it in the workspace (two small launches). 1: use the  */

@@ -274,7 +274,7 @@ DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* 
 struct SharedLayout {
   WsLayout suf, pre;
   size_t pre_base, lcp, start, desc, seg, pm, pl, po, total;
-  int blocks_pre, blocks_suf, g;
+  int blocks, g;                 // resident workgroups of the launch holding both passes
 };
 
 pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_dtype q_dtype,
@@ -289,14 +289,14 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
   if (!pa::mfma_supported((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs) || g > 8)
     return PA_ERR_UNSUPPORTED;
   L->g = g;
-  L->blocks_pre = pa::sk_blocks_shared((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs, 1);
-  L->blocks_suf = pa::sk_blocks_shared((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs, 2);
+  L->blocks = pa::sk_blocks_shared_dual((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
+  if (L->blocks <= 0) return PA_ERR_UNSUPPORTED;
   const int H = c->num_kv_heads;
-  L->suf = ws_layout(pa::sk_slots(L->blocks_suf, num_seqs, H) * g, c->head_dim,
-                     (size_t)L->blocks_suf * 4);
+  // each pass runs on at most all of the launch's workgroups
+  L->suf = ws_layout(pa::sk_slots(L->blocks, num_seqs, H) * g, c->head_dim, (size_t)L->blocks * 4);
   L->pre_base = L->suf.total;
-  L->pre = ws_layout(pa::sk_slots(L->blocks_pre, num_seqs, H) * pa::PA_PREFIX_COLS, c->head_dim,
-                     (size_t)L->blocks_pre * 4);
+  L->pre = ws_layout(pa::sk_slots(L->blocks, num_seqs, H) * pa::PA_PREFIX_COLS, c->head_dim,
+                     (size_t)L->blocks * 4);
   const size_t S = (size_t)num_seqs;
   L->lcp = L->pre_base + L->pre.total;
   L->start = L->lcp + align256(S * 4);
@@ -657,41 +657,46 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   a.pre_m = reinterpret_cast<float*>(w + L.pm);
   a.pre_l = reinterpret_cast<float*>(w + L.pl);
   a.pre_o = reinterpret_cast<float*>(w + L.po);
-  // The prefix pass runs on at most half the resident workgroups: a prefix
-  // chunk serves up to 32 query columns (two matrix tiles), twice a plain
-  // decode chunk's arithmetic, and fewer, longer team ranges halve the
-  // pieces the combine reads (32 prompts x 8 samples, fp16: prefix pass plus
-  // combine 41 us on half the grid, 49 us on all of it, 53 us on a quarter).
-  // A batch has at most num_seqs / 2 prefix slots, which caps small batches
-  // as in the plain decode.
+  // One launch runs both passes side by side: workgroups 0 .. pre_blocks - 1
+  // the prefix pass, the rest the suffix pass, which does not wait for the
+  // prefix (it leaves a prefixed sequence's result as a partial that the
+  // combine completes). The split is fixed (the sizes of the two passes are
+  // known only on the device): a quarter of the workgroups for the prefix
+  // pass, whose slots read each prompt once for up to 32 / G samples while
+  // the samples' own tokens grow every step. On 32 prompts x 8 samples
+  // (1,024 prompt tokens, 64-256 own, fp16) the step took 88-90 us with a
+  // quarter, 89-90 us with 5/16 or 3/8 and 92-95 us with half. A batch has
+  // at most num_seqs / 2 prefix slots, and both parts are capped for small
+  // batches as in the plain decode.
+  const int H = cache->num_kv_heads;
   const int pre_blocks =
-      std::min(pa::sk_launch_blocks(L.blocks_pre, std::max(1, num_seqs / 2), max_context_len,
-                                    cache->num_kv_heads),
-               std::max(8, L.blocks_pre / 2 / 8 * 8));
+      std::min(pa::sk_launch_blocks(L.blocks, std::max(1, num_seqs / 2), max_context_len, H),
+               std::max(8, L.blocks / 4 / 8 * 8));
+  const int suf_blocks =
+      pa::sk_launch_blocks(std::max(8, L.blocks - pre_blocks), num_seqs, max_context_len, H);
   a.pre_teams = pre_blocks * 4 / a.team;
   const int kv = (int)cache->dtype, qt = (int)q_dtype;
   if (!reuse_plan && pa::launch_share_plan(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
-  // prefix pass: pieces into its own region
+  // the prefix pass's pieces and the suffix pass's, each in its own region
   char* wp = w + L.pre_base;
-  a.ws_o = reinterpret_cast<float*>(wp + L.pre.o);
-  a.ws_m = reinterpret_cast<float*>(wp + L.pre.m);
-  a.ws_l = reinterpret_cast<float*>(wp + L.pre.l);
-  a.ws_team = reinterpret_cast<int32_t*>(wp + L.pre.team);
-  if (pa::launch_attend_shared(a, kv, qt, L.g, pre_blocks, 1, stream) != hipSuccess)
+  DecodeParams pre = a, suf = a;
+  pre.ws_o = reinterpret_cast<float*>(wp + L.pre.o);
+  pre.ws_m = reinterpret_cast<float*>(wp + L.pre.m);
+  pre.ws_l = reinterpret_cast<float*>(wp + L.pre.l);
+  pre.ws_team = reinterpret_cast<int32_t*>(wp + L.pre.team);
+  suf.ws_o = reinterpret_cast<float*>(w + L.suf.o);
+  suf.ws_m = reinterpret_cast<float*>(w + L.suf.m);
+  suf.ws_l = reinterpret_cast<float*>(w + L.suf.l);
+  suf.ws_team = reinterpret_cast<int32_t*>(w + L.suf.team);
+  if (pa::launch_attend_shared_dual(pre, suf, kv, qt, L.g, pre_blocks, pre_blocks + suf_blocks,
+                                    stream) != hipSuccess ||
+      pa::launch_merge_shared(suf, qt, L.g, suf_blocks, 2, stream) != hipSuccess)
     return PA_ERR_HIP;
-  // the prefix pieces, combined per sequence and head
-  a.pre_ws_o = a.ws_o;
-  a.pre_ws_m = a.ws_m;
-  a.pre_ws_l = a.ws_l;
-  if (pa::launch_prefix_combine(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
-  // suffix pass: continues from the combined partials, merges its own pieces
-  a.ws_o = reinterpret_cast<float*>(w + L.suf.o);
-  a.ws_m = reinterpret_cast<float*>(w + L.suf.m);
-  a.ws_l = reinterpret_cast<float*>(w + L.suf.l);
-  a.ws_team = reinterpret_cast<int32_t*>(w + L.suf.team);
-  if (pa::launch_attend_shared(a, kv, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess ||
-      pa::launch_merge_shared(a, qt, L.g, L.blocks_suf, 2, stream) != hipSuccess)
-    return PA_ERR_HIP;
+  // each prefixed sequence: its own partial and its prefix pieces, combined
+  a.pre_ws_o = pre.ws_o;
+  a.pre_ws_m = pre.ws_m;
+  a.pre_ws_l = pre.ws_l;
+  if (pa::launch_prefix_combine(a, qt, L.g, stream) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }
 

@@ -18,8 +18,9 @@
 //     after it (share_start), and each group of up to 32/G consecutive
 //     members is one prefix slot, kept at its first member's index; every
 //     member records its slot (share_desc).
-// Then the matrix-core kernel's prefix pass, prefix_combine_kernel, and the
-// suffix pass (pa_decode_sk.h).
+// Then one launch of the matrix-core kernel runs the prefix pass and the
+// suffix pass side by side (pa_decode_sk.h), the suffix pass's merge
+// follows, and prefix_combine_kernel completes each prefixed sequence.
 #include "pa_decode_sk.h"
 
 namespace pa {
@@ -168,11 +169,13 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
   }
 }
 
-// Each sequence's prefix pieces, combined into one partial (M, L, O) per
-// query head for the suffix pass: one wave per (sequence, KV head), 64 / G
-// lanes per head, every piece's loads of a batch of eight in flight before
-// they are combined (M = max m_p, L = sum 2^(m_p - M) l_p, O likewise).
-template <int G, int D>
+// The result of each sequence that has a shared prefix: the partial of its
+// own tokens (left by the suffix pass or its merge) combined with the prefix
+// pass's pieces of its columns, normalised and stored. One wave per
+// (sequence, KV head), 64 / G lanes per head, every piece's loads of a batch
+// of eight in flight before they are combined (M = max m_p,
+// L = sum 2^(m_p - M) l_p, O likewise).
+template <Ty QT, int G, int D>
 __global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams a) {
   constexpr int LPH = 64 / G;                    // lanes per head
   constexpr int DPL = D / LPH;                   // dims per lane
@@ -182,14 +185,15 @@ __global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams 
   const int H = a.num_kv_heads, T = a.team, HG = H / T;
   if (w >= (int64_t)a.num_seqs * H) return;
   const int s = (int)(w / H), kvh = (int)(w - (int64_t)s * H);
-  if (a.share_start[s] <= 0) return;
+  if (own_start(a, s, a.context_lens[s]) <= 0) return;   // written by the suffix pass
   const int hh = lane / LPH, d0 = (lane % LPH) * DPL;
   const int64_t pr = (int64_t)s * a.num_q_heads + (int64_t)kvh * G + hh;
   int64_t cs = 0, ccp = 0;
   int col0 = 0, t0 = 0, t1 = -1;
-  float M = -__builtin_inff(), L = 0.f, O[DPL];
+  // start from the partial of the sequence's own tokens
+  float M = a.pre_m[pr], L = a.pre_l[pr], O[DPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
+  for (int i = 0; i < DPL; ++i) O[i] = a.pre_o[pr * D + d0 + i];
   if (!prefix_segment(a, s, kvh / T, HG, PA_PREFIX_COLS / G, G, cs, col0, t0, t1, ccp)) L = __builtin_nanf("");
   for (int tb = t0; tb <= t1; tb += NB) {
     float mv[NB], lv[NB], ov[NB][DPL];
@@ -223,18 +227,15 @@ __global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams 
       M = mn;
     }
   }
-  float* o = a.pre_o + pr * D + d0;
+  const float norm = a.v_scale / L;
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) o[i] = O[i];
-  if (lane % LPH == 0) {
-    a.pre_m[pr] = M;
-    a.pre_l[pr] = L;
-  }
+  for (int i = 0; i < DPL; ++i) store_out<QT>(a.out, pr * D + d0 + i, O[i] * norm);
 }
 
 }  // namespace
 
-hipError_t launch_prefix_combine(const DecodeParams& a, int g, hipStream_t st) {
+template <Ty QT>
+static hipError_t launch_prefix_combine_q(const DecodeParams& a, int g, hipStream_t st) {
   const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
   const dim3 grid((unsigned)((waves + 3) / 4));
   auto go = [&](auto kernel) {
@@ -243,19 +244,25 @@ hipError_t launch_prefix_combine(const DecodeParams& a, int g, hipStream_t st) {
   };
   if (a.head_dim == 128) {
     switch (g) {
-      case 1: return go(prefix_combine_kernel<1, 128>);
-      case 2: return go(prefix_combine_kernel<2, 128>);
-      case 4: return go(prefix_combine_kernel<4, 128>);
-      case 8: return go(prefix_combine_kernel<8, 128>);
+      case 1: return go(prefix_combine_kernel<QT, 1, 128>);
+      case 2: return go(prefix_combine_kernel<QT, 2, 128>);
+      case 4: return go(prefix_combine_kernel<QT, 4, 128>);
+      case 8: return go(prefix_combine_kernel<QT, 8, 128>);
     }
   } else if (a.head_dim == 64) {
     switch (g) {
-      case 1: return go(prefix_combine_kernel<1, 64>);
-      case 2: return go(prefix_combine_kernel<2, 64>);
-      case 4: return go(prefix_combine_kernel<4, 64>);
-      case 8: return go(prefix_combine_kernel<8, 64>);
+      case 1: return go(prefix_combine_kernel<QT, 1, 64>);
+      case 2: return go(prefix_combine_kernel<QT, 2, 64>);
+      case 4: return go(prefix_combine_kernel<QT, 4, 64>);
+      case 8: return go(prefix_combine_kernel<QT, 8, 64>);
     }
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st) {
+  if ((Ty)q_ty == Ty::BF16) return launch_prefix_combine_q<Ty::BF16>(a, g, st);
+  if ((Ty)q_ty == Ty::F16) return launch_prefix_combine_q<Ty::F16>(a, g, st);
   return hipErrorInvalidValue;
 }
 
@@ -273,20 +280,72 @@ hipError_t launch_share_plan(const DecodeParams& a, int g, hipStream_t st) {
   return hipGetLastError();
 }
 
-int sk_blocks_shared(int kv_ty, int q_ty, int head_dim, int g, int num_seqs, int mode) {
-  return mode == M_PREFIX ? sk_blocks_mode<M_PREFIX>(kv_ty, q_ty, head_dim, g, num_seqs)
-                          : sk_blocks_mode<M_SUFFIX>(kv_ty, q_ty, head_dim, g, num_seqs);
+namespace {
+
+// The shared-prefix decode's launch of both passes (attend_sk_dual_kernel):
+// f(pool type, query type, head dim, group) for the runtime values, as
+// integral constants; -1 for a combination it does not take.
+template <Ty V> using TyC = std::integral_constant<Ty, V>;
+template <int V> using IntC = std::integral_constant<int, V>;
+template <typename F>
+static int sk_dual_dispatch(int kv_ty, int q_ty, int head_dim, int g, F&& f) {
+  auto by_g = [&](auto kv, auto q, auto d) -> int {
+    switch (g) {
+      case 1: return f(kv, q, d, IntC<1>{});
+      case 2: return f(kv, q, d, IntC<2>{});
+      case 4: return f(kv, q, d, IntC<4>{});
+      case 8: return f(kv, q, d, IntC<8>{});
+      default: return -1;
+    }
+  };
+  auto by_d = [&](auto kv, auto q) -> int {
+    if (head_dim == 64) return by_g(kv, q, IntC<64>{});
+    if (head_dim == 128) return by_g(kv, q, IntC<128>{});
+    return -1;
+  };
+  const Ty kv = (Ty)kv_ty, q = (Ty)q_ty;
+  if (kv == Ty::BF16 && q == Ty::BF16) return by_d(TyC<Ty::BF16>{}, TyC<Ty::BF16>{});
+  if (kv == Ty::F16 && q == Ty::F16) return by_d(TyC<Ty::F16>{}, TyC<Ty::F16>{});
+  if (kv == Ty::FP8 && q == Ty::BF16) return by_d(TyC<Ty::FP8>{}, TyC<Ty::BF16>{});
+  if (kv == Ty::FP8 && q == Ty::F16) return by_d(TyC<Ty::FP8>{}, TyC<Ty::F16>{});
+  return -1;
 }
 
-hipError_t launch_attend_shared(const DecodeParams& a, int kv_ty, int q_ty, int g, int blocks,
-                                int mode, hipStream_t st) {
-  return mode == M_PREFIX ? sk_launch_attend<M_PREFIX>(a, kv_ty, q_ty, g, blocks, st)
-                          : sk_launch_attend<M_SUFFIX>(a, kv_ty, q_ty, g, blocks, st);
+static int sk_blocks_dual(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {
+  return sk_dual_dispatch(kv_ty, q_ty, head_dim, g, [&](auto kv, auto q, auto d, auto gg) -> int {
+    constexpr Ty KV = decltype(kv)::value, QT = decltype(q)::value;
+    constexpr int D = decltype(d)::value, G = decltype(gg)::value;
+    return sk_resident_blocks(reinterpret_cast<const void*>(&attend_sk_dual_kernel<KV, QT, D, G>),
+                              sk_lds_bytes(num_seqs, M_PREFIX), sk_waves_per_simd<KV, D, G, M_PREFIX>());
+  });
+}
+
+static hipError_t sk_launch_dual(const DecodeParams& p, const DecodeParams& q, int kv_ty, int q_ty,
+                                 int g, int pre_blocks, int blocks, hipStream_t st) {
+  const int r = sk_dual_dispatch(kv_ty, q_ty, p.head_dim, g, [&](auto kv, auto qt, auto d, auto gg) -> int {
+    constexpr Ty KV = decltype(kv)::value, QT = decltype(qt)::value;
+    constexpr int D = decltype(d)::value, G = decltype(gg)::value;
+    hipLaunchKernelGGL((attend_sk_dual_kernel<KV, QT, D, G>), dim3(blocks), dim3(NWM * 64),
+                       sk_lds_bytes(p.num_seqs, M_PREFIX), st, p, q, pre_blocks);
+    return (int)hipGetLastError();
+  });
+  return r < 0 ? hipErrorInvalidValue : (hipError_t)r;
+}
+
+}  // namespace
+
+int sk_blocks_shared_dual(int kv_ty, int q_ty, int head_dim, int g, int num_seqs) {
+  return sk_blocks_dual(kv_ty, q_ty, head_dim, g, num_seqs);
+}
+
+hipError_t launch_attend_shared_dual(const DecodeParams& pre, const DecodeParams& suf, int kv_ty,
+                                     int q_ty, int g, int pre_blocks, int blocks, hipStream_t st) {
+  return sk_launch_dual(pre, suf, kv_ty, q_ty, g, pre_blocks, blocks, st);
 }
 
 hipError_t launch_merge_shared(const DecodeParams& a, int q_ty, int g, int blocks, int mode,
                                hipStream_t st) {
-  if (mode != M_SUFFIX) return hipErrorInvalidValue;   // prefix pieces merge in the suffix pass
+  if (mode != M_SUFFIX) return hipErrorInvalidValue;   // prefix pieces go to the combine
   return sk_launch_merge<M_SUFFIX>(a, q_ty, g, blocks, st);
 }
 

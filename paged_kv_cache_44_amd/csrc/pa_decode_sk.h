@@ -51,7 +51,8 @@
 // the prompt's blocks; "Continuous Batching and PagedAttention", section
 // "Sharing, the part that goes beyond fixing what broke") are read once per
 // up to 32/G sequences instead of once per sequence, in two passes of the
-// same kernel:
+// same kernel body that run side by side in one launch
+// (attend_sk_dual_kernel):
 //  * M_PREFIX: a segment is a slot of up to 32/G consecutive sequences
 //    whose tables share the prefix blocks; their queries fill the 32
 //    columns of two tiles side by side (column c: sequence first + c/G,
@@ -59,11 +60,13 @@
 //    them (its operands built once, both tiles' products from them). Every
 //    piece is left as a partial (m, l, o) per column, and the team range of
 //    each prefix segment is recorded.
-//  * prefix_combine_kernel (pa_decode_shared.hip) combines each sequence's
-//    prefix pieces into one partial per head.
-//  * M_SUFFIX: each sequence's segment starts after its shared prefix, and
-//    the piece holding its first chunk continues from the prefix's partial,
-//    so the usual finish / merge produce the full result.
+//  * M_SUFFIX: each sequence's segment starts after its shared prefix (the
+//    whole context when it has none). A sequence without a prefix is
+//    finished as in the plain decode; one with a prefix leaves the partial
+//    of its own tokens (pre_m, pre_l, pre_o: written here for a whole
+//    segment or an empty one, by the merge for a cut one).
+//  * prefix_combine_kernel (pa_decode_shared.hip) combines that partial
+//    with the sequence's prefix pieces and stores the result.
 #pragma once
 
 #include <type_traits>
@@ -86,6 +89,15 @@ __device__ __forceinline__ int seq_chunks(const DecodeParams& a, int ctx) {
   const int64_t nb = ((int64_t)ctx + a.block_size - 1) >> a.log2_block_size;
   if (nb > a.max_blocks_per_seq) return 0;
   return (ctx + CH - 1) / CH;
+}
+
+// Tokens of sequence s covered by a shared prefix: the plan's start when it
+// is a multiple of 16 inside a valid context, else 0 (no prefix). Every
+// kernel of the shared-prefix decode decides "has a prefix" by this.
+__device__ __forceinline__ int own_start(const DecodeParams& a, int s, int ctx) {
+  if (seq_chunks(a, ctx) == 0) return 0;
+  const int st0 = a.share_start[s];
+  return (st0 < 0 || st0 > ctx || (st0 & (CH - 1))) ? 0 : st0;
 }
 
 // The prefix-pass segment holding sequence s's prefix for head group hg:
@@ -145,10 +157,15 @@ constexpr int sk_waves_per_simd() {
   return MODE == M_PREFIX ? 2 : ((KV == Ty::FP8 || D == 64) ? 3 : 2);
 }
 
-template <Ty KV, Ty QT, int D, int G, int MODE>
-__global__ void __launch_bounds__(NWM * 64)
-__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G, MODE>())))
-attend_sk_kernel(const DecodeParams a) {
+// The kernel body: a launch of its own (attend_sk_kernel: the workgroup
+// index and count are the grid's), or one part of a launch that runs two
+// modes side by side (attend_sk_dual_kernel, PART: workgroup part_blk of the
+// part's part_nblk).
+template <Ty KV, Ty QT, int D, int G, int MODE, bool PART>
+__device__ __forceinline__ void attend_sk_body(const DecodeParams& a, const int part_blk,
+                                               const int part_nblk) {
+  auto blk = [&]() __attribute__((always_inline)) { return PART ? part_blk : (int)blockIdx.x; };
+  auto nblk = [&]() __attribute__((always_inline)) { return PART ? part_nblk : (int)gridDim.x; };
   static_assert(QT == Ty::BF16 || QT == Ty::F16, "16-bit queries");
   static_assert(G >= 1 && G <= 16, "group fits the 16-column tile");
   static_assert(MODE == M_PLAIN || MODE == M_PREFIX || MODE == M_SUFFIX, "mode");
@@ -207,8 +224,7 @@ attend_sk_kernel(const DecodeParams a) {
           const bool ok = seq_chunks(a, ctx) > 0;
           int st0 = 0;                              // tokens already covered by a prefix
           if constexpr (MODE == M_SUFFIX) {
-            st0 = ok ? a.share_start[s] : 0;
-            if (st0 < 0 || st0 > ctx || (st0 & (CH - 1))) st0 = 0;
+            st0 = own_start(a, s, ctx);
             s_aux[s] = (uint32_t)(st0 / CH);
           }
           v = ok ? (ctx - st0 + CH - 1) / CH : 0;
@@ -238,17 +254,18 @@ attend_sk_kernel(const DecodeParams a) {
   }
   // rows of sequences with nothing to attend to: zeros for an empty context,
   // NaN for an invalid one (negative, beyond max_context_len or the table);
-  // in M_SUFFIX a context that is all shared prefix takes the prefix's
-  // partial, normalised
+  // in M_SUFFIX a context that is all shared prefix gets an empty partial of
+  // its own tokens, to which prefix_combine_kernel adds the prefix
   if constexpr (MODE != M_PREFIX) {
-    for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    for (int s = blk(); s < S; s += nblk()) {
       if (s_cum[s + 1] == s_cum[s]) {
         const int64_t base = (int64_t)s * a.num_q_heads * D;
         if (MODE == M_SUFFIX && s_aux[s] > 0) {
-          // the whole context is shared prefix: its partial, normalised
-          for (int e = tid; e < a.num_q_heads * D; e += NWM * 64)
-            store_out<QT>(a.out, base + e,
-                          a.pre_o[base + e] * (a.v_scale / a.pre_l[(int64_t)s * a.num_q_heads + e / D]));
+          for (int e = tid; e < a.num_q_heads * D; e += NWM * 64) a.pre_o[base + e] = 0.f;
+          for (int e = tid; e < a.num_q_heads; e += NWM * 64) {
+            a.pre_m[(int64_t)s * a.num_q_heads + e] = -__builtin_inff();
+            a.pre_l[(int64_t)s * a.num_q_heads + e] = 0.f;
+          }
         } else {
           const float fill = a.context_lens[s] == 0 ? 0.f : __builtin_nanf("");
           for (int e = tid; e < a.num_q_heads * D; e += NWM * 64) store_out<QT>(a.out, base + e, fill);
@@ -261,12 +278,13 @@ attend_sk_kernel(const DecodeParams a) {
   // (Cc == 0: every team's range is empty; each still records "nothing to
   // merge" below, so the merge never reads a stale descriptor)
   // XCD-contiguous wave numbering: workgroup b runs on XCD b % 8; give each
-  // XCD one contiguous stretch of the column stream (gridDim.x is a multiple
-  // of 8, and T divides the 8 waves of a workgroup pair)
-  const int per_xcd = gridDim.x / NXCD;
-  const int vb = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  // XCD one contiguous stretch of the column stream (nblk, and the first
+  // workgroup of this part of the launch, are multiples of 8, and T divides
+  // the 8 waves of a workgroup pair)
+  const int per_xcd = nblk() / NXCD;
+  const int vb = (blk() % NXCD) * per_xcd + blk() / NXCD;
   const int64_t w = (int64_t)vb * NWM + wave;
-  const int64_t Wt = (int64_t)gridDim.x * NWM / T;              // teams
+  const int64_t Wt = (int64_t)nblk() * NWM / T;                 // teams
   const int64_t team = w / T;
   const int ti = (int)(w - team * T);                           // KV head within the group
 
@@ -518,7 +536,18 @@ attend_sk_kernel(const DecodeParams a) {
         const float lh = __shfl(lt, h);
         const float mh = __shfl(m_ref[t], h);
         if (col < ncol) {
-          if (whole && MODE != M_PREFIX) {
+          if (MODE == M_SUFFIX && whole && d.x > 0) {
+            // a sequence with a shared prefix: the partial of its own
+            // tokens, to which prefix_combine_kernel adds the prefix
+            const int64_t prow = (int64_t)d.seq * a.num_q_heads + (int64_t)kvh * G + col;
+            float* po = a.pre_o + prow * D + VPL * n;
+#pragma unroll
+            for (int m = 0; m < VPL; ++m) po[m] = bad ? __builtin_nanf("") : acc[t][m][r];
+            if (n == 0) {
+              a.pre_m[prow] = bad ? 0.f : mh;
+              a.pre_l[prow] = bad ? __builtin_nanf("") : lh;
+            }
+          } else if (whole && MODE != M_PREFIX) {
             const float norm = bad ? __builtin_nanf("") : a.v_scale / lh;
             const int64_t o = out_row0 + (int64_t)col * D + VPL * n;
 #pragma unroll
@@ -545,24 +574,6 @@ attend_sk_kernel(const DecodeParams a) {
   auto process_chunk = [&](const uint32_t (&kr)[KR][KW], const uint32_t (&vr)[4][VDW],
                            const Desc& d) __attribute__((always_inline)) {
     if (d.f & F_FIRST) pj0 = d.j;
-    if constexpr (MODE == M_SUFFIX) {
-      if ((d.f & F_FIRST) && d.x > 0 && d.j == d.x) {
-        // the piece opening the sequence's own tokens continues from the
-        // shared prefix's partial (state layout of softmax_pv: column n =
-        // head n's max and sum, accumulator rows 4g + r = heads)
-        const int64_t r0 = (int64_t)d.seq * a.num_q_heads + (int64_t)(d.hg * T + ti) * G;
-        m_ref[0] = n < G ? a.pre_m[r0 + n] : -__builtin_inff();
-        l_sum[0] = (n < G && g == 0) ? a.pre_l[r0 + n] : 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (4 * g + r < G) {
-            const float* po = a.pre_o + (r0 + 4 * g + r) * D + VPL * n;
-#pragma unroll
-            for (int m = 0; m < VPL; ++m) acc[0][m][r] = po[m];
-          }
-        }
-      }
-    }
     const int ctx = d.ctx;
     const int cb = d.j * CH;
     const bool tail = cb + CH > ctx;
@@ -644,6 +655,28 @@ attend_sk_kernel(const DecodeParams a) {
   }
 }
 
+template <Ty KV, Ty QT, int D, int G, int MODE>
+__global__ void __launch_bounds__(NWM * 64)
+__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G, MODE>())))
+attend_sk_kernel(const DecodeParams a) {
+  attend_sk_body<KV, QT, D, G, MODE, false>(a, 0, 0);
+}
+
+// The shared-prefix decode's two passes in one launch: workgroups
+// 0 .. pre_blocks - 1 run the prefix pass (parameters p), the others the
+// suffix pass (parameters q), at the same time. Neither reads what the other
+// writes: the suffix pass leaves the result of a sequence that has a prefix
+// as a partial, and prefix_combine_kernel adds the prefix afterwards.
+template <Ty KV, Ty QT, int D, int G>
+__global__ void __launch_bounds__(NWM * 64)
+__attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G, M_PREFIX>())))
+attend_sk_dual_kernel(const DecodeParams p, const DecodeParams q, int pre_blocks) {
+  if ((int)blockIdx.x < pre_blocks)
+    attend_sk_body<KV, QT, D, G, M_PREFIX, true>(p, blockIdx.x, pre_blocks);
+  else
+    attend_sk_body<KV, QT, D, G, M_SUFFIX, true>(q, blockIdx.x - pre_blocks, gridDim.x - pre_blocks);
+}
+
 // Merge of segments cut by team range boundaries: M = max_p m_p,
 // out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p. Workgroup (t, i)
 // merges KV head i of the group of the segment recorded by team t (if any),
@@ -655,12 +688,12 @@ attend_sk_kernel(const DecodeParams a) {
 // pieces, as in batches of many sequences.
 // SPLITH: one query head per workgroup (grid z), so a few long segments
 // spread over G times the workgroups, each with G times the piece groups.
-// (The prefix pass of the shared-prefix decode has no merge: the suffix pass
-// combines its pieces.)
+// (The prefix pass of the shared-prefix decode has no merge of its own:
+// prefix_combine_kernel combines its pieces with each sequence's partial.)
 template <Ty QT, int D, int G, int MODE, int NT = 256, bool BYSEG = false, bool SPLITH = false>
 __global__ void __launch_bounds__(NT)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
-  static_assert(MODE != M_PREFIX, "prefix pieces are combined by the suffix pass");
+  static_assert(MODE != M_PREFIX, "prefix pieces are combined by prefix_combine_kernel");
   static_assert(!SPLITH || BYSEG, "one query head per workgroup: segment-indexed merge only");
   constexpr int GC = SPLITH ? 1 : G;                   // query heads per workgroup
   constexpr int GD = GC * D;
@@ -808,6 +841,20 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
     for (int q = 0; q < PG; ++q)
       combine(s_m[q][hl], s_l[q][hl], reinterpret_cast<const float4*>(&s_o[q][hl * D + d0]));
   }
+  if constexpr (MODE == M_SUFFIX) {
+    if (own_start(a, seq, a.context_lens[seq]) > 0) {
+      // a sequence with a shared prefix: the partial of its own tokens, to
+      // which prefix_combine_kernel adds the prefix
+      const int64_t prow = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) a.pre_o[orow + e] = O[e];
+      if (d0 == 0) {
+        a.pre_m[prow] = M;
+        a.pre_l[prow] = L;
+      }
+      return;
+    }
+  }
   const float norm = a.v_scale / L;
 #pragma unroll
   for (int e = 0; e < DPT; ++e) store_out<QT>(a.out, orow + e, O[e] * norm);
@@ -857,26 +904,27 @@ static hipError_t sk_launch_attend(const DecodeParams& a, int kv_ty, int q_ty, i
 
 // Workgroups to launch: exactly the number that are resident at once (every
 // wave's range is processed concurrently), a multiple of the XCD count.
-template <Ty KV, Ty QT, int D, int G, int MODE>
-static int sk_blocks_t(int num_seqs) {
+// More resident workgroups than the compiled target adds no bandwidth (the
+// slab reads already keep the memory system full at that occupancy) and only
+// shortens each wave's range, raising the merge's share of the work.
+static int sk_resident_blocks(const void* kernel, size_t lds, int target) {
   int dev = 0, cus = 256, per_cu = 0;
-  const size_t lds = sk_lds_bytes(num_seqs, MODE);
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&attend_sk_kernel<KV, QT, D, G, MODE>), NWM * 64,
-            lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NWM * 64, lds) != hipSuccess)
       per_cu = 0;
   }
-  // More resident workgroups than the compiled target adds no bandwidth (the
-  // slab reads already keep the memory system full at that occupancy) and
-  // only shortens each wave's range, raising the merge's share of the work.
-  const int target = sk_waves_per_simd<KV, D, G, MODE>();
   if (per_cu <= 0 || per_cu > target) per_cu = target;
   const int b = cus * per_cu;
   return b >= NXCD ? b / NXCD * NXCD : NXCD;
+}
+
+template <Ty KV, Ty QT, int D, int G, int MODE>
+static int sk_blocks_t(int num_seqs) {
+  return sk_resident_blocks(reinterpret_cast<const void*>(&attend_sk_kernel<KV, QT, D, G, MODE>),
+                            sk_lds_bytes(num_seqs, MODE), sk_waves_per_simd<KV, D, G, MODE>());
 }
 
 template <Ty KV, Ty QT, int D, int MODE>
