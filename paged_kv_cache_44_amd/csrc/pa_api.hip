@@ -241,7 +241,7 @@ DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* 
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t max_context_len,
                            int32_t num_seqs, int32_t num_q_heads, float scale) {
-  DecodeParams a;
+  DecodeParams a{};
   memset(&a, 0, sizeof(a));
   a.k_pool = cache->k;
   a.v_pool = cache->v;
@@ -273,7 +273,7 @@ DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* 
 // each prefix segment.
 struct SharedLayout {
   WsLayout suf, pre;
-  size_t pre_base, lcp, start, desc, seg, pm, pl, po, total;
+  size_t pre_base, lcp, start, desc, seg, sseg, pm, pl, po, total;
   int blocks, g;                 // resident workgroups of the launch holding both passes
 };
 
@@ -302,8 +302,9 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
   L->start = L->lcp + align256(S * 4);
   L->desc = L->start + align256(S * 4);
   L->seg = L->desc + align256(S * 16);
+  L->sseg = L->seg + align256(S * (size_t)H * 16);
   const size_t R = S * (size_t)num_q_heads;
-  L->pm = L->seg + align256(S * (size_t)H * 16);
+  L->pm = L->sseg + align256(S * (size_t)H * 16);
   L->pl = L->pm + align256(R * 4);
   L->po = L->pl + align256(R * 4);
   L->total = L->po + align256(R * (size_t)c->head_dim * 4);
@@ -654,6 +655,7 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   a.share_start = reinterpret_cast<int32_t*>(w + L.start);
   a.share_desc = reinterpret_cast<int32_t*>(w + L.desc);
   a.share_seg = reinterpret_cast<int32_t*>(w + L.seg);
+  a.suf_seg = reinterpret_cast<int32_t*>(w + L.sseg);
   a.pre_m = reinterpret_cast<float*>(w + L.pm);
   a.pre_l = reinterpret_cast<float*>(w + L.pl);
   a.pre_o = reinterpret_cast<float*>(w + L.po);
@@ -675,6 +677,7 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   const int suf_blocks =
       pa::sk_launch_blocks(std::max(8, L.blocks - pre_blocks), num_seqs, max_context_len, H);
   a.pre_teams = pre_blocks * 4 / a.team;
+  a.suf_teams = suf_blocks * 4 / a.team;
   const int kv = (int)cache->dtype, qt = (int)q_dtype;
   if (!reuse_plan && pa::launch_share_plan(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
   // the prefix pass's pieces and the suffix pass's, each in its own region
@@ -689,14 +692,15 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   suf.ws_l = reinterpret_cast<float*>(w + L.suf.l);
   suf.ws_team = reinterpret_cast<int32_t*>(w + L.suf.team);
   if (pa::launch_attend_shared_dual(pre, suf, kv, qt, L.g, pre_blocks, pre_blocks + suf_blocks,
-                                    stream) != hipSuccess ||
-      pa::launch_merge_shared(suf, qt, L.g, suf_blocks, 2, stream) != hipSuccess)
+                                    stream) != hipSuccess)
     return PA_ERR_HIP;
-  // each prefixed sequence: its own partial and its prefix pieces, combined
-  a.pre_ws_o = pre.ws_o;
-  a.pre_ws_m = pre.ws_m;
-  a.pre_ws_l = pre.ws_l;
-  if (pa::launch_prefix_combine(a, qt, L.g, stream) != hipSuccess) return PA_ERR_HIP;
+  // every row the suffix pass left open: its pieces (or own partial) and,
+  // with a prefix, the prefix pieces, combined
+  DecodeParams fin = suf;
+  fin.pre_ws_o = pre.ws_o;
+  fin.pre_ws_m = pre.ws_m;
+  fin.pre_ws_l = pre.ws_l;
+  if (pa::launch_shared_combine(fin, qt, L.g, stream) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }
 

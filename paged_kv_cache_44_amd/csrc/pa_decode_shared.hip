@@ -19,8 +19,8 @@
 //     members is one prefix slot, kept at its first member's index; every
 //     member records its slot (share_desc).
 // Then one launch of the matrix-core kernel runs the prefix pass and the
-// suffix pass side by side (pa_decode_sk.h), the suffix pass's merge
-// follows, and prefix_combine_kernel completes each prefixed sequence.
+// suffix pass side by side (pa_decode_sk.h), and shared_combine_kernel
+// finishes every row the suffix pass leaves open.
 #include "pa_decode_sk.h"
 
 namespace pa {
@@ -169,14 +169,16 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
   }
 }
 
-// The result of each sequence that has a shared prefix: the partial of its
-// own tokens (left by the suffix pass or its merge) combined with the prefix
-// pass's pieces of its columns, normalised and stored. One wave per
+// Every row the suffix pass does not finish: a sequence without a prefix
+// whose segment was cut across teams (its pieces, combined as the plain
+// decode's merge does), and every sequence with a prefix (the suffix pass's
+// pieces, or the partial it left for a segment inside one team, plus the
+// prefix pass's pieces of its columns), normalised and stored. One wave per
 // (sequence, KV head), 64 / G lanes per head, every piece's loads of a batch
 // of eight in flight before they are combined (M = max m_p,
 // L = sum 2^(m_p - M) l_p, O likewise).
 template <Ty QT, int G, int D>
-__global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams a) {
+__global__ void __launch_bounds__(256) shared_combine_kernel(const DecodeParams a) {
   constexpr int LPH = 64 / G;                    // lanes per head
   constexpr int DPL = D / LPH;                   // dims per lane
   constexpr int NB = 8;                          // pieces per batch
@@ -185,47 +187,87 @@ __global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams 
   const int H = a.num_kv_heads, T = a.team, HG = H / T;
   if (w >= (int64_t)a.num_seqs * H) return;
   const int s = (int)(w / H), kvh = (int)(w - (int64_t)s * H);
-  if (own_start(a, s, a.context_lens[s]) <= 0) return;   // written by the suffix pass
+  const int hg = kvh / T, ti = kvh % T;
+  const int ctx = a.context_lens[s];
+  const int st0 = own_start(a, s, ctx);
+  // the suffix segment: its chunks and the teams holding its pieces
+  const int nsuf = seq_chunks(a, ctx) > 0 ? (ctx - st0 + CH - 1) / CH : 0;
+  int t0 = 0, t1 = -1;
+  int64_t ccs = 0;
+  bool own_partial = false, bad_record = false;
+  if (nsuf > 0) {
+    const int4 sg = reinterpret_cast<const int4*>(a.suf_seg)[(int64_t)s * HG + hg];
+    if (!(sg.x >= 0 && sg.x <= sg.y && sg.y < a.suf_teams && sg.z > 0 && sg.w == a.suf_teams)) {
+      bad_record = true;
+    } else if (sg.x == sg.y) {
+      if (st0 <= 0) return;                      // finished by the suffix pass
+      own_partial = true;
+    } else {
+      t0 = sg.x;
+      t1 = sg.y;
+      ccs = sg.z;
+    }
+  } else if (st0 <= 0) {
+    return;                                      // empty or invalid row: written by the suffix pass
+  }
   const int hh = lane / LPH, d0 = (lane % LPH) * DPL;
   const int64_t pr = (int64_t)s * a.num_q_heads + (int64_t)kvh * G + hh;
-  int64_t cs = 0, ccp = 0;
-  int col0 = 0, t0 = 0, t1 = -1;
-  // start from the partial of the sequence's own tokens
-  float M = a.pre_m[pr], L = a.pre_l[pr], O[DPL];
+  float M = -__builtin_inff(), L = 0.f, O[DPL];
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) O[i] = a.pre_o[pr * D + d0 + i];
-  if (!prefix_segment(a, s, kvh / T, HG, PA_PREFIX_COLS / G, G, cs, col0, t0, t1, ccp)) L = __builtin_nanf("");
-  for (int tb = t0; tb <= t1; tb += NB) {
-    float mv[NB], lv[NB], ov[NB][DPL];
+  for (int i = 0; i < DPL; ++i) O[i] = 0.f;
+  if (own_partial) {
+    M = a.pre_m[pr];
+    L = a.pre_l[pr];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int tm = tb + u;
-      const bool ok = tm <= t1 && team_begin(tm, ccp, a.pre_teams) != team_begin(tm + 1, ccp, a.pre_teams);
-      const int64_t sl = ((tm + cs) * T + kvh % T) * PA_PREFIX_COLS + col0 + hh;
-      mv[u] = ok ? a.pre_ws_m[ok ? sl : 0] : -__builtin_inff();
-      lv[u] = ok ? a.pre_ws_l[ok ? sl : 0] : 0.f;
-      const float* po = a.pre_ws_o + (ok ? sl : 0) * D + d0;
-      if constexpr (DPL % 4 == 0) {
+    for (int i = 0; i < DPL; ++i) O[i] = a.pre_o[pr * D + d0 + i];
+  }
+  if (bad_record) L = __builtin_nanf("");
+  // the pieces of teams ta .. tb of a pass (a team with an empty range holds
+  // none) at slots ((team + cseg) * T + ti) * gc + col
+  auto combine_pieces = [&](const float* wm, const float* wl, const float* wo, int64_t cseg, int ta,
+                            int tb, int64_t cc, int teams, int gc, int col) __attribute__((always_inline)) {
+    for (int tq = ta; tq <= tb; tq += NB) {
+      float mv[NB], lv[NB], ov[NB][DPL];
 #pragma unroll
-        for (int i = 0; i < DPL; i += 4) {
-          const float4 x = ok ? *reinterpret_cast<const float4*>(po + i) : make_float4(0, 0, 0, 0);
-          ov[u][i] = x.x; ov[u][i + 1] = x.y; ov[u][i + 2] = x.z; ov[u][i + 3] = x.w;
+      for (int u = 0; u < NB; ++u) {
+        const int tm = tq + u;
+        const bool ok = tm <= tb && team_begin(tm, cc, teams) != team_begin(tm + 1, cc, teams);
+        const int64_t sl = ok ? ((tm + cseg) * T + ti) * gc + col : 0;
+        mv[u] = ok ? wm[sl] : -__builtin_inff();
+        lv[u] = ok ? wl[sl] : 0.f;
+        const float* po = wo + sl * D + d0;
+        if constexpr (DPL % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < DPL; i += 4) {
+            const float4 x = ok ? *reinterpret_cast<const float4*>(po + i) : make_float4(0, 0, 0, 0);
+            ov[u][i] = x.x; ov[u][i + 1] = x.y; ov[u][i + 2] = x.z; ov[u][i + 3] = x.w;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) ov[u][i] = ok ? po[i] : 0.f;
         }
-      } else {
+      }
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) ov[u][i] = ok ? po[i] : 0.f;
+      for (int u = 0; u < NB; ++u) {
+        const float mn = fmaxf(M, mv[u]);
+        if (mn == -__builtin_inff()) continue;
+        const float f1 = __builtin_amdgcn_exp2f(M - mn), f2 = __builtin_amdgcn_exp2f(mv[u] - mn);
+        L = L * f1 + lv[u] * f2;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) O[i] = O[i] * f1 + ov[u][i] * f2;
+        M = mn;
       }
     }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const float mn = fmaxf(M, mv[u]);
-      if (mn == -__builtin_inff()) continue;
-      const float f1 = __builtin_amdgcn_exp2f(M - mn), f2 = __builtin_amdgcn_exp2f(mv[u] - mn);
-      L = L * f1 + lv[u] * f2;
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) O[i] = O[i] * f1 + ov[u][i] * f2;
-      M = mn;
-    }
+  };
+  // the suffix pass's pieces of a cut segment
+  combine_pieces(a.ws_m, a.ws_l, a.ws_o, (int64_t)s * HG + hg, t0, t1, ccs, a.suf_teams, G, hh);
+  // the prefix pass's pieces of the sequence's columns
+  if (st0 > 0) {
+    int64_t cs = 0, ccp = 0;
+    int col0 = 0, p0 = 0, p1 = -1;
+    if (!prefix_segment(a, s, hg, HG, PA_PREFIX_COLS / G, G, cs, col0, p0, p1, ccp)) L = __builtin_nanf("");
+    combine_pieces(a.pre_ws_m, a.pre_ws_l, a.pre_ws_o, cs, p0, p1, ccp, a.pre_teams, PA_PREFIX_COLS,
+                   col0 + hh);
   }
   const float norm = a.v_scale / L;
 #pragma unroll
@@ -235,7 +277,7 @@ __global__ void __launch_bounds__(256) prefix_combine_kernel(const DecodeParams 
 }  // namespace
 
 template <Ty QT>
-static hipError_t launch_prefix_combine_q(const DecodeParams& a, int g, hipStream_t st) {
+static hipError_t launch_shared_combine_q(const DecodeParams& a, int g, hipStream_t st) {
   const int64_t waves = (int64_t)a.num_seqs * a.num_kv_heads;
   const dim3 grid((unsigned)((waves + 3) / 4));
   auto go = [&](auto kernel) {
@@ -244,25 +286,25 @@ static hipError_t launch_prefix_combine_q(const DecodeParams& a, int g, hipStrea
   };
   if (a.head_dim == 128) {
     switch (g) {
-      case 1: return go(prefix_combine_kernel<QT, 1, 128>);
-      case 2: return go(prefix_combine_kernel<QT, 2, 128>);
-      case 4: return go(prefix_combine_kernel<QT, 4, 128>);
-      case 8: return go(prefix_combine_kernel<QT, 8, 128>);
+      case 1: return go(shared_combine_kernel<QT, 1, 128>);
+      case 2: return go(shared_combine_kernel<QT, 2, 128>);
+      case 4: return go(shared_combine_kernel<QT, 4, 128>);
+      case 8: return go(shared_combine_kernel<QT, 8, 128>);
     }
   } else if (a.head_dim == 64) {
     switch (g) {
-      case 1: return go(prefix_combine_kernel<QT, 1, 64>);
-      case 2: return go(prefix_combine_kernel<QT, 2, 64>);
-      case 4: return go(prefix_combine_kernel<QT, 4, 64>);
-      case 8: return go(prefix_combine_kernel<QT, 8, 64>);
+      case 1: return go(shared_combine_kernel<QT, 1, 64>);
+      case 2: return go(shared_combine_kernel<QT, 2, 64>);
+      case 4: return go(shared_combine_kernel<QT, 4, 64>);
+      case 8: return go(shared_combine_kernel<QT, 8, 64>);
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefix_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st) {
-  if ((Ty)q_ty == Ty::BF16) return launch_prefix_combine_q<Ty::BF16>(a, g, st);
-  if ((Ty)q_ty == Ty::F16) return launch_prefix_combine_q<Ty::F16>(a, g, st);
+hipError_t launch_shared_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st) {
+  if ((Ty)q_ty == Ty::BF16) return launch_shared_combine_q<Ty::BF16>(a, g, st);
+  if ((Ty)q_ty == Ty::F16) return launch_shared_combine_q<Ty::F16>(a, g, st);
   return hipErrorInvalidValue;
 }
 
@@ -343,10 +385,5 @@ hipError_t launch_attend_shared_dual(const DecodeParams& pre, const DecodeParams
   return sk_launch_dual(pre, suf, kv_ty, q_ty, g, pre_blocks, blocks, st);
 }
 
-hipError_t launch_merge_shared(const DecodeParams& a, int q_ty, int g, int blocks, int mode,
-                               hipStream_t st) {
-  if (mode != M_SUFFIX) return hipErrorInvalidValue;   // prefix pieces go to the combine
-  return sk_launch_merge<M_SUFFIX>(a, q_ty, g, blocks, st);
-}
 
 }  // namespace pa

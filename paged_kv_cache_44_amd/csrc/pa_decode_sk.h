@@ -61,12 +61,13 @@
 //    piece is left as a partial (m, l, o) per column, and the team range of
 //    each prefix segment is recorded.
 //  * M_SUFFIX: each sequence's segment starts after its shared prefix (the
-//    whole context when it has none). A sequence without a prefix is
-//    finished as in the plain decode; one with a prefix leaves the partial
-//    of its own tokens (pre_m, pre_l, pre_o: written here for a whole
-//    segment or an empty one, by the merge for a cut one).
-//  * prefix_combine_kernel (pa_decode_shared.hip) combines that partial
-//    with the sequence's prefix pieces and stores the result.
+//    whole context when it has none). A segment inside one team's range is
+//    finished here when its sequence has no prefix, and left as a partial
+//    of the sequence's own tokens (pre_m, pre_l, pre_o) when it has one; a
+//    cut segment leaves pieces as in the plain decode. Both passes record
+//    each segment's team range.
+//  * shared_combine_kernel (pa_decode_shared.hip) finishes every other row:
+//    the suffix pieces or own partial, plus the prefix pieces.
 #pragma once
 
 #include <type_traits>
@@ -254,19 +255,13 @@ __device__ __forceinline__ void attend_sk_body(const DecodeParams& a, const int 
   }
   // rows of sequences with nothing to attend to: zeros for an empty context,
   // NaN for an invalid one (negative, beyond max_context_len or the table);
-  // in M_SUFFIX a context that is all shared prefix gets an empty partial of
-  // its own tokens, to which prefix_combine_kernel adds the prefix
+  // in M_SUFFIX a context that is all shared prefix is left to
+  // shared_combine_kernel
   if constexpr (MODE != M_PREFIX) {
     for (int s = blk(); s < S; s += nblk()) {
       if (s_cum[s + 1] == s_cum[s]) {
         const int64_t base = (int64_t)s * a.num_q_heads * D;
-        if (MODE == M_SUFFIX && s_aux[s] > 0) {
-          for (int e = tid; e < a.num_q_heads * D; e += NWM * 64) a.pre_o[base + e] = 0.f;
-          for (int e = tid; e < a.num_q_heads; e += NWM * 64) {
-            a.pre_m[(int64_t)s * a.num_q_heads + e] = -__builtin_inff();
-            a.pre_l[(int64_t)s * a.num_q_heads + e] = 0.f;
-          }
-        } else {
+        if (!(MODE == M_SUFFIX && s_aux[s] > 0)) {
           const float fill = a.context_lens[s] == 0 ? 0.f : __builtin_nanf("");
           for (int e = tid; e < a.num_q_heads * D; e += NWM * 64) store_out<QT>(a.out, base + e, fill);
         }
@@ -388,9 +383,10 @@ __device__ __forceinline__ void attend_sk_body(const DecodeParams& a, const int 
       d.ctx = is.ctx;
       d.j = first_chunk(is.x) + ij;
       d.x = is.x;
-      if constexpr (MODE == M_PREFIX) {
+      if constexpr (MODE != M_PLAIN) {
+        // the team range of the segment, for shared_combine_kernel
         if (ij == 0 && ti == 0 && lane == 0)
-          reinterpret_cast<int4*>(a.share_seg)[(int64_t)is.seq * HG + is.hg] =
+          reinterpret_cast<int4*>(MODE == M_PREFIX ? a.share_seg : a.suf_seg)[(int64_t)is.seq * HG + is.hg] =
               make_int4((int)team, (int)team_of(ic + is.nc - 1, Cc, Wt), (int)Cc, (int)Wt);
       }
       ++ic;
@@ -538,7 +534,7 @@ __device__ __forceinline__ void attend_sk_body(const DecodeParams& a, const int 
         if (col < ncol) {
           if (MODE == M_SUFFIX && whole && d.x > 0) {
             // a sequence with a shared prefix: the partial of its own
-            // tokens, to which prefix_combine_kernel adds the prefix
+            // tokens, to which shared_combine_kernel adds the prefix
             const int64_t prow = (int64_t)d.seq * a.num_q_heads + (int64_t)kvh * G + col;
             float* po = a.pre_o + prow * D + VPL * n;
 #pragma unroll
@@ -688,12 +684,11 @@ attend_sk_dual_kernel(const DecodeParams p, const DecodeParams q, int pre_blocks
 // pieces, as in batches of many sequences.
 // SPLITH: one query head per workgroup (grid z), so a few long segments
 // spread over G times the workgroups, each with G times the piece groups.
-// (The prefix pass of the shared-prefix decode has no merge of its own:
-// prefix_combine_kernel combines its pieces with each sequence's partial.)
+// (The shared-prefix decode's passes are finished by shared_combine_kernel.)
 template <Ty QT, int D, int G, int MODE, int NT = 256, bool BYSEG = false, bool SPLITH = false>
 __global__ void __launch_bounds__(NT)
 merge_sk_kernel(const DecodeParams a, int64_t W) {
-  static_assert(MODE != M_PREFIX, "prefix pieces are combined by prefix_combine_kernel");
+  static_assert(MODE == M_PLAIN, "the shared-prefix passes are finished by shared_combine_kernel");
   static_assert(!SPLITH || BYSEG, "one query head per workgroup: segment-indexed merge only");
   constexpr int GC = SPLITH ? 1 : G;                   // query heads per workgroup
   constexpr int GD = GC * D;
@@ -840,20 +835,6 @@ merge_sk_kernel(const DecodeParams a, int64_t W) {
 #pragma unroll
     for (int q = 0; q < PG; ++q)
       combine(s_m[q][hl], s_l[q][hl], reinterpret_cast<const float4*>(&s_o[q][hl * D + d0]));
-  }
-  if constexpr (MODE == M_SUFFIX) {
-    if (own_start(a, seq, a.context_lens[seq]) > 0) {
-      // a sequence with a shared prefix: the partial of its own tokens, to
-      // which prefix_combine_kernel adds the prefix
-      const int64_t prow = (int64_t)seq * a.num_q_heads + (int64_t)kvh * G + h;
-#pragma unroll
-      for (int e = 0; e < DPT; ++e) a.pre_o[orow + e] = O[e];
-      if (d0 == 0) {
-        a.pre_m[prow] = M;
-        a.pre_l[prow] = L;
-      }
-      return;
-    }
   }
   const float norm = a.v_scale / L;
 #pragma unroll

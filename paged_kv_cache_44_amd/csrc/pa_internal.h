@@ -50,8 +50,10 @@ struct DecodeParams {
                              // prefix are nonzero only at a slot's own index
   int32_t* share_seg;        // [num_seqs * head groups] int4 {first team, last team, Cc, teams}
                              // of each prefix segment, written by the prefix pass
+  int32_t* suf_seg;          // the same for each suffix segment, written by the suffix pass
+  int32_t suf_teams;         // teams of the suffix pass
   const float* pre_ws_o;     // the prefix pass's pieces (its ws_o, ws_m, ws_l), combined
-  const float* pre_ws_m;     // per sequence and head with pre_m, pre_l, pre_o
+  const float* pre_ws_m;     // per sequence and head with the suffix pass's result
   const float* pre_ws_l;
   int32_t pre_teams;         // teams of the prefix pass
   float* pre_m;              // [num_seqs][num_q_heads] partials of a prefixed sequence's own
@@ -150,16 +152,14 @@ hipError_t launch_attend_mfma(const DecodeParams& a, int kv_ty, int q_ty, int g,
                               hipStream_t st);
 hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks, hipStream_t st);
 // shared-prefix decode: planning (fills share_lcp, share_start, share_desc);
-// the prefix (mode 1) and suffix (mode 2) passes in one launch; the merge of
-// the suffix pass's cut segments; the combine of each prefixed sequence's
-// own partial with its prefix pieces
+// the prefix (mode 1) and suffix (mode 2) passes in one launch; the combine
+// of every row that is not finished by the suffix pass (cut segments, and
+// every sequence with a prefix)
 hipError_t launch_share_plan(const DecodeParams& a, int g, hipStream_t st);
 int sk_blocks_shared_dual(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
 hipError_t launch_attend_shared_dual(const DecodeParams& pre, const DecodeParams& suf, int kv_ty,
                                      int q_ty, int g, int pre_blocks, int blocks, hipStream_t st);
-hipError_t launch_merge_shared(const DecodeParams& a, int q_ty, int g, int blocks, int mode,
-                               hipStream_t st);
-hipError_t launch_prefix_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st);
+hipError_t launch_shared_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st);
 bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g);
 int prefill_tiles(int g, int max_query_len);
 hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
