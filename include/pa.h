@@ -276,9 +276,10 @@ pa_status pa_decode_no_alloc(const pa_kv_cache* cache, int32_t layer, const void
 /* matrix-core tiles, so each prefix block is read once per group, while,   */
 /* in the same launch on the other workgroups, each member attends to the   */
 /* rest of its context; a final combine joins the two partial results.     */
-/* Put the samples of one prompt next to each other in the batch. A batch   */
-/* with no sharing gets the right result but runs slower than pa_decode     */
-/* (a quarter of the workgroups are set aside for prefixes and find none).  */
+/* Put the samples of one prompt next to each other in the batch. The two   */
+/* passes split the workgroups by the plan's chunk counts; a batch with no  */
+/* sharing gives them all to the second pass and gets the right result,     */
+/* though a few percent slower than pa_decode (planning and a combine).     */
 /*                                                                           */
 /*  reuse_plan   0: find the sharing from block_tables / context_lens and    */
 /*               store it in the workspace (two small launches). 1: use the  */

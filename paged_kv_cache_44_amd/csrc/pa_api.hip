@@ -273,7 +273,7 @@ DecodeParams decode_params(const pa_kv_cache* cache, int32_t layer, const void* 
 // each prefix segment.
 struct SharedLayout {
   WsLayout suf, pre;
-  size_t pre_base, lcp, start, desc, seg, sseg, pm, pl, po, total;
+  size_t pre_base, lcp, tot, start, desc, seg, sseg, pm, pl, po, total;
   int blocks, g;                 // resident workgroups of the launch holding both passes
 };
 
@@ -290,7 +290,7 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
     return PA_ERR_UNSUPPORTED;
   L->g = g;
   L->blocks = pa::sk_blocks_shared_dual((int)c->dtype, (int)q_dtype, c->head_dim, g, num_seqs);
-  if (L->blocks <= 0) return PA_ERR_UNSUPPORTED;
+  if (L->blocks < 16) return PA_ERR_UNSUPPORTED;   // both passes need a round of the XCDs
   const int H = c->num_kv_heads;
   // each pass runs on at most all of the launch's workgroups
   L->suf = ws_layout(pa::sk_slots(L->blocks, num_seqs, H) * g, c->head_dim, (size_t)L->blocks * 4);
@@ -299,7 +299,8 @@ pa_status shared_layout(const pa_kv_cache* c, int num_seqs, int num_q_heads, pa_
                      (size_t)L->blocks * 4);
   const size_t S = (size_t)num_seqs;
   L->lcp = L->pre_base + L->pre.total;
-  L->start = L->lcp + align256(S * 4);
+  L->tot = L->lcp + align256(S * 4);
+  L->start = L->tot + 256;
   L->desc = L->start + align256(S * 4);
   L->seg = L->desc + align256(S * 16);
   L->sseg = L->seg + align256(S * (size_t)H * 16);
@@ -656,28 +657,17 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   a.share_desc = reinterpret_cast<int32_t*>(w + L.desc);
   a.share_seg = reinterpret_cast<int32_t*>(w + L.seg);
   a.suf_seg = reinterpret_cast<int32_t*>(w + L.sseg);
+  a.share_tot = reinterpret_cast<int32_t*>(w + L.tot);
   a.pre_m = reinterpret_cast<float*>(w + L.pm);
   a.pre_l = reinterpret_cast<float*>(w + L.pl);
   a.pre_o = reinterpret_cast<float*>(w + L.po);
-  // One launch runs both passes side by side: workgroups 0 .. pre_blocks - 1
-  // the prefix pass, the rest the suffix pass, which does not wait for the
-  // prefix (it leaves a prefixed sequence's result as a partial that the
-  // combine completes). The split is fixed (the sizes of the two passes are
-  // known only on the device): a quarter of the workgroups for the prefix
-  // pass, whose slots read each prompt once for up to 32 / G samples while
-  // the samples' own tokens grow every step. On 32 prompts x 8 samples
-  // (1,024 prompt tokens, 64-256 own, fp16) the step took 88-90 us with a
-  // quarter, 89-90 us with 5/16 or 3/8 and 92-95 us with half. A batch has
-  // at most num_seqs / 2 prefix slots, and both parts are capped for small
-  // batches as in the plain decode.
-  const int H = cache->num_kv_heads;
-  const int pre_blocks =
-      std::min(pa::sk_launch_blocks(L.blocks, std::max(1, num_seqs / 2), max_context_len, H),
-               std::max(8, L.blocks / 4 / 8 * 8));
-  const int suf_blocks =
-      pa::sk_launch_blocks(std::max(8, L.blocks - pre_blocks), num_seqs, max_context_len, H);
-  a.pre_teams = pre_blocks * 4 / a.team;
-  a.suf_teams = suf_blocks * 4 / a.team;
+  // One launch runs both passes side by side (the kernel splits its
+  // workgroups between them from the plan, see attend_sk_dual_kernel): all
+  // the resident workgroups, or fewer for small batches as in the plain
+  // decode, and never under two rounds of the XCDs.
+  const int blocks = std::max(
+      16, pa::sk_launch_blocks(L.blocks, num_seqs, max_context_len, cache->num_kv_heads));
+  a.pre_teams = a.suf_teams = blocks * 4 / a.team;
   const int kv = (int)cache->dtype, qt = (int)q_dtype;
   if (!reuse_plan && pa::launch_share_plan(a, L.g, stream) != hipSuccess) return PA_ERR_HIP;
   // the prefix pass's pieces and the suffix pass's, each in its own region
@@ -691,8 +681,7 @@ pa_status pa_decode_shared(const pa_kv_cache* cache, int32_t layer, const void* 
   suf.ws_m = reinterpret_cast<float*>(w + L.suf.m);
   suf.ws_l = reinterpret_cast<float*>(w + L.suf.l);
   suf.ws_team = reinterpret_cast<int32_t*>(w + L.suf.team);
-  if (pa::launch_attend_shared_dual(pre, suf, kv, qt, L.g, pre_blocks, pre_blocks + suf_blocks,
-                                    stream) != hipSuccess)
+  if (pa::launch_attend_shared_dual(pre, suf, kv, qt, L.g, blocks, stream) != hipSuccess)
     return PA_ERR_HIP;
   // every row the suffix pass left open: its pieces (or own partial) and,
   // with a prefix, the prefix pieces, combined

@@ -152,6 +152,9 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
   for (int i = 0; i < E; ++i)
     if (s0 + i < s1 && lead[i] != s0 + i) atomicMin(&s_min[lead[i]], lcp[i]);
   __syncthreads();
+  // the sizes of the two passes, for the split of the launch that runs them:
+  // prefix chunks of every slot, and every sequence's own chunks
+  int cp = 0, cs = 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const int s = s0 + i;
@@ -164,8 +167,33 @@ __global__ void __launch_bounds__(PT) share_plan_kernel(const DecodeParams a) {
     // group's first member
     const int slot = pre > 0 ? L + (s - L) / NS * NS : s;
     int4 d = make_int4(slot, 0, 0, 0);
-    if (pre > 0 && slot == s) d = make_int4(s, min(NS, end[i] - s), pre, 0);
+    if (pre > 0 && slot == s) {
+      d = make_int4(s, min(NS, end[i] - s), pre, 0);
+      cp += pre / 16;
+    }
     reinterpret_cast<int4*>(a.share_desc)[s] = d;
+    const int ctx = a.context_lens[s];
+    if (row_valid(a, ctx)) cs += (ctx - pre + 15) / 16;
+  }
+  __shared__ int s_tot[2][PT / 64];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    cp += __shfl_xor(cp, o);
+    cs += __shfl_xor(cs, o);
+  }
+  if ((t & 63) == 0) {
+    s_tot[0][t >> 6] = cp;
+    s_tot[1][t >> 6] = cs;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int tp = 0, tq = 0;
+    for (int w = 0; w < PT / 64; ++w) {
+      tp += s_tot[0][w];
+      tq += s_tot[1][w];
+    }
+    a.share_tot[0] = tp;
+    a.share_tot[1] = tq;
   }
 }
 
@@ -192,12 +220,12 @@ __global__ void __launch_bounds__(256) shared_combine_kernel(const DecodeParams 
   const int st0 = own_start(a, s, ctx);
   // the suffix segment: its chunks and the teams holding its pieces
   const int nsuf = seq_chunks(a, ctx) > 0 ? (ctx - st0 + CH - 1) / CH : 0;
-  int t0 = 0, t1 = -1;
+  int t0 = 0, t1 = -1, steams = 1;
   int64_t ccs = 0;
   bool own_partial = false, bad_record = false;
   if (nsuf > 0) {
     const int4 sg = reinterpret_cast<const int4*>(a.suf_seg)[(int64_t)s * HG + hg];
-    if (!(sg.x >= 0 && sg.x <= sg.y && sg.y < a.suf_teams && sg.z > 0 && sg.w == a.suf_teams)) {
+    if (!segment_record_ok(sg, a.suf_teams)) {
       bad_record = true;
     } else if (sg.x == sg.y) {
       if (st0 <= 0) return;                      // finished by the suffix pass
@@ -206,6 +234,7 @@ __global__ void __launch_bounds__(256) shared_combine_kernel(const DecodeParams 
       t0 = sg.x;
       t1 = sg.y;
       ccs = sg.z;
+      steams = sg.w;
     }
   } else if (st0 <= 0) {
     return;                                      // empty or invalid row: written by the suffix pass
@@ -260,13 +289,14 @@ __global__ void __launch_bounds__(256) shared_combine_kernel(const DecodeParams 
     }
   };
   // the suffix pass's pieces of a cut segment
-  combine_pieces(a.ws_m, a.ws_l, a.ws_o, (int64_t)s * HG + hg, t0, t1, ccs, a.suf_teams, G, hh);
+  combine_pieces(a.ws_m, a.ws_l, a.ws_o, (int64_t)s * HG + hg, t0, t1, ccs, steams, G, hh);
   // the prefix pass's pieces of the sequence's columns
   if (st0 > 0) {
     int64_t cs = 0, ccp = 0;
-    int col0 = 0, p0 = 0, p1 = -1;
-    if (!prefix_segment(a, s, hg, HG, PA_PREFIX_COLS / G, G, cs, col0, p0, p1, ccp)) L = __builtin_nanf("");
-    combine_pieces(a.pre_ws_m, a.pre_ws_l, a.pre_ws_o, cs, p0, p1, ccp, a.pre_teams, PA_PREFIX_COLS,
+    int col0 = 0, p0 = 0, p1 = -1, pteams = 1;
+    if (!prefix_segment(a, s, hg, HG, PA_PREFIX_COLS / G, G, cs, col0, p0, p1, ccp, pteams))
+      L = __builtin_nanf("");
+    combine_pieces(a.pre_ws_m, a.pre_ws_l, a.pre_ws_o, cs, p0, p1, ccp, pteams, PA_PREFIX_COLS,
                    col0 + hh);
   }
   const float norm = a.v_scale / L;
@@ -363,12 +393,12 @@ static int sk_blocks_dual(int kv_ty, int q_ty, int head_dim, int g, int num_seqs
 }
 
 static hipError_t sk_launch_dual(const DecodeParams& p, const DecodeParams& q, int kv_ty, int q_ty,
-                                 int g, int pre_blocks, int blocks, hipStream_t st) {
+                                 int g, int blocks, hipStream_t st) {
   const int r = sk_dual_dispatch(kv_ty, q_ty, p.head_dim, g, [&](auto kv, auto qt, auto d, auto gg) -> int {
     constexpr Ty KV = decltype(kv)::value, QT = decltype(qt)::value;
     constexpr int D = decltype(d)::value, G = decltype(gg)::value;
     hipLaunchKernelGGL((attend_sk_dual_kernel<KV, QT, D, G>), dim3(blocks), dim3(NWM * 64),
-                       sk_lds_bytes(p.num_seqs, M_PREFIX), st, p, q, pre_blocks);
+                       sk_lds_bytes(p.num_seqs, M_PREFIX), st, p, q);
     return (int)hipGetLastError();
   });
   return r < 0 ? hipErrorInvalidValue : (hipError_t)r;
@@ -381,8 +411,8 @@ int sk_blocks_shared_dual(int kv_ty, int q_ty, int head_dim, int g, int num_seqs
 }
 
 hipError_t launch_attend_shared_dual(const DecodeParams& pre, const DecodeParams& suf, int kv_ty,
-                                     int q_ty, int g, int pre_blocks, int blocks, hipStream_t st) {
-  return sk_launch_dual(pre, suf, kv_ty, q_ty, g, pre_blocks, blocks, st);
+                                     int q_ty, int g, int blocks, hipStream_t st) {
+  return sk_launch_dual(pre, suf, kv_ty, q_ty, g, blocks, st);
 }
 
 

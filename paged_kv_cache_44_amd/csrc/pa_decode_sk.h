@@ -101,24 +101,30 @@ __device__ __forceinline__ int own_start(const DecodeParams& a, int s, int ctx) 
   return (st0 < 0 || st0 > ctx || (st0 & (CH - 1))) ? 0 : st0;
 }
 
+// A pass's record of a segment, {first team, last team, column count, teams
+// of the pass}, checked against the most teams the launch can have.
+__device__ __forceinline__ bool segment_record_ok(const int4 sg, int max_teams) {
+  return sg.w > 0 && sg.w <= max_teams && sg.x >= 0 && sg.x <= sg.y && sg.y < sg.w && sg.z > 0;
+}
+
 // The prefix-pass segment holding sequence s's prefix for head group hg:
 // its index cs, the sequence's first tile column col0, and the teams t0 ..
-// t1 (and the column count Ccp) of the prefix pass whose ranges hold its
+// t1 (of the pass's teams, and its column count Ccp) whose ranges hold its
 // pieces. False when s has no prefix slot or the records do not fit the
 // batch (they then are not read).
 __device__ __forceinline__ bool prefix_segment(const DecodeParams& a, int s, int hg, int hgs,
                                                int ns, int g, int64_t& cs, int& col0, int& t0,
-                                               int& t1, int64_t& ccp) {
+                                               int& t1, int64_t& ccp, int& teams) {
   const int4 sd = reinterpret_cast<const int4*>(a.share_desc)[s];
   const int p = sd.x;
   if (p < 0 || p > s || s - p >= ns) return false;
   cs = (int64_t)p * hgs + hg;
   const int4 sg = reinterpret_cast<const int4*>(a.share_seg)[cs];
-  if (!(sg.x >= 0 && sg.x <= sg.y && sg.y < a.pre_teams && sg.z > 0 && sg.w == a.pre_teams))
-    return false;
+  if (!segment_record_ok(sg, a.pre_teams)) return false;
   t0 = sg.x;
   t1 = sg.y;
   ccp = sg.z;
+  teams = sg.w;
   col0 = (s - p) * g;
   return true;
 }
@@ -658,19 +664,37 @@ attend_sk_kernel(const DecodeParams a) {
   attend_sk_body<KV, QT, D, G, MODE, false>(a, 0, 0);
 }
 
-// The shared-prefix decode's two passes in one launch: workgroups
-// 0 .. pre_blocks - 1 run the prefix pass (parameters p), the others the
-// suffix pass (parameters q), at the same time. Neither reads what the other
-// writes: the suffix pass leaves the result of a sequence that has a prefix
-// as a partial, and prefix_combine_kernel adds the prefix afterwards.
+// The shared-prefix decode's two passes in one launch: the first pre
+// workgroups run the prefix pass (parameters p), the others the suffix pass
+// (parameters q), at the same time. Neither reads what the other writes:
+// the suffix pass leaves the result of a sequence that has a prefix as a
+// partial, and shared_combine_kernel adds the prefix afterwards. The split
+// follows the plan's totals: the prefix chunks of the slots (cp) and each
+// sequence's own chunks (cs); the prefix pass gets nblk * cp / (cp + 2 cs)
+// workgroups (a prefix chunk weighs half an own chunk: it is read once for
+// a whole slot, while the short own segments run below streaming speed),
+// in whole rounds of the XCDs; none without prefixes, and at least one
+// round for each pass otherwise. (32 prompts x 8 samples, 1,024 prompt
+// tokens and 64-256 own: about a quarter, which measured best among fixed
+// fractions.)
 template <Ty KV, Ty QT, int D, int G>
 __global__ void __launch_bounds__(NWM * 64)
 __attribute__((amdgpu_waves_per_eu(sk_waves_per_simd<KV, D, G, M_PREFIX>())))
-attend_sk_dual_kernel(const DecodeParams p, const DecodeParams q, int pre_blocks) {
-  if ((int)blockIdx.x < pre_blocks)
-    attend_sk_body<KV, QT, D, G, M_PREFIX, true>(p, blockIdx.x, pre_blocks);
+attend_sk_dual_kernel(const DecodeParams p, const DecodeParams q) {
+  // (totals of a stale plan only steer the split; any split is correct)
+  const float tp = (float)max(__builtin_amdgcn_readfirstlane(p.share_tot[0]), 0);
+  const float ts = (float)max(__builtin_amdgcn_readfirstlane(p.share_tot[1]), 0);
+  const int nb = gridDim.x;                   // a multiple of 8, at least 16
+  int pre = 0;
+  if (tp > 0.f) {
+    const int x = (int)((float)nb * tp / (tp + 2.f * ts)) / NXCD * NXCD;
+    pre = min(max(x, NXCD), nb - NXCD);
+  }
+  pre = __builtin_amdgcn_readfirstlane(pre);   // the same in every lane: keep the parts' indices scalar
+  if ((int)blockIdx.x < pre)
+    attend_sk_body<KV, QT, D, G, M_PREFIX, true>(p, blockIdx.x, pre);
   else
-    attend_sk_body<KV, QT, D, G, M_SUFFIX, true>(q, blockIdx.x - pre_blocks, gridDim.x - pre_blocks);
+    attend_sk_body<KV, QT, D, G, M_SUFFIX, true>(q, blockIdx.x - pre, nb - pre);
 }
 
 // Merge of segments cut by team range boundaries: M = max_p m_p,

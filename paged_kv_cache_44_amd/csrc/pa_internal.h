@@ -51,11 +51,13 @@ struct DecodeParams {
   int32_t* share_seg;        // [num_seqs * head groups] int4 {first team, last team, Cc, teams}
                              // of each prefix segment, written by the prefix pass
   int32_t* suf_seg;          // the same for each suffix segment, written by the suffix pass
-  int32_t suf_teams;         // teams of the suffix pass
+  int32_t* share_tot;        // [2] from the plan: prefix chunks of all slots, own chunks of all
+                             // sequences (the split of the launch that runs both passes)
+  int32_t suf_teams;         // most teams the suffix pass can have (records carry the count)
   const float* pre_ws_o;     // the prefix pass's pieces (its ws_o, ws_m, ws_l), combined
   const float* pre_ws_m;     // per sequence and head with the suffix pass's result
   const float* pre_ws_l;
-  int32_t pre_teams;         // teams of the prefix pass
+  int32_t pre_teams;         // most teams the prefix pass can have (records carry the count)
   float* pre_m;              // [num_seqs][num_q_heads] partials of a prefixed sequence's own
   float* pre_l;              // tokens (after its shared prefix): running max (log2), sum of
   float* pre_o;              // weights, [head_dim] unnormalised output
@@ -158,7 +160,7 @@ hipError_t launch_merge_mfma(const DecodeParams& a, int q_ty, int g, int blocks,
 hipError_t launch_share_plan(const DecodeParams& a, int g, hipStream_t st);
 int sk_blocks_shared_dual(int kv_ty, int q_ty, int head_dim, int g, int num_seqs);
 hipError_t launch_attend_shared_dual(const DecodeParams& pre, const DecodeParams& suf, int kv_ty,
-                                     int q_ty, int g, int pre_blocks, int blocks, hipStream_t st);
+                                     int q_ty, int g, int blocks, hipStream_t st);
 hipError_t launch_shared_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st);
 bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g);
 int prefill_tiles(int g, int max_query_len);
