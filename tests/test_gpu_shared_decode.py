@@ -4,8 +4,9 @@ whose tables name the prompt's blocks, copy-on-write of a partly filled last
 prompt block), over pool / query dtypes, head dims, group sizes and block
 sizes; runs longer than one tile of samples, prefixes that are not a
 multiple of 16, contexts that are all prefix, singletons, empty and invalid
-rows inside runs, a reused plan, and the shared-prefix workload at full size
-on sampled sequences. The pages fix the result: sharing blocks does not
+rows inside runs, a reused plan, the split of the launch between the two
+passes at its extremes (no sharing, one short prefix, contexts that are all
+prefix), and the shared-prefix workload at full size on sampled sequences. The pages fix the result: sharing blocks does not
 change the attention ("Efficient Memory Management for Large Language Model
 Serving with PagedAttention", kernel and sampling paragraphs)."""
 
@@ -103,6 +104,31 @@ def test_runs_filling_both_prefix_tiles(pool, q, G, hkv):
     ref = st.oracle_decode()
     err = max_err_stored(got, ref, wl.q_dtype, _tol(wl))
     say(f"{wl.num_seqs} sequences, G {G}: error beyond output rounding {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= _tol(wl)
+
+
+# The launch splits its workgroups between the passes by the plan's chunk
+# counts: a batch with no sharing gives the prefix pass none; one short
+# shared prefix among long private contexts gives it the least (one round
+# of the XCDs); contexts that are all prefix give the suffix pass the least.
+_R = np.random.default_rng(17)
+SPLITS = {
+    "no_sharing": [(int(p), [int(t)]) for p, t in zip(_R.integers(20, 600, 24), _R.integers(0, 60, 24))],
+    "one_short_prefix": [(16, [3, 5])] + [(600, [int(t)]) for t in _R.integers(1, 80, 20)],
+    "all_prefix": [(512, [0] * 8), (256, [0] * 8), (160, [0, 0, 0])],
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLITS))
+@pytest.mark.parametrize("pool,q,G,hkv", [("f16", "f16", 4, 2), ("fp8_e4m3", "bf16", 8, 1)])
+def test_split_extremes(case, pool, q, G, hkv):
+    wl = workloads.shared_prefix(14, SPLITS[case], pool_dtype=pool, q_dtype=q, num_q_heads=hkv * G,
+                                 num_kv_heads=hkv, head_dim=128, block_size=16)
+    st = _state(wl)
+    got = _shared(st)
+    ref = st.oracle_decode()
+    err = max_err_stored(got, ref, wl.q_dtype, _tol(wl))
+    say(f"{case}: {wl.num_seqs} sequences, error beyond output rounding {err:.3e}")
     assert np.all(np.isfinite(got)) and err <= _tol(wl)
 
 
