@@ -59,7 +59,7 @@ def _shared_prefix_flow(wl):
 def test_shared_prefix_cow_write_and_decode(prefix):
     kw = {} if prefix == 1024 else dict(prefix_tokens=1020)
     wl = workloads.config4(**kw)
-    say(f"config 4 prefix {prefix}: S={wl.num_seqs} cow pairs {len(wl.extra['cow_pairs'])}")
+    say(f"shared-prefix fp16, prefix {prefix}: S={wl.num_seqs} cow pairs {len(wl.extra['cow_pairs'])}")
     st = _shared_prefix_flow(wl)
     same, _, _ = st.pools_equal_oracle()
     assert same
@@ -67,7 +67,7 @@ def test_shared_prefix_cow_write_and_decode(prefix):
     ref = st.oracle_decode()
     assert np.all(np.isfinite(got))
     err = max_err(got, ref)
-    say(f"config 4: max abs err {err:.3e}")
+    say(f"shared-prefix fp16: max abs err {err:.3e}")
     assert err <= TOL["f16"]
 
 
@@ -102,7 +102,7 @@ def test_shared_blocks_unchanged_by_private_writes():
 def test_long_fp8_with_swap_in():
     wl = workloads.config5()
     ex = wl.extra
-    say(f"config 5: S={wl.num_seqs} ctx {list(wl.context_lens)} k_scale {wl.k_scale:.5g} "
+    say(f"long FP8: S={wl.num_seqs} ctx {list(wl.context_lens)} k_scale {wl.k_scale:.5g} "
         f"v_scale {wl.v_scale:.5g}")
     st = DeviceState(wl)
     _fill(st)
@@ -138,5 +138,5 @@ def test_long_fp8_with_swap_in():
     ref = st.oracle_decode()
     assert np.all(np.isfinite(got))
     err = max_err(got, ref)
-    say(f"config 5: max abs err {err:.3e}")
+    say(f"long FP8: max abs err {err:.3e}")
     assert err <= TOL["fp8_e4m3"]

@@ -120,7 +120,7 @@ class Workload:
     # index into write_* of each sequence's newest token (the token one decode
     # step writes before attending); -1 when that token is not in write_*
     step_token: Optional[np.ndarray] = None
-    # extra scenario inputs (config 4: copy-on-write; config 5: swap victim)
+    # extra scenario inputs (shared prefix: copy-on-write pairs; long FP8: the swap victim)
     extra: Dict[str, object] = field(default_factory=dict)
 
     @property
