@@ -31,7 +31,7 @@ def _forked(tokens: int):
 
 
 def check_full_block_cow(seq_cls=Sequence):
-    """Config-4 style: the last shared block is full (8 tokens in blocks 3 and
+    """As the shared-prefix workload does: the last shared block is full (8 tokens in blocks 3 and
     0, both held twice); the child privatises it up front."""
     pool = BlockPool(6, 4, order=ORDER)
     parent = seq_cls(pool, "parent")
