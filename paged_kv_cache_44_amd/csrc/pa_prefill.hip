@@ -22,12 +22,13 @@ namespace {
 // Tiled prefill: each workgroup takes 128 query rows of one (sequence, KV
 // head) -- 128 / G consecutive positions x the G query heads -- 32 rows per
 // wave, and walks the keys of the causal range in tiles of FKT = 32 or 64
-// keys. The four
-// waves stage each tile once in LDS, gathered through the block table (FP8
-// codes widened there, exactly, to the query's 16-bit type): K as rows, V
-// transposed (a row per dim), double buffered, one barrier per tile. Both
-// products run on the 32x32x16 matrix cores, transposed so that a query row
-// owns a lane pair:
+// keys. The four waves stage each tile once in LDS, gathered through the
+// block table, double buffered, one barrier per tile. 16-bit pools are
+// staged by the memory unit straight into LDS (global_load_lds_dwordx4),
+// K and V as key rows; FP8 pools go through registers, their codes widened
+// exactly to the query's 16-bit type, K as rows and V transposed (a row per
+// dim). Both products run on the 32x32x16 matrix cores, transposed so that
+// a query row owns a lane pair:
 //   S^T[FKT keys][32 rows] = K[FKT][D] . Q^T[D][32]    (A = K rows from LDS)
 //   O^T[D][32 rows]      += V^T[D][FKT] . P^T[FKT][32] (A = V^T rows from LDS,
 //                                                       B = P from registers)
@@ -35,8 +36,11 @@ namespace {
 // each 32 keys, or of the dims, in lane l ^ 32), so the row's softmax state,
 // maximum, sum, rescale and normalisation never leave the lane pair. The
 // k-slots of P^T's operand follow the score tile's own key order (lane half h
-// holds keys 4h + j and 8 + 4h + j of each 16); V^T is staged with its keys
-// in that order, so each of its operands is one 16-byte LDS read.
+// holds keys 4h + j and 8 + 4h + j of each 16). From key rows, each V^T
+// operand is two transposing LDS reads (ds_read_b64_tr_b16: within 16 lanes,
+// lane 4j + a reads 4 dims of key j and lane 4a + b receives one dim of 4
+// keys); from transposed FP8 staging, V^T is laid out with its keys in that
+// order, one 16-byte LDS read per operand.
 constexpr int NXCD_PF = 8;        // XCDs of an MI355X
 constexpr int FW = 4;             // waves per workgroup
 constexpr int FR = 32;            // query rows per wave
@@ -45,6 +49,8 @@ constexpr int FR = 32;            // query rows per wave
 constexpr float MASKED = -3.0e38f;
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short tr16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 template <Op O>
 __device__ __forceinline__ f32x16_t mfma32(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x16_t c) {
@@ -76,6 +82,17 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// 16 bytes per lane from global memory straight into LDS, lane i's at LDS
+// byte offset lds_off + 16 i (the memory unit writes LDS; no registers).
+// Issued from asm so that the compiler does not hold every later LDS read
+// (of the other buffer) behind it; callers wait for vmcnt to reach 0 before
+// the barrier that publishes the tile. No outputs; m0 is set here (one wait
+// state before the load reads it).
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_off) : "memory", "m0");
+}
+
 // Position of key kk (0..15 in a 16-key block) in the staged V^T rows: bits
 // 2 and 3 swapped, so that lane half h's 8 keys (4h + j, 8 + 4h + j) are
 // contiguous at 8h.
@@ -83,18 +100,22 @@ __device__ __forceinline__ int vt_slot(int kk) {
   return (kk & 3) | ((kk & 4) << 1) | ((kk & 8) >> 1);
 }
 
-template <int D, int FKT>
+// LDS of one tile, double buffered. Register-staged (FP8 pools, widened on
+// the way): K rows padded by 16 bytes, V transposed (a row per dim).
+// Staged straight from memory (16-bit pools): K and V as unpadded key rows,
+// their 16-byte chunks permuted per row (see prefill_tiled_kernel).
+template <int D, int FKT, bool DIRECT>
 struct FaLds {
-  static constexpr int PK = D * 2 + 16;           // bytes per staged K row (a key)
-  static constexpr int PV = FKT * 2 + 16;         // bytes per staged V^T row (a dim)
+  static constexpr int PK = DIRECT ? D * 2 : D * 2 + 16;   // bytes per staged K row (a key)
+  static constexpr int PV = FKT * 2 + 16;                  // bytes per staged V^T row (a dim)
   static constexpr int KT = FKT * PK;
-  static constexpr int VT = D * PV;
+  static constexpr int VT = DIRECT ? FKT * D * 2 : D * PV;
   static constexpr int BUF = KT + VT;
-  static constexpr int BYTES = 2 * BUF;           // double buffered
+  static constexpr int BYTES = 2 * BUF;
 };
 
 // Keys per tile, and occupancy: 32-key tiles fit 3 waves per SIMD (at most
-// 168 registers and 37 KB of LDS at D = 128), which hides more latency when
+// 168 registers and 33-37 KB of LDS at D = 128), which hides more latency when
 // the grid has many workgroups; 64-key tiles run at 2 and halve the barriers
 // and per-tile work of each workgroup, which wins when there are few (a
 // single long recompute).
@@ -121,7 +142,22 @@ prefill_tiled_kernel(const PrefillParams a) {
   constexpr int JOBS = PAIRS * CPR;               // staging jobs per tile: (key pair, chunk)
   constexpr int NJ = (JOBS + FW * 64 - 1) / (FW * 64);   // jobs per thread
   static_assert(FKT == 32 || FKT == 64, "keys per tile");
-  using L = FaLds<D, FKT>;
+  // 16-bit pools are staged by the memory unit straight into LDS (no
+  // registers, no LDS writes): a wave instruction moves 64 x 16 bytes to
+  // 1 KiB of consecutive LDS, RPI key rows of ROWB bytes. In row r, LDS
+  // chunk position p holds K's 16-byte chunk p ^ (r mod R16) (so the 16
+  // rows a score operand read touches hit distinct banks) and V's chunk
+  // p ^ 4 (r mod SEGS) (whole 64-byte segments permuted, so the eight rows
+  // of a transposing read fall on different banks in pairs at most).
+  constexpr bool DIRECT = EB == 2;
+  constexpr int ROWB = D * 2;                     // bytes per key row
+  constexpr int R16 = ROWB / 16;                  // 16-byte chunks per row
+  constexpr int SEGS = ROWB / 64;                 // 64-byte segments per row
+  constexpr int RPI = 1024 / ROWB;                // rows per wave instruction
+  constexpr int NIW = FKT / (RPI * FW);           // instructions per wave per tile (each of K, V)
+  static_assert(!DIRECT || FKT % (RPI * FW) == 0, "tile rows split evenly over the waves");
+  constexpr int NID = DIRECT ? NIW : NJ * 2;      // block ids a thread fetches per tile
+  using L = FaLds<D, FKT, DIRECT>;
   __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
 
   const int tid = threadIdx.x;
@@ -220,31 +256,61 @@ prefill_tiled_kernel(const PrefillParams a) {
     return min(kt * FKT + 2 * (jb % PAIRS) + odd, ctx - 1);
   };
   auto job_of = [&](int i) __attribute__((always_inline)) { return tid + FW * 64 * i; };
-  auto fetch_ids = [&](int kt, int (&ids)[NJ][2]) __attribute__((always_inline)) {
+  // direct staging: this lane's row of wave instruction j, and its chunk
+  // position in that row
+  auto drow = [&](int j) __attribute__((always_inline)) { return (wave * NIW + j) * RPI + lane / R16; };
+  const int dpos = lane % R16;
+  // transposing V reads: lane 16q + 4J + A reads key J's dims from 4A of
+  // its 16-dim half vdh = q % 2
+  const int vJ = (lane >> 2) & 3, vA = lane & 3, vdh = (lane >> 4) & 1;
+  auto fetch_ids = [&](int kt, int (&ids)[NID]) __attribute__((always_inline)) {
+    if constexpr (DIRECT) {
 #pragma unroll
-    for (int i = 0; i < NJ; ++i)
+      for (int j = 0; j < NIW; ++j) ids[j] = trow[min(kt * FKT + drow(j), ctx - 1) >> lg];
+    } else {
 #pragma unroll
-      for (int o = 0; o < 2; ++o) ids[i][o] = trow[key_at(kt, job_of(i) % JOBS, o) >> lg];
+      for (int i = 0; i < NJ; ++i)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) ids[2 * i + o] = trow[key_at(kt, job_of(i) % JOBS, o) >> lg];
+    }
   };
   bool bad = false;                               // a bad block id was staged
-  uint32_t stk[NJ][2][4], stv[NJ][2][4];
-  auto load_tile = [&](int kt, const int (&ids)[NJ][2]) __attribute__((always_inline)) {
+  uint32_t stk[DIRECT ? 1 : NJ][2][4], stv[DIRECT ? 1 : NJ][2][4];
+  auto load_tile = [&](int kt, const int (&ids)[NID]) __attribute__((always_inline)) {
+    if constexpr (DIRECT) {
+      char* kb = lds + (kt & 1) * L::BUF;
 #pragma unroll
-    for (int i = 0; i < NJ; ++i) {
-      const int jb = job_of(i) % JOBS;            // (a thread past the jobs repeats one)
-#pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        const int k = key_at(kt, jb, o);
-        const bool ok = ids[i][o] >= 0 && ids[i][o] < a.num_blocks;
+      for (int j = 0; j < NIW; ++j) {
+        const int r = drow(j);
+        const int k = min(kt * FKT + r, ctx - 1);
+        const bool ok = ids[j] >= 0 && ids[j] < a.num_blocks;
         bad = bad || !ok;
-        const int64_t e = (int64_t)(ok ? ids[i][o] : 0) * a.block_stride + head_off +
-                          (int64_t)(k & bmask) * D + (jb / PAIRS) * CD;
-        ld<4>(reinterpret_cast<const uint32_t*>(kpool + e * EB), stk[i][o]);
-        ld<4>(reinterpret_cast<const uint32_t*>(vpool + e * EB), stv[i][o]);
+        const int64_t e = (int64_t)(ok ? ids[j] : 0) * a.block_stride + head_off + (int64_t)(k & bmask) * D;
+        const int ck = dpos ^ (r % R16), cv = dpos ^ ((r % SEGS) << 2);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(kb + (wave * NIW + j) * 1024));
+        lds_dma16(kpool + (e + 8 * ck) * 2, dst);
+        lds_dma16(vpool + (e + 8 * cv) * 2, dst + L::KT);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NJ; ++i) {
+        const int jb = job_of(i) % JOBS;          // (a thread past the jobs repeats one)
+#pragma unroll
+        for (int o = 0; o < 2; ++o) {
+          const int k = key_at(kt, jb, o);
+          const bool ok = ids[2 * i + o] >= 0 && ids[2 * i + o] < a.num_blocks;
+          bad = bad || !ok;
+          const int64_t e = (int64_t)(ok ? ids[2 * i + o] : 0) * a.block_stride + head_off +
+                            (int64_t)(k & bmask) * D + (jb / PAIRS) * CD;
+          ld<4>(reinterpret_cast<const uint32_t*>(kpool + e * EB), stk[i][o]);
+          ld<4>(reinterpret_cast<const uint32_t*>(vpool + e * EB), stv[i][o]);
+        }
       }
     }
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (!DIRECT) {                      // (direct: the memory unit wrote it)
     char* kb = lds + buf * L::BUF;
     char* vb = kb + L::KT;
 #pragma unroll
@@ -285,6 +351,7 @@ prefill_tiled_kernel(const PrefillParams a) {
         *reinterpret_cast<uint32_t*>(vdst + (d + 1) * L::PV) = __builtin_amdgcn_perm(w[1][q], w[0][q], 0x07060302u);
       }
     }
+    }
   };
 
   // ---- per-row state: reference max (log2 units), this lane's share of the
@@ -309,8 +376,11 @@ prefill_tiled_kernel(const PrefillParams a) {
       // all of the block's K operands first, then the products
       uint4 kv[KSTEPS];
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k)
-        kv[k] = *reinterpret_cast<const uint4*>(kb + (32 * b + n) * L::PK + (16 * k + 8 * h) * 2);
+      for (int k = 0; k < KSTEPS; ++k) {
+        const int row = 32 * b + n, c = 2 * k + h;          // key row, 16-byte chunk
+        kv[k] = *reinterpret_cast<const uint4*>(kb + row * L::PK +
+                                                (DIRECT ? (c ^ (row % R16)) * 16 : c * 16));
+      }
       sb[b] = (f32x16_t){};
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
@@ -365,8 +435,29 @@ prefill_tiled_kernel(const PrefillParams a) {
     for (int kb2 = 0; kb2 < NKB; ++kb2) {
       uint4 vv[NB];
 #pragma unroll
-      for (int mb = 0; mb < NB; ++mb)
-        vv[mb] = *reinterpret_cast<const uint4*>(vb + (32 * mb + n) * L::PV + (16 * kb2 + 8 * h) * 2);
+      for (int mb = 0; mb < NB; ++mb) {
+        if constexpr (DIRECT) {
+          // V^T operand from key rows by two transposing reads: in each
+          // 16-lane group, lane 4J + A reads 4 dims (from 4A) of key J, and
+          // lane 4A + B receives dim 4A + B of keys 0..3 (k-slots 4r .. +3:
+          // keys 16 kb2 + 8r + 4h + 0..3, as P's operand holds them)
+          uint32_t w4[4];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int key = 16 * kb2 + 8 * r + 4 * h + vJ;
+            const int c = 4 * mb + 2 * vdh + (vA >> 1);
+            const char* src = vb + key * ROWB + (c ^ ((key % SEGS) << 2)) * 16 + (vA & 1) * 8;
+            const auto t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) tr16x4_t*)src);
+            const u32x2_t tw = __builtin_bit_cast(u32x2_t, t);
+            w4[2 * r] = tw[0];
+            w4[2 * r + 1] = tw[1];
+          }
+          vv[mb] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        } else {
+          vv[mb] = *reinterpret_cast<const uint4*>(vb + (32 * mb + n) * L::PV + (16 * kb2 + 8 * h) * 2);
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < NB; ++mb) {
         const uint32_t av[4] = {vv[mb].x, vv[mb].y, vv[mb].z, vv[mb].w};
@@ -377,11 +468,14 @@ prefill_tiled_kernel(const PrefillParams a) {
 
   // ---- the tile loop: loads of tile kt+1 and block ids of tile kt+2 in
   // flight while tile kt is processed from LDS; one barrier per tile
-  int ids_a[NJ][2], ids_b[NJ][2];
+  // (direct staging: each wave waits for its own loads into LDS before the
+  // barrier that hands the tile to all four)
+  int ids_a[NID], ids_b[NID];
   fetch_ids(0, ids_a);
   load_tile(0, ids_a);
   if (nkt > 1) fetch_ids(1, ids_b);
   store_tile(0);
+  if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   auto step = [&](int kt, auto mask_tag) __attribute__((always_inline)) {
     const bool more = kt + 1 < nkt;
@@ -390,12 +484,10 @@ prefill_tiled_kernel(const PrefillParams a) {
     // a wave with no rows, or whose rows all end before this tile, skips it
     if (wave_live && kt * FKT <= wmax) compute(kt, kt & 1, mask_tag);
     if (more) store_tile((kt + 1) & 1);
+    if constexpr (DIRECT) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NJ; ++i) {
-      ids_b[i][0] = ids_a[i][0];
-      ids_b[i][1] = ids_a[i][1];
-    }
+    for (int i = 0; i < NID; ++i) ids_b[i] = ids_a[i];
   };
   // tiles 0 .. nfull - 1 end at or before the workgroup's first position
   // (every key at or before every row's, none past the context); two loops,
