@@ -158,6 +158,12 @@ LARGE_GRID = [
     ("fp8_e4m3", "bf16", 128, 8, 16),
     ("fp8_e4m3", "f16", 64, 1, 4),
     ("bf16", "bf16", 128, 16, 32),
+    # blocks smaller than the 4 key rows (D = 128; 8 at D = 64) one wave
+    # instruction stages straight into LDS: the rows of one instruction
+    # come from different blocks
+    ("f16", "f16", 128, 4, 2),
+    ("bf16", "bf16", 64, 8, 1),
+    ("bf16", "bf16", 128, 2, 4),
 ]
 
 
