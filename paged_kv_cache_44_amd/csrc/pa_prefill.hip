@@ -289,8 +289,8 @@ prefill_tiled_kernel(const PrefillParams a) {
         const int ck = dpos ^ (r % R16), cv = dpos ^ ((r % SEGS) << 2);
         const uint32_t dst = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(kb + (wave * NIW + j) * 1024));
-        lds_dma16(kpool + (e + 8 * ck) * 2, dst);
-        lds_dma16(vpool + (e + 8 * cv) * 2, dst + L::KT);
+        lds_dma16(kpool + (e + 8 * ck) * EB, dst);
+        lds_dma16(vpool + (e + 8 * cv) * EB, dst + L::KT);
       }
     } else {
 #pragma unroll
