@@ -42,6 +42,9 @@
  *    dtype combinations, unsupported sizes, a too-small workspace, host-side
  *    copy pairs) are reported before any HIP call is made and leave every
  *    buffer untouched. Launch failures return PA_ERR_HIP.
+ *  - Alignment: pool base pointers, q and pa_write_kv's sources 16-byte,
+ *    out 4-byte, workspaces 256-byte aligned; a misaligned pointer gives
+ *    PA_ERR_UNSUPPORTED.
  *  - Bad values inside device arrays never cause an out-of-bounds access:
  *      * pa_write_kv skips a token whose slot lies beyond the pool;
  *      * pa_decode writes a NaN output row for a sequence whose context

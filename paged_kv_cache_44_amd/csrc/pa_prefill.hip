@@ -496,9 +496,54 @@ prefill_tiled_kernel(const PrefillParams a) {
   for (int kt = 0; kt < nfull; ++kt) step(kt, std::false_type{});
   for (int kt = nfull; kt < nkt; ++kt) step(kt, std::true_type{});
   bad = __syncthreads_or(bad);
-  if (!rvalid) return;
   const float lt = l_sum + __shfl_xor(l_sum, 32);
-  store_row(o, bad ? __builtin_nanf("") : a.v_scale / lt);
+  const float norm = bad ? __builtin_nanf("") : a.v_scale / lt;
+  // Rows leave as whole 16-byte pieces, 16 lanes per row: a lane's O^T
+  // elements are 4-dim pieces of one row, so they pass through LDS (free
+  // now: every wave is past its last tile). The wave's FR rows are stored
+  // row-major with 16-byte chunk c of row r at c ^ (r mod R16), so both the
+  // writes and the reads spread over the banks.
+  static_assert(FW * FR * ROWB <= L::BYTES, "the output rows fit in the tile buffers");
+  char* ob = lds + wave * (FR * ROWB);
+  // the lane's row and half again, from the lane counter (rather than
+  // values kept in registers through the tile loop)
+  int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(ln));
+  const int on = ln & 31, oh = ln >> 5;
+  auto h16 = [](float x) __attribute__((always_inline)) -> uint32_t {
+    return QT == Ty::BF16 ? f32_to_bf16_rne(x) : f32_to_f16_rne(x);
+  };
+#pragma unroll
+  for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // dims 32 mb + 8q + 4h .. +3: half h of chunk 4 mb + q
+      const uint32_t w0 = h16(o[mb][4 * q] * norm) | (h16(o[mb][4 * q + 1] * norm) << 16);
+      const uint32_t w1 = h16(o[mb][4 * q + 2] * norm) | (h16(o[mb][4 * q + 3] * norm) << 16);
+      const int c = 4 * mb + q;
+      *reinterpret_cast<uint2*>(ob + on * ROWB + (c ^ (on % R16)) * 16 + oh * 8) = make_uint2(w0, w1);
+    }
+  __syncthreads();
+  const bool out16 = (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < FR / RPI; ++i) {
+    const int row = i * RPI + ln / R16, c = ln % R16;
+    const uint4 v = *reinterpret_cast<const uint4*>(ob + row * ROWB + (c ^ (row % R16)) * 16);
+    const int Rw = wave * FR + row, qw = tpos0 + Rw / G;
+    if (qw < nq) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                      (((int64_t)r0 + qw) * a.num_q_heads + (int64_t)kvh * G + Rw % G) * D + 8 * c;
+      if (out16) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {                                    // an output only 4-byte aligned
+        uint32_t* d4 = reinterpret_cast<uint32_t*>(dst);
+        d4[0] = v.x;
+        d4[1] = v.y;
+        d4[2] = v.z;
+        d4[3] = v.w;
+      }
+    }
+  }
 }
 
 template <Ty KV, Ty QT, int D, int FKT>

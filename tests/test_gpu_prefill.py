@@ -28,12 +28,12 @@ def _announce(request, gpu):
     torch.cuda.synchronize()
 
 
-def _run(st, q_codes, qsl, tables=None, ctx=None, max_q=None, out_fill=None):
+def _run(st, q_codes, qsl, tables=None, ctx=None, max_q=None, out_fill=None, out=None):
     wl = st.wl
     tables = wl.block_tables if tables is None else tables
     ctx = wl.context_lens if ctx is None else ctx
     q = codes_to_tensor(q_codes, wl.q_dtype)
-    out = torch.empty_like(q)
+    out = torch.empty_like(q) if out is None else out
     if out_fill is not None:
         out.view(torch.int16).fill_(out_fill)
     tt = torch.from_numpy(np.ascontiguousarray(tables, dtype=np.int32)).cuda()
@@ -85,6 +85,32 @@ def test_prefill_matches_oracle(pool, q, D, G, B, HKV):
     ex = max_err_stored(got, ref, q, TOL[pool])
     say(f"{int(qsl[-1])} rows, max abs err {err:.3e}, beyond output rounding {ex:.3e}")
     assert ex <= TOL[pool]
+
+
+@pytest.mark.parametrize("pool,q,D", [("bf16", "bf16", 128), ("f16", "f16", 64),
+                                      ("fp8_e4m3", "bf16", 128)])
+def test_prefill_output_alignment(pool, q, D):
+    """Rows leave the kernel as 16-byte pieces when the output is 16-byte
+    aligned and element by element otherwise: an output 4 bytes off that
+    alignment (the least the call accepts) gets the same values bit for bit,
+    and nothing around it is written."""
+    ctx, nq = [1, 40, 257, 100], [1, 40, 200, 33]
+    wl = workloads.custom(321, ctx, pool_dtype=pool, q_dtype=q, num_q_heads=8, num_kv_heads=2,
+                          head_dim=D, block_size=16)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    qc, qsl = workloads.prefill_queries(wl, nq, 322)
+    ref = _run(st, qc, qsl)
+    assert ref.data_ptr() % 16 == 0
+    n = ref.numel()
+    buf = torch.full((n + 16,), -7, dtype=torch.int16, device=ref.device)
+    out = buf[2:2 + n].view(ref.dtype).view(ref.shape)
+    assert out.data_ptr() % 16 == 4
+    _run(st, qc, qsl, out=out)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert bool((buf[:2] == -7).all()) and bool((buf[2 + n:] == -7).all())
+    got = codecs.decode(tensor_codes(ref), q)
+    assert max_err_stored(got, _oracle(st, qc, qsl), q, TOL[pool]) <= TOL[pool]
 
 
 def test_prefill_recompute_long_fp8():
