@@ -93,6 +93,20 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_off) {
                :: "v"(gptr), "s"(lds_off) : "memory", "m0");
 }
 
+// The same from a wave-uniform base address (scalar registers) plus the
+// lane's 32-bit byte offset.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds_off) : "memory", "m0");
+}
+
+// 16 bytes from LDS byte address addr.
+__device__ __forceinline__ uint4 lds_ld16(uint32_t addr) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)addr;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Position of key kk (0..15 in a 16-key block) in the staged V^T rows: bits
 // 2 and 3 swapped, so that lane half h's 8 keys (4h + j, 8 + 4h + j) are
 // contiguous at 8h.
@@ -122,7 +136,10 @@ struct FaLds {
 template <int FKT>
 constexpr int pf_waves_per_simd() { return FKT == 32 ? 3 : 2; }
 
-template <Ty KV, Ty QT, int D, int G, int FKT>
+// UB (16-bit pools, block_size >= the RPI rows one staging instruction
+// moves): each instruction's rows are consecutive keys of one block, so its
+// block id and base address are wave-uniform and computed in scalar registers.
+template <Ty KV, Ty QT, int D, int G, int FKT, bool UB>
 __global__ void __launch_bounds__(FW * 64)
 __attribute__((amdgpu_waves_per_eu(pf_waves_per_simd<FKT>())))
 prefill_tiled_kernel(const PrefillParams a) {
@@ -156,9 +173,10 @@ prefill_tiled_kernel(const PrefillParams a) {
   constexpr int RPI = 1024 / ROWB;                // rows per wave instruction
   constexpr int NIW = FKT / (RPI * FW);           // instructions per wave per tile (each of K, V)
   static_assert(!DIRECT || FKT % (RPI * FW) == 0, "tile rows split evenly over the waves");
+  static_assert(DIRECT || !UB, "uniform staging bases: 16-bit pools only");
   constexpr int NID = DIRECT ? NIW : NJ * 2;      // block ids a thread fetches per tile
   using L = FaLds<D, FKT, DIRECT>;
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[L::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -263,8 +281,21 @@ prefill_tiled_kernel(const PrefillParams a) {
   // transposing V reads: lane 16q + 4J + A reads key J's dims from 4A of
   // its 16-dim half vdh = q % 2
   const int vJ = (lane >> 2) & 3, vA = lane & 3, vdh = (lane >> 4) & 1;
+  // (UB) lane byte offsets of instruction j's rows from its base, K and V
+  uint32_t koff[UB ? NIW : 1], voff[UB ? NIW : 1];
+  if constexpr (UB) {
+#pragma unroll
+    for (int j = 0; j < NIW; ++j) {
+      const int r = drow(j);
+      koff[j] = (lane / R16) * ROWB + (dpos ^ (r % R16)) * 16;
+      voff[j] = (lane / R16) * ROWB + (dpos ^ ((r % SEGS) << 2)) * 16;
+    }
+  }
   auto fetch_ids = [&](int kt, int (&ids)[NID]) __attribute__((always_inline)) {
-    if constexpr (DIRECT) {
+    if constexpr (UB) {
+#pragma unroll
+      for (int j = 0; j < NIW; ++j) ids[j] = trow[min(kt * FKT + (wave * NIW + j) * RPI, ctx - 1) >> lg];
+    } else if constexpr (DIRECT) {
 #pragma unroll
       for (int j = 0; j < NIW; ++j) ids[j] = trow[min(kt * FKT + drow(j), ctx - 1) >> lg];
     } else {
@@ -277,7 +308,29 @@ prefill_tiled_kernel(const PrefillParams a) {
   bool bad = false;                               // a bad block id was staged
   uint32_t stk[DIRECT ? 1 : NJ][2][4], stv[DIRECT ? 1 : NJ][2][4];
   auto load_tile = [&](int kt, const int (&ids)[NID]) __attribute__((always_inline)) {
-    if constexpr (DIRECT) {
+    if constexpr (UB) {
+      char* kb = lds + (kt & 1) * L::BUF;
+#pragma unroll
+      for (int j = 0; j < NIW; ++j) {
+        // key0: the instruction's first row; rows past the context read the
+        // last key again (then key0 + lane row is clamped per lane)
+        const int key0 = min(kt * FKT + (wave * NIW + j) * RPI, ctx - 1);
+        const int id = __builtin_amdgcn_readfirstlane(ids[j]);
+        const bool ok = id >= 0 && id < a.num_blocks;
+        bad = bad || !ok;
+        const int64_t e0 = (int64_t)(ok ? id : 0) * a.block_stride + head_off + (int64_t)(key0 & bmask) * D;
+        uint32_t lk = koff[j], lv = voff[j];
+        if (key0 + RPI > ctx) {
+          const int lr = min(lane / R16, ctx - 1 - key0), r = drow(j);
+          lk = lr * ROWB + (dpos ^ (r % R16)) * 16;
+          lv = lr * ROWB + (dpos ^ ((r % SEGS) << 2)) * 16;
+        }
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(kb + (wave * NIW + j) * 1024));
+        lds_dma16_s(kpool + e0 * EB, lk, dst);
+        lds_dma16_s(vpool + e0 * EB, lv, dst + L::KT);
+      }
+    } else if constexpr (DIRECT) {
       char* kb = lds + (kt & 1) * L::BUF;
 #pragma unroll
       for (int j = 0; j < NIW; ++j) {
@@ -375,11 +428,21 @@ prefill_tiled_kernel(const PrefillParams a) {
     for (int b = 0; b < NSB; ++b) {
       // all of the block's K operands first, then the products
       uint4 kv[KSTEPS];
+      if constexpr (DIRECT) {
+        // chunk c = 2k + h of row 32b + n sits at c ^ (n mod R16): one lane
+        // base (the buffer is 1 KiB aligned), step k flips bits 5 and up of
+        // the chunk offset
+        const uint32_t kl = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)kb +
+                            n * L::PK + ((h ^ (n % R16)) << 4);
 #pragma unroll
-      for (int k = 0; k < KSTEPS; ++k) {
-        const int row = 32 * b + n, c = 2 * k + h;          // key row, 16-byte chunk
-        kv[k] = *reinterpret_cast<const uint4*>(kb + row * L::PK +
-                                                (DIRECT ? (c ^ (row % R16)) * 16 : c * 16));
+        for (int k = 0; k < KSTEPS; ++k)
+          kv[k] = lds_ld16((kl ^ (k << 5)) + 32 * b * L::PK);
+      } else {
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) {
+          const int row = 32 * b + n, c = 2 * k + h;          // key row, 16-byte chunk
+          kv[k] = *reinterpret_cast<const uint4*>(kb + row * L::PK + c * 16);
+        }
       }
       sb[b] = (f32x16_t){};
 #pragma unroll
@@ -441,14 +504,17 @@ prefill_tiled_kernel(const PrefillParams a) {
           // 16-lane group, lane 4J + A reads 4 dims (from 4A) of key J, and
           // lane 4A + B receives dim 4A + B of keys 0..3 (k-slots 4r .. +3:
           // keys 16 kb2 + 8r + 4h + 0..3, as P's operand holds them)
+          // key 16 kb2 + 8r + 4h + vJ, chunk c = 4mb + 2vdh + vA/2 at
+          // c ^ 4(vJ mod SEGS): a lane base, dim block mb flips bits 6 and up
+          const uint32_t vl = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)vb +
+                              (4 * h + vJ) * ROWB + (vA & 1) * 8 + (2 * vdh + (vA >> 1)) * 16 +
+                              ((vJ % SEGS) << 6);
           uint32_t w4[4];
 #pragma unroll
           for (int r = 0; r < 2; ++r) {
-            const int key = 16 * kb2 + 8 * r + 4 * h + vJ;
-            const int c = 4 * mb + 2 * vdh + (vA >> 1);
-            const char* src = vb + key * ROWB + (c ^ ((key % SEGS) << 2)) * 16 + (vA & 1) * 8;
+            const uint32_t src = (vl ^ (mb << 6)) + (16 * kb2 + 8 * r) * ROWB;
             const auto t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) tr16x4_t*)src);
+                (__attribute__((address_space(3))) tr16x4_t*)(uintptr_t)src);
             const u32x2_t tw = __builtin_bit_cast(u32x2_t, t);
             w4[2 * r] = tw[0];
             w4[2 * r + 1] = tw[1];
@@ -546,23 +612,33 @@ prefill_tiled_kernel(const PrefillParams a) {
   }
 }
 
-template <Ty KV, Ty QT, int D, int FKT>
+template <Ty KV, Ty QT, int D, int FKT, bool UB>
 hipError_t launch_g(const PrefillParams& a, int g, dim3 grid, hipStream_t st) {
   switch (g) {
-    case 1: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 1, FKT>), grid, dim3(FW * 64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 2, FKT>), grid, dim3(FW * 64), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 4, FKT>), grid, dim3(FW * 64), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 8, FKT>), grid, dim3(FW * 64), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 16, FKT>), grid, dim3(FW * 64), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 1, FKT, UB>), grid, dim3(FW * 64), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 2, FKT, UB>), grid, dim3(FW * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 4, FKT, UB>), grid, dim3(FW * 64), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 8, FKT, UB>), grid, dim3(FW * 64), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((prefill_tiled_kernel<KV, QT, D, 16, FKT, UB>), grid, dim3(FW * 64), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+// 16-bit pools whose blocks hold at least the rows of one staging
+// instruction take the uniform-base form
+template <Ty KV, Ty QT, int D, int FKT>
+hipError_t launch_u(const PrefillParams& a, int g, dim3 grid, hipStream_t st) {
+  if constexpr (TyInfo<KV>::bytes == 2) {
+    if (a.block_size >= 1024 / (2 * D)) return launch_g<KV, QT, D, FKT, true>(a, g, grid, st);
+  }
+  return launch_g<KV, QT, D, FKT, false>(a, g, grid, st);
+}
+
 template <Ty KV, Ty QT>
 hipError_t launch_d(const PrefillParams& a, int g, dim3 grid, bool wide, hipStream_t st) {
-  if (a.head_dim == 64) return wide ? launch_g<KV, QT, 64, 64>(a, g, grid, st) : launch_g<KV, QT, 64, 32>(a, g, grid, st);
-  if (a.head_dim == 128) return wide ? launch_g<KV, QT, 128, 64>(a, g, grid, st) : launch_g<KV, QT, 128, 32>(a, g, grid, st);
+  if (a.head_dim == 64) return wide ? launch_u<KV, QT, 64, 64>(a, g, grid, st) : launch_u<KV, QT, 64, 32>(a, g, grid, st);
+  if (a.head_dim == 128) return wide ? launch_u<KV, QT, 128, 64>(a, g, grid, st) : launch_u<KV, QT, 128, 32>(a, g, grid, st);
   return hipErrorInvalidValue;
 }
 
