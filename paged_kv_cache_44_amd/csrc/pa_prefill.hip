@@ -450,6 +450,19 @@ prefill_tiled_kernel(const PrefillParams a) {
         const uint32_t av[4] = {kv[k].x, kv[k].y, kv[k].z, kv[k].w};
         sb[b] = mfma32<OP>(av, qr[k], sb[b]);
       }
+      if constexpr (DIRECT) {
+        // keep KA operand reads in flight ahead of the dependent products
+        // (the scheduler otherwise waits for each read just before its
+        // product); more than 3 measured no faster
+        constexpr int KA = 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, KA, 0);
+#pragma unroll
+        for (int k = 0; k < KSTEPS - KA; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, KA, 0);
+      }
     }
     // causal mask: key 32b + 8(v/4) + v%4 + 4h of the tile <= pos_row (a
     // tile wholly before the wave's first position masks nothing)
