@@ -25,10 +25,13 @@ namespace {
 // keys. The four waves stage each tile once in LDS, gathered through the
 // block table, double buffered, one barrier per tile. 16-bit pools are
 // staged by the memory unit straight into LDS (global_load_lds_dwordx4),
-// K and V as key rows; FP8 pools go through registers, their codes widened
-// exactly to the query's 16-bit type, K as rows and V transposed (a row per
-// dim). Both products run on the 32x32x16 matrix cores, transposed so that
-// a query row owns a lane pair:
+// K and V as key rows, from wave-uniform base addresses when a block holds
+// all the rows of one such instruction; FP8 pools go through registers,
+// their codes widened exactly to the query's 16-bit type, K as rows and V
+// transposed (a row per dim). After the walk the normalised rows pass
+// through LDS, so that they leave as whole 16-byte pieces. Both products
+// run on the 32x32x16 matrix cores, transposed so that a query row owns a
+// lane pair:
 //   S^T[FKT keys][32 rows] = K[FKT][D] . Q^T[D][32]    (A = K rows from LDS)
 //   O^T[D][32 rows]      += V^T[D][FKT] . P^T[FKT][32] (A = V^T rows from LDS,
 //                                                       B = P from registers)
