@@ -410,7 +410,7 @@ pa_status prefill_impl(const pa_kv_cache* cache, int32_t layer, const void* q, p
   if (!pa::prefill_supported((int)cache->dtype, (int)q_dtype, cache->head_dim, g))
     return PA_ERR_UNSUPPORTED;
   // one workgroup per (sequence, KV head, row tile), in a one-dimensional grid
-  if ((int64_t)num_seqs * cache->num_kv_heads * pa::prefill_tiles(g, max_query_len) > 0x7ffffff8)
+  if (pa::prefill_grid(num_seqs, cache->num_kv_heads, pa::prefill_tiles(g, max_query_len)) > 0x7ffffff8)
     return PA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(out, 4)) return PA_ERR_UNSUPPORTED;
   pa::PrefillParams a;

@@ -164,6 +164,7 @@ hipError_t launch_attend_shared_dual(const DecodeParams& pre, const DecodeParams
 hipError_t launch_shared_combine(const DecodeParams& a, int q_ty, int g, hipStream_t st);
 bool prefill_supported(int kv_ty, int q_ty, int head_dim, int g);
 int prefill_tiles(int g, int max_query_len);
+int64_t prefill_grid(int num_seqs, int num_kv_heads, int tiles);
 hipError_t launch_prefill(const PrefillParams& a, int kv_ty, int q_ty, int g, int max_query_len,
                           hipStream_t st);
 hipError_t launch_write(const WriteParams& a, int src_ty, int dst_ty, hipStream_t st);

@@ -187,19 +187,20 @@ prefill_tiled_kernel(const PrefillParams a) {
   const int n = lane & 31;                        // row of the wave (output column)
   const int h = lane >> 5;                        // lane half: keys / dims it holds
   const int H = a.num_kv_heads;
-  // Workgroup numbering: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous stretch of the virtual order, which takes every row tile of
-  // one (sequence, KV head) in turn, longest causal range first, so the
-  // tiles that stream the same keys and values run together and share them
-  // in that XCD's L2.
-  const unsigned per_xcd = gridDim.x / NXCD_PF;
-  const unsigned vb = (blockIdx.x % NXCD_PF) * per_xcd + blockIdx.x / NXCD_PF;
+  // Workgroup numbering: workgroup b runs on XCD b % 8, as its (b / 8)-th.
+  // The (sequence, KV head) pairs are dealt round-robin over the XCDs (pair
+  // p to XCD p % 8: with 8 KV heads each XCD gets one head of every
+  // sequence, so the XCDs get equal work whatever the length mix), and an
+  // XCD takes every row tile of one pair in turn, longest causal range
+  // first, so the tiles that stream the same keys and values run together
+  // and share them in that XCD's L2.
   const unsigned tiles = (unsigned)a.row_tiles;
-  const unsigned sh = vb / tiles;
+  const unsigned xi = blockIdx.x / NXCD_PF;                        // place on its XCD
+  const unsigned sh = (xi / tiles) * NXCD_PF + blockIdx.x % NXCD_PF;   // the pair
   if (sh >= (unsigned)a.num_seqs * (unsigned)H) return;          // padding to whole XCD rounds
   const int s = (int)(sh / H);
   const int kvh = (int)(sh - (unsigned)s * H);
-  const int tpos0 = (int)(tiles - 1 - (vb - sh * tiles)) * TPOS;   // first query index of the tile
+  const int tpos0 = (int)(tiles - 1 - xi % tiles) * TPOS;          // first query index of the tile
   const int r0 = a.query_start_loc[s];
   const int nq = a.query_start_loc[s + 1] - r0;
   // rows outside the packed query array are never touched
@@ -674,12 +675,20 @@ int prefill_tiles(int g, int max_query_len) {
   return (int)(((int64_t)max_query_len + per - 1) / per);
 }
 
+// The launch: the (sequence, KV head) pairs rounded up to whole rounds of
+// the XCDs, times the row tiles of each (the kernel deals pairs round-robin
+// over the XCDs).
+int64_t prefill_grid(int num_seqs, int num_kv_heads, int tiles) {
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  return (pairs + NXCD_PF - 1) / NXCD_PF * NXCD_PF * tiles;
+}
+
 hipError_t launch_prefill(const PrefillParams& a0, int kv_ty, int q_ty, int g, int max_query_len,
                           hipStream_t st) {
   PrefillParams a = a0;
   a.row_tiles = prefill_tiles(g, max_query_len);
   const int64_t used = (int64_t)a.num_seqs * a.num_kv_heads * a.row_tiles;
-  int64_t wgs = (used + NXCD_PF - 1) / NXCD_PF * NXCD_PF;
+  const int64_t wgs = prefill_grid(a.num_seqs, a.num_kv_heads, a.row_tiles);
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs);
   // 64-key tiles when the grid is at most two rounds of two workgroups per
