@@ -156,10 +156,9 @@ prefill_tiled_kernel(const PrefillParams a) {
   constexpr int TPOS = FW * FR / G;               // positions per workgroup
   constexpr int CD = 16 / EB;                     // dims per 16-byte pool chunk
   constexpr int CPR = D / CD;                     // chunks per key row
-  constexpr int PAIRS = FKT / 2;                  // key pairs per tile
   constexpr int NSB = FKT / 32;                   // score blocks of 32 keys per tile
   constexpr int NKB = FKT / 16;                   // key blocks of 16 per tile
-  constexpr int JOBS = PAIRS * CPR;               // staging jobs per tile: (key pair, chunk)
+  constexpr int JOBS = FKT * CPR;                 // register staging jobs per tile: (key, chunk)
   constexpr int NJ = (JOBS + FW * 64 - 1) / (FW * 64);   // jobs per thread
   static_assert(FKT == 32 || FKT == 64, "keys per tile");
   // 16-bit pools are staged by the memory unit straight into LDS (no
@@ -177,7 +176,7 @@ prefill_tiled_kernel(const PrefillParams a) {
   constexpr int NIW = FKT / (RPI * FW);           // instructions per wave per tile (each of K, V)
   static_assert(!DIRECT || FKT % (RPI * FW) == 0, "tile rows split evenly over the waves");
   static_assert(DIRECT || !UB, "uniform staging bases: 16-bit pools only");
-  constexpr int NID = DIRECT ? NIW : NJ * 2;      // block ids a thread fetches per tile
+  constexpr int NID = DIRECT ? NIW : NJ;          // block ids a thread fetches per tile
   using L = FaLds<D, FKT, DIRECT>;
   __shared__ __attribute__((aligned(1024))) char lds[L::BYTES];
 
@@ -263,9 +262,11 @@ prefill_tiled_kernel(const PrefillParams a) {
     }
   }
 
-  // ---- staging: job j = (key pair j % PAIRS, chunk j / PAIRS): both keys' chunk
-  // of K and of V. K goes to its rows as is; V's two keys are interleaved
-  // per dim (one dword per dim) into the V^T rows.
+  // ---- register staging: job j = (key j % FKT, chunk j / FKT): the key's
+  // chunk of K and of V. K goes to its row as is. Neighbouring lanes hold
+  // the two keys of a pair (same chunk); V^T interleaves them per dim (one
+  // dword per dim), the even key's lane writing the chunk's first 8 dims and
+  // the odd key's lane the last 8.
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   const int bmask = a.block_size - 1;
@@ -274,8 +275,8 @@ prefill_tiled_kernel(const PrefillParams a) {
   // keys past the context (the last tile's tail) read the last key again:
   // finite values behind masked scores; table entries past the context are
   // never read
-  auto key_at = [&](int kt, int jb, int odd) __attribute__((always_inline)) {
-    return min(kt * FKT + 2 * (jb % PAIRS) + odd, ctx - 1);
+  auto key_at = [&](int kt, int jb) __attribute__((always_inline)) {
+    return min(kt * FKT + jb % FKT, ctx - 1);
   };
   auto job_of = [&](int i) __attribute__((always_inline)) { return tid + FW * 64 * i; };
   // direct staging: this lane's row of wave instruction j, and its chunk
@@ -305,12 +306,11 @@ prefill_tiled_kernel(const PrefillParams a) {
     } else {
 #pragma unroll
       for (int i = 0; i < NJ; ++i)
-#pragma unroll
-        for (int o = 0; o < 2; ++o) ids[2 * i + o] = trow[key_at(kt, job_of(i) % JOBS, o) >> lg];
+        ids[i] = (JOBS % (FW * 64) != 0 && job_of(i) >= JOBS) ? 0 : trow[key_at(kt, job_of(i)) >> lg];
     }
   };
   bool bad = false;                               // a bad block id was staged
-  uint32_t stk[DIRECT ? 1 : NJ][2][4], stv[DIRECT ? 1 : NJ][2][4];
+  uint32_t stk[DIRECT ? 1 : NJ][4], stv[DIRECT ? 1 : NJ][4];
   auto load_tile = [&](int kt, const int (&ids)[NID]) __attribute__((always_inline)) {
     if constexpr (UB) {
       char* kb = lds + (kt & 1) * L::BUF;
@@ -352,17 +352,15 @@ prefill_tiled_kernel(const PrefillParams a) {
     } else {
 #pragma unroll
       for (int i = 0; i < NJ; ++i) {
-        const int jb = job_of(i) % JOBS;          // (a thread past the jobs repeats one)
-#pragma unroll
-        for (int o = 0; o < 2; ++o) {
-          const int k = key_at(kt, jb, o);
-          const bool ok = ids[2 * i + o] >= 0 && ids[2 * i + o] < a.num_blocks;
-          bad = bad || !ok;
-          const int64_t e = (int64_t)(ok ? ids[2 * i + o] : 0) * a.block_stride + head_off +
-                            (int64_t)(k & bmask) * D + (jb / PAIRS) * CD;
-          ld<4>(reinterpret_cast<const uint32_t*>(kpool + e * EB), stk[i][o]);
-          ld<4>(reinterpret_cast<const uint32_t*>(vpool + e * EB), stv[i][o]);
-        }
+        if (JOBS % (FW * 64) != 0 && job_of(i) >= JOBS) continue;   // (whole waves past the jobs)
+        const int jb = job_of(i);
+        const int k = key_at(kt, jb);
+        const bool ok = ids[i] >= 0 && ids[i] < a.num_blocks;
+        bad = bad || !ok;
+        const int64_t e = (int64_t)(ok ? ids[i] : 0) * a.block_stride + head_off +
+                          (int64_t)(k & bmask) * D + (jb / FKT) * CD;
+        ld<4>(reinterpret_cast<const uint32_t*>(kpool + e * EB), stk[i]);
+        ld<4>(reinterpret_cast<const uint32_t*>(vpool + e * EB), stv[i]);
       }
     }
   };
@@ -374,38 +372,42 @@ prefill_tiled_kernel(const PrefillParams a) {
     for (int i = 0; i < NJ; ++i) {
       if (JOBS % (FW * 64) != 0 && job_of(i) >= JOBS) continue;
       const int jb = job_of(i);
-      const int key = 2 * (jb % PAIRS), ch = jb / PAIRS;
-      // the two keys' values as 16-bit pairs (dims 2q, 2q+1 in dword q)
-      uint32_t w[2][CD / 2];
+      const int key = jb % FKT, ch = jb / FKT;
+      static_assert(DIRECT || EB == 1, "register staging: FP8 pools");
+      // K: the key's 16 codes widened, into its row
+      uint32_t w[8];
 #pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        if constexpr (EB == 2) {
+      for (int x = 0; x < 4; ++x) fp8x4_to<OP>(stk[i][x], w[2 * x], w[2 * x + 1]);
+      char* dst = kb + key * L::PK + ch * CD * 2;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+      // V^T: this lane writes dims 8hv .. 8hv + 7 of the chunk for the pair
+      // (hv = key parity); it sends the other half of its own codes to its
+      // neighbour (lane ^ 1, the pair's other key) and gets that key's codes
+      // of its half back
+      const int hv = key & 1;
+      uint32_t mine[2], theirs[2];
 #pragma unroll
-          for (int x = 0; x < 4; ++x) w[o][x] = stk[i][o][x];
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) fp8x4_to<OP>(stk[i][o][x], w[o][2 * x], w[o][2 * x + 1]);
-        }
-        char* dst = kb + (key + o) * L::PK + ch * CD * 2;
-#pragma unroll
-        for (int x = 0; x < CD / 8; ++x)
-          *reinterpret_cast<uint4*>(dst + 16 * x) =
-              make_uint4(w[o][4 * x], w[o][4 * x + 1], w[o][4 * x + 2], w[o][4 * x + 3]);
-        if constexpr (EB == 2) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) w[o][x] = stv[i][o][x];
-        } else {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) fp8x4_to<OP>(stv[i][o][x], w[o][2 * x], w[o][2 * x + 1]);
-        }
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t send = hv ? stv[i][x] : stv[i][2 + x];
+        theirs[x] = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+        mine[x] = hv ? stv[i][2 + x] : stv[i][x];
       }
-      // V^T: dim d's dword holds (key, key + 1) at the pair's slot
-      char* vdst = vb + ((key & ~15) + vt_slot(key & 15)) * 2;
+      // the pair's even key (wa) and odd key (wb): dims 8hv + 2q, +1 in dword q
+      uint32_t wa[4], wb[4];
 #pragma unroll
-      for (int q = 0; q < CD / 2; ++q) {
-        const int d = ch * CD + 2 * q;
-        *reinterpret_cast<uint32_t*>(vdst + d * L::PV) = __builtin_amdgcn_perm(w[1][q], w[0][q], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(vdst + (d + 1) * L::PV) = __builtin_amdgcn_perm(w[1][q], w[0][q], 0x07060302u);
+      for (int x = 0; x < 2; ++x) {
+        fp8x4_to<OP>(hv ? theirs[x] : mine[x], wa[2 * x], wa[2 * x + 1]);
+        fp8x4_to<OP>(hv ? mine[x] : theirs[x], wb[2 * x], wb[2 * x + 1]);
+      }
+      // dim d's dword holds (even key, odd key) at the pair's slot
+      const int kp = key & ~1;
+      char* vdst = vb + ((kp & ~15) + vt_slot(kp & 15)) * 2;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = ch * CD + 8 * hv + 2 * q;
+        *reinterpret_cast<uint32_t*>(vdst + d * L::PV) = __builtin_amdgcn_perm(wb[q], wa[q], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(vdst + (d + 1) * L::PV) = __builtin_amdgcn_perm(wb[q], wa[q], 0x07060302u);
       }
     }
     }
