@@ -45,6 +45,11 @@ namespace {
 // keys); from transposed FP8 staging, V^T is laid out with its keys in that
 // order, one 16-byte LDS read per operand.
 constexpr int NXCD_PF = 8;        // XCDs of an MI355X
+// (sequence, KV head) pairs dealt round-robin over the XCDs: a multiple of
+// their count, or enough of them to even out
+__host__ __device__ inline bool pf_round_robin(int64_t pairs) {
+  return pairs % NXCD_PF == 0 || pairs >= 4 * NXCD_PF;
+}
 constexpr int FW = 4;             // waves per workgroup
 constexpr int FR = 32;            // query rows per wave
 // score of a masked key: finite, so exp2(score * c - m) is exactly 0 without
@@ -187,19 +192,31 @@ prefill_tiled_kernel(const PrefillParams a) {
   const int h = lane >> 5;                        // lane half: keys / dims it holds
   const int H = a.num_kv_heads;
   // Workgroup numbering: workgroup b runs on XCD b % 8, as its (b / 8)-th.
-  // The (sequence, KV head) pairs are dealt round-robin over the XCDs (pair
-  // p to XCD p % 8: with 8 KV heads each XCD gets one head of every
-  // sequence, so the XCDs get equal work whatever the length mix), and an
-  // XCD takes every row tile of one pair in turn, longest causal range
-  // first, so the tiles that stream the same keys and values run together
-  // and share them in that XCD's L2.
+  // An XCD takes every row tile of one (sequence, KV head) pair in turn,
+  // longest causal range first, so the tiles that stream the same keys and
+  // values run together and share them in that XCD's L2. The pairs are
+  // dealt round-robin over the XCDs (pair p to XCD p % 8: with 8 KV heads
+  // each XCD gets one head of every sequence, so the XCDs get equal work
+  // whatever the length mix); with fewer than 32 pairs, not a multiple of
+  // 8, each XCD takes a contiguous eighth of the (pair, row tile) list
+  // instead, so that every XCD has work.
   const unsigned tiles = (unsigned)a.row_tiles;
-  const unsigned xi = blockIdx.x / NXCD_PF;                        // place on its XCD
-  const unsigned sh = (xi / tiles) * NXCD_PF + blockIdx.x % NXCD_PF;   // the pair
-  if (sh >= (unsigned)a.num_seqs * (unsigned)H) return;          // padding to whole XCD rounds
+  const unsigned pairs = (unsigned)a.num_seqs * (unsigned)H;
+  unsigned sh, tl;                                // the pair, and its row tile from the longest
+  if (pf_round_robin(pairs)) {
+    const unsigned xi = blockIdx.x / NXCD_PF;     // place on its XCD
+    sh = (xi / tiles) * NXCD_PF + blockIdx.x % NXCD_PF;
+    tl = xi % tiles;
+  } else {
+    const unsigned per_xcd = gridDim.x / NXCD_PF;
+    const unsigned vb = (blockIdx.x % NXCD_PF) * per_xcd + blockIdx.x / NXCD_PF;
+    sh = vb / tiles;
+    tl = vb - sh * tiles;
+  }
+  if (sh >= pairs) return;                        // padding to whole XCD rounds
   const int s = (int)(sh / H);
   const int kvh = (int)(sh - (unsigned)s * H);
-  const int tpos0 = (int)(tiles - 1 - xi % tiles) * TPOS;          // first query index of the tile
+  const int tpos0 = (int)(tiles - 1 - tl) * TPOS;  // first query index of the tile
   const int r0 = a.query_start_loc[s];
   const int nq = a.query_start_loc[s + 1] - r0;
   // rows outside the packed query array are never touched
@@ -677,12 +694,13 @@ int prefill_tiles(int g, int max_query_len) {
   return (int)(((int64_t)max_query_len + per - 1) / per);
 }
 
-// The launch: the (sequence, KV head) pairs rounded up to whole rounds of
-// the XCDs, times the row tiles of each (the kernel deals pairs round-robin
-// over the XCDs).
+// The launch: with pairs dealt round-robin over the XCDs, the (sequence, KV
+// head) pairs rounded up to whole rounds of the XCDs, times the row tiles of
+// each; otherwise the (pair, row tile) list rounded up to whole rounds.
 int64_t prefill_grid(int num_seqs, int num_kv_heads, int tiles) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  return (pairs + NXCD_PF - 1) / NXCD_PF * NXCD_PF * tiles;
+  if (pf_round_robin(pairs)) return (pairs + NXCD_PF - 1) / NXCD_PF * NXCD_PF * tiles;
+  return (pairs * tiles + NXCD_PF - 1) / NXCD_PF * NXCD_PF;
 }
 
 hipError_t launch_prefill(const PrefillParams& a0, int kv_ty, int q_ty, int g, int max_query_len,
