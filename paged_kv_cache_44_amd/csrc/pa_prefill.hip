@@ -197,9 +197,9 @@ prefill_tiled_kernel(const PrefillParams a) {
   // values run together and share them in that XCD's L2. The pairs are
   // dealt round-robin over the XCDs (pair p to XCD p % 8: with 8 KV heads
   // each XCD gets one head of every sequence, so the XCDs get equal work
-  // whatever the length mix); with fewer than 32 pairs, not a multiple of
-  // 8, each XCD takes a contiguous eighth of the (pair, row tile) list
-  // instead, so that every XCD has work.
+  // whatever the length mix). With fewer than 32 pairs, not a multiple of
+  // 8, the (pair, row tile) items go to the XCDs in turn instead (item b on
+  // XCD b % 8), so that every XCD gets an even share of every pair.
   const unsigned tiles = (unsigned)a.row_tiles;
   const unsigned pairs = (unsigned)a.num_seqs * (unsigned)H;
   unsigned sh, tl;                                // the pair, and its row tile from the longest
@@ -208,8 +208,7 @@ prefill_tiled_kernel(const PrefillParams a) {
     sh = (xi / tiles) * NXCD_PF + blockIdx.x % NXCD_PF;
     tl = xi % tiles;
   } else {
-    const unsigned per_xcd = gridDim.x / NXCD_PF;
-    const unsigned vb = (blockIdx.x % NXCD_PF) * per_xcd + blockIdx.x / NXCD_PF;
+    const unsigned vb = blockIdx.x;
     sh = vb / tiles;
     tl = vb - sh * tiles;
   }
@@ -696,7 +695,7 @@ int prefill_tiles(int g, int max_query_len) {
 
 // The launch: with pairs dealt round-robin over the XCDs, the (sequence, KV
 // head) pairs rounded up to whole rounds of the XCDs, times the row tiles of
-// each; otherwise the (pair, row tile) list rounded up to whole rounds.
+// each; otherwise the (pair, row tile) items rounded up to whole rounds.
 int64_t prefill_grid(int num_seqs, int num_kv_heads, int tiles) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
   if (pf_round_robin(pairs)) return (pairs + NXCD_PF - 1) / NXCD_PF * NXCD_PF * tiles;
