@@ -102,9 +102,9 @@ def parse():
                          "layer and 64 layers, block-major and layer-major pools; then the "
                          "swap pipeline (copy stream beside decode); one JSON line per case")
     ap.add_argument("--prefill", action="store_true",
-                    help="time paged prefill: the GQA bf16 workload's contexts prefilled whole, "
-                         "and the long FP8 workload's 1,500-token victim recomputed; one JSON "
-                         "line each")
+                    help="time paged prefill: the GQA bf16 workload's contexts prefilled whole "
+                         "(bf16 pool, and an FP8 pool with bf16 queries), and the long FP8 "
+                         "workload's 1,500-token victim recomputed; one JSON line each")
     ap.add_argument("--block-size-sweep", action="store_true",
                     help="the GQA bf16 decode step at block sizes 8..256: step and attention-kernel "
                          "time, and the slots the blocks hold beyond the context (one JSON line each)")
@@ -458,7 +458,11 @@ def prefill_bench(steps: int, warmup: int):
     import paged_kv_cache_44_amd as pa
     import workloads
     dev = torch.device("cuda:0")
-    cases = [("prefill_gqa_bf16", workloads.make(3), None),
+    gqa = workloads.make(3)
+    cases = [("prefill_gqa_bf16", gqa, None),
+             ("prefill_gqa_fp8", workloads.custom(3, gqa.context_lens, pool_dtype="fp8_e4m3",
+                                                  q_dtype="bf16", num_q_heads=32, num_kv_heads=8,
+                                                  head_dim=128, block_size=16), None),
              ("recompute_fp8_1500", workloads.custom(505, [1500], pool_dtype="fp8_e4m3",
                                                      q_dtype="bf16", num_q_heads=64, num_kv_heads=8,
                                                      head_dim=128, block_size=16), None)]
