@@ -215,3 +215,32 @@ def test_prefill_large_grid_matches_oracle(pool, q, D, G, B):
     ex = max_err_stored(got, ref, q, TOL[pool])
     say(f"{int(qsl[-1])} rows, max abs err {err:.3e}, with the output-rounding allowance {ex:.3e}")
     assert ex <= TOL[pool]
+
+
+# (sequences, KV heads): the pair counts that pick each workgroup order.
+# Pairs dealt round-robin over the 8 XCDs when their count is a multiple of
+# 8 or at least 32 (33 leaves the last round with one pair and seven padding
+# slots); fewer, not a multiple of 8, deal (pair, row tile) items in turn.
+ORDERS = [(1, 3), (5, 1), (3, 5), (2, 8), (11, 3), (40, 1)]
+
+
+@pytest.mark.parametrize("S,HKV", ORDERS)
+def test_prefill_workgroup_orders(S, HKV):
+    """Every workgroup order of the launch covers each (sequence, KV head,
+    row tile) exactly once: prompts of mixed lengths, every row against the
+    oracle."""
+    rng = np.random.default_rng(31 * S + HKV)
+    ctx = rng.integers(1, 300, S)
+    ctx[0] = 300                                   # one long prompt sets the row tiles of all
+    wl = workloads.custom(int(rng.integers(1000)), ctx, pool_dtype="bf16", q_dtype="bf16",
+                          num_q_heads=4 * HKV, num_kv_heads=HKV, head_dim=128, block_size=16)
+    st = DeviceState(wl)
+    st.write(wl.write_k, wl.write_v, wl.write_slots)
+    qc, qsl = workloads.prefill_queries(wl, ctx, 19)
+    out = _run(st, qc, qsl)
+    got = codecs.decode(tensor_codes(out), "bf16")
+    ref = _oracle(st, qc, qsl)
+    assert np.all(np.isfinite(got))
+    ex = max_err_stored(got, ref, "bf16", TOL["bf16"])
+    say(f"{S} x {HKV} pairs, {int(qsl[-1])} rows, error with the output-rounding allowance {ex:.3e}")
+    assert ex <= TOL["bf16"]
