@@ -45,10 +45,11 @@ namespace {
 // keys); from transposed FP8 staging, V^T is laid out with its keys in that
 // order, one 16-byte LDS read per operand.
 constexpr int NXCD_PF = 8;        // XCDs of an MI355X
-// (sequence, KV head) pairs dealt round-robin over the XCDs: a multiple of
-// their count, or enough of them to even out
-__host__ __device__ inline bool pf_round_robin(int64_t pairs) {
-  return pairs % NXCD_PF == 0 || pairs >= 4 * NXCD_PF;
+// (sequence, KV head) pairs dealt round-robin over the XCDs: when the KV
+// heads are a multiple of the XCDs, so that each XCD gets the same share of
+// every sequence
+__host__ __device__ inline bool pf_round_robin(int num_kv_heads) {
+  return num_kv_heads % NXCD_PF == 0;
 }
 constexpr int FW = 4;             // waves per workgroup
 constexpr int FR = 32;            // query rows per wave
@@ -194,16 +195,17 @@ prefill_tiled_kernel(const PrefillParams a) {
   // Workgroup numbering: workgroup b runs on XCD b % 8, as its (b / 8)-th.
   // An XCD takes every row tile of one (sequence, KV head) pair in turn,
   // longest causal range first, so the tiles that stream the same keys and
-  // values run together and share them in that XCD's L2. The pairs are
-  // dealt round-robin over the XCDs (pair p to XCD p % 8: with 8 KV heads
-  // each XCD gets one head of every sequence, so the XCDs get equal work
-  // whatever the length mix). With fewer than 32 pairs, not a multiple of
-  // 8, the (pair, row tile) items go to the XCDs in turn instead (item b on
-  // XCD b % 8), so that every XCD gets an even share of every pair.
+  // values run together and share them in that XCD's L2. With a multiple
+  // of 8 KV heads the pairs are dealt round-robin over the XCDs (pair p to
+  // XCD p % 8: each XCD gets the same heads of every sequence, so the XCDs
+  // get equal work whatever the length mix). Otherwise a sequence's heads
+  // would not spread evenly, and the (pair, row tile) items go to the XCDs
+  // in turn instead (item b on XCD b % 8), so that every XCD gets an even
+  // share of every pair.
   const unsigned tiles = (unsigned)a.row_tiles;
   const unsigned pairs = (unsigned)a.num_seqs * (unsigned)H;
   unsigned sh, tl;                                // the pair, and its row tile from the longest
-  if (pf_round_robin(pairs)) {
+  if (pf_round_robin(H)) {
     const unsigned xi = blockIdx.x / NXCD_PF;     // place on its XCD
     sh = (xi / tiles) * NXCD_PF + blockIdx.x % NXCD_PF;
     tl = xi % tiles;
@@ -693,12 +695,11 @@ int prefill_tiles(int g, int max_query_len) {
   return (int)(((int64_t)max_query_len + per - 1) / per);
 }
 
-// The launch: with pairs dealt round-robin over the XCDs, the (sequence, KV
-// head) pairs rounded up to whole rounds of the XCDs, times the row tiles of
-// each; otherwise the (pair, row tile) items rounded up to whole rounds.
+// The launch: the (pair, row tile) items, rounded up to whole rounds of the
+// XCDs (with pairs dealt round-robin, their count is already a multiple of 8).
 int64_t prefill_grid(int num_seqs, int num_kv_heads, int tiles) {
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  if (pf_round_robin(pairs)) return (pairs + NXCD_PF - 1) / NXCD_PF * NXCD_PF * tiles;
+  if (pf_round_robin(num_kv_heads)) return pairs * tiles;   // (pairs: a multiple of 8)
   return (pairs * tiles + NXCD_PF - 1) / NXCD_PF * NXCD_PF;
 }
 

@@ -217,11 +217,11 @@ def test_prefill_large_grid_matches_oracle(pool, q, D, G, B):
     assert ex <= TOL[pool]
 
 
-# (sequences, KV heads): the pair counts that pick each workgroup order.
-# Pairs dealt round-robin over the 8 XCDs when their count is a multiple of
-# 8 or at least 32 (33 leaves the last round with one pair and seven padding
-# slots); fewer, not a multiple of 8, deal (pair, row tile) items in turn.
-ORDERS = [(1, 3), (5, 1), (3, 5), (2, 8), (11, 3), (40, 1)]
+# (sequences, KV heads) for each workgroup order: pairs dealt round-robin
+# over the 8 XCDs when the KV heads are a multiple of 8, (pair, row tile)
+# items dealt in turn otherwise (including item counts that leave padding
+# slots in the last round).
+ORDERS = [(1, 3), (5, 1), (3, 5), (11, 3), (40, 1), (2, 8), (3, 16)]
 
 
 @pytest.mark.parametrize("S,HKV", ORDERS)
